@@ -1,0 +1,319 @@
+"""Benchmark: ms per denoise step of the write-time RoPE + FP8 ring cache path.
+
+One step (the production attention shape on one GPU's 12-head share):
+  * one launch writing the new chunk (757 tokens) of all 60 layer caches
+    (RoPE + FP8 at write time), then
+  * 240 FP8 window-attention calls (4 denoise passes x 60 layers, pass-major),
+    each from the 757 new-token queries over the full 5788-slot window.
+Also reported: the delta rebase of the whole 60-layer window (ms, GB/s), the
+naive per-call upkeep path on the same shapes (re-rotate, re-quantise and
+shift the window on all 240 calls), and the CPU oracle timed on a bounded
+sample.  Inputs are seeded synthetic tensors (kv_cache_attention_ring_amd.inputs).
+
+    python bench.py [--gpus 1] [--steps 42] [--warmup 5]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms per denoise step (240 attn calls + KV upkeep); HBM GB/s and FP8 MFMA % of peak"
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=42)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--naive-steps", type=int, default=3)
+    ap.add_argument("--rebase-iters", type=int, default=20)
+    ap.add_argument("--splits", type=int, default=0, help="attention key splits (0 = default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-naive", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; --gpus must be 1 "
+                                   "(the path shards over heads, see the design notes)"}))
+        sys.exit(2)
+    import torch
+
+    from kv_cache_attention_ring_amd import inputs
+    from kv_cache_attention_ring_amd import kvring as K
+
+    dev = "cuda"
+    shp = inputs.PAGE_STEP
+    L, H, D, W, N, P = shp.n_layers, shp.n_heads, shp.head_dim, shp.window, shp.n_new, shp.passes
+    pre = 8
+    total_steps = pre + args.warmup + args.steps + 2
+    pos_lo = -inputs.DELTA_MAX - 8 * N
+    rope = K.RopeTable(pos_lo, total_steps * N - pos_lo, D, device=dev)
+    cache = K.KVCache(L, H, D, W, device=dev)
+    ring = K.kvr_ring_init()
+    log(f"cache {cache.nbytes / 1e9:.3f} GB, rope table {rope.cs.numel() * 4 / 1e6:.1f} MB")
+
+    pool = 8
+    chunks = [inputs.torch_chunk(shp, s, 0, dev, n_layers=L) for s in range(pool)]
+    qpool = [inputs.torch_queries(shp, 0, p, l, dev) for p in range(P) for l in range(L)]
+    outs = [torch.empty((N, H, D), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    ws_bytes = K.attn_fp8_window_workspace_bytes(cache, N, W, args.splits)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+
+    for s in range(pre):
+        k, v = chunks[s % pool]
+        K.kv_write_rope_quant(cache, ring, 0, k, v, rope)
+        K.kvr_ring_after_write(ring, W, N)
+    torch.cuda.synchronize()
+    log(f"prefilled {pre} chunks: head {ring.head}, n_valid {ring.n_valid}")
+
+    def write(step_idx):
+        k, v = chunks[step_idx % pool]
+        K.kv_write_rope_quant(cache, ring, 0, k, v, rope)
+        K.kvr_ring_after_write(ring, W, N)
+
+    def attend(layer, pss, start):
+        K.attn_fp8_window(cache, layer, start, ring.n_valid, qpool[pss * L + layer], ring.pos_next - N,
+                          rope, out=outs[layer], n_splits=args.splits, ws=ws)
+
+    def step(step_idx):
+        write(step_idx)
+        start = K.kvr_ring_logical_start(ring, W)
+        for p in range(P):
+            for layer in range(L):
+                attend(layer, p, start)
+
+    sidx = pre
+    for _ in range(args.warmup):
+        step(sidx)
+        sidx += 1
+    torch.cuda.synchronize()
+
+    # ---- timed steps ---------------------------------------------------------
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step(sidx)
+        sidx += 1
+    ev1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1e3
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"{args.steps} steps: {ms_step:.4f} ms/step (wall {wall_ms / args.steps:.4f})")
+
+    # ---- per-kernel times, measured with events on the launch stream -----------
+    n_meas = 2
+    w_ms, a_ms = [], []
+    for _ in range(n_meas):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2 + 2 * P * L)]
+        e[0].record()
+        write(sidx)
+        e[1].record()
+        start = K.kvr_ring_logical_start(ring, W)
+        i = 2
+        for p in range(P):
+            for layer in range(L):
+                e[i].record()
+                attend(layer, p, start)
+                e[i + 1].record()
+                i += 2
+        torch.cuda.synchronize()
+        sidx += 1
+        w_ms.append(e[0].elapsed_time(e[1]))
+        a_ms += [e[j].elapsed_time(e[j + 1]) for j in range(2, len(e), 2)]
+    write_ms = sum(w_ms) / len(w_ms)
+    attn_ms = sum(a_ms) / len(a_ms)
+    attn_flops = 4.0 * N * W * H * D
+    attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
+    write_bytes = L * (2 * N * H * D * 2 + 2 * N * H * D + 2 * N * H * 4)
+    write_gbs = write_bytes / (write_ms * 1e-3) / 1e9
+    log(f"write (60 layers) {write_ms * 1e3:.1f} us = {write_gbs:.0f} GB/s; attention call "
+        f"{attn_ms * 1e3:.2f} us = {attn_tflops:.1f} TFLOP/s")
+
+    # ---- rebase (position reset) -------------------------------------------------
+    delta = inputs.rebase_delta()
+    reb_bytes = 2 * (L * H * W * D + L * H * W * 4)
+    for i in range(5):
+        K.kv_delta_rebase(cache, ring, 0, L, delta if i % 2 == 0 else -delta)
+    torch.cuda.synchronize()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record()
+    for i in range(args.rebase_iters):
+        K.kv_delta_rebase(cache, ring, 0, L, delta if i % 2 == 0 else -delta)
+    r1.record()
+    torch.cuda.synchronize()
+    reb_ms = r0.elapsed_time(r1) / args.rebase_iters
+    reb_gbs = reb_bytes / (reb_ms * 1e-3) / 1e9
+    log(f"rebase delta={delta}: {reb_ms:.4f} ms = {reb_gbs:.0f} GB/s")
+
+    # ---- naive per-call upkeep -------------------------------------------------------
+    naive = None
+    if not args.no_naive and args.naive_steps > 0:
+        naive = run_naive(args, K, inputs, shp, rope, chunks, qpool, outs, ws, torch, dev, pre)
+
+    # ---- CPU oracle on a bounded sample -----------------------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(K, inputs, shp, cache, qpool, ring, chunks, torch)
+
+    line = {
+        "metric": METRIC,
+        "value": round(ms_step, 5),
+        "unit": "ms/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": "full denoise step: 60 layer caches x 12 heads x head_dim 128, ring window "
+                        "5788 slots, 757 new tokens per step; one 60-layer write + 240 attention calls",
+            "layers": L, "heads": H, "head_dim": D, "window": W, "new_tokens": N, "passes": P,
+            "attention_splits": args.splits or "default",
+        },
+        "roofline": {
+            "kernel": "attn_fp8_window (attention + split combine), per call",
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 2),
+            "peak": FP8_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
+            "traffic": None,
+        },
+        "breakdown": {
+            "write_60_layers_us": round(write_ms * 1e3, 2),
+            "write_GBps": round(write_gbs, 1),
+            "write_frac_hbm": round(write_gbs / HBM_PEAK_GBS, 4),
+            "attention_call_us": round(attn_ms * 1e3, 3),
+            "attention_ms_per_step": round(attn_ms * P * L, 4),
+            "rebase_ms": round(reb_ms, 4),
+            "rebase_GBps": round(reb_gbs, 1),
+            "rebase_frac_hbm": round(reb_gbs / HBM_PEAK_GBS, 4),
+            "rebase_delta": delta,
+        },
+        "naive": naive,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_naive(args, K, inputs, shp, rope, chunks, qpool, outs, ws, torch, dev, pre):
+    """Naive path: on every one of the 240 calls, rebuild the shifted bf16 window
+    and re-rotate / re-quantise all of it, then attend over the linear window."""
+    L, H, D, W, N, P = shp.n_layers, shp.n_heads, shp.head_dim, shp.window, shp.n_new, shp.passes
+    wins = [[torch.zeros((H, W, D), dtype=torch.bfloat16, device=dev) for _ in range(4)]
+            for _ in range(L)]
+    lin = K.KVCache(L, H, D, W, device=dev)
+    ring = K.kvr_ring_init()
+    ping = [0]
+
+    def upkeep(layer, k, v):
+        a = wins[layer]
+        s = ping[0]
+        K.naive_upkeep(a[2 * s], a[2 * s + 1], k[layer], v[layer], ring.n_valid, ring.pos_next, rope,
+                       a[2 - 2 * s], a[3 - 2 * s], lin.k_codes[layer], lin.v_codes[layer],
+                       lin.k_scales[layer], lin.v_scales[layer])
+
+    for s in range(pre):
+        k, v = chunks[s % len(chunks)]
+        for layer in range(L):
+            upkeep(layer, k, v)
+        ping[0] = 1 - ping[0]
+        K.kvr_ring_after_write(ring, W, N)
+    torch.cuda.synchronize()
+
+    def nstep(sidx, with_attn=True):
+        k, v = chunks[sidx % len(chunks)]
+        n_valid = min(ring.n_valid + N, W)
+        for p in range(P):
+            for layer in range(L):
+                upkeep(layer, k, v)
+                if with_attn:
+                    K.attn_fp8_window(lin, layer, 0, n_valid, qpool[p * L + layer], ring.pos_next, rope,
+                                      out=outs[layer], n_splits=args.splits, ws=ws)
+        ping[0] = 1 - ping[0]
+        K.kvr_ring_after_write(ring, W, N)
+
+    sidx = pre
+    nstep(sidx)
+    sidx += 1
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.naive_steps):
+        nstep(sidx)
+        sidx += 1
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.naive_steps
+    e0.record()
+    for _ in range(args.naive_steps):
+        nstep(sidx, with_attn=False)
+        sidx += 1
+    e1.record()
+    torch.cuda.synchronize()
+    up_ms = e0.elapsed_time(e1) / args.naive_steps
+    call_bytes = 2 * H * W * D * 2 * 2 + 2 * H * W * D + 2 * H * W * 4
+    gbs = P * L * call_bytes / (up_ms * 1e-3) / 1e9
+    log(f"naive: {ms_step:.3f} ms/step, upkeep {up_ms:.3f} ms/step = {gbs:.0f} GB/s")
+    del wins, lin
+    return {"ms_per_step": round(ms_step, 4), "upkeep_ms_per_step": round(up_ms, 4),
+            "upkeep_GBps": round(gbs, 1), "upkeep_frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes_per_call": call_bytes}
+
+
+def cpu_baseline(K, inputs, shp, cache, qpool, ring, chunks, torch):
+    """The oracle, as it stands, on one full attention call and one layer's write."""
+    import numpy as np
+
+    import oracle
+    L, H, D, W, N, P = shp.n_layers, shp.n_heads, shp.head_dim, shp.window, shp.n_new, shp.passes
+    cores = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    lc = oracle.LayerCache(H, D, W)
+    lc.k_codes[:] = cache.k_codes[0].cpu().numpy()
+    lc.v_codes[:] = cache.v_codes[0].cpu().numpy()
+    lc.k_scales[:] = cache.k_scales[0].cpu().numpy()
+    lc.v_scales[:] = cache.v_scales[0].cpu().numpy()
+    q = qpool[0].float().cpu().numpy()
+    k, v = chunks[0]
+    kn, vn = k[0].float().cpu().numpy(), v[0].float().cpu().numpy()
+    start = K.kvr_ring_logical_start(ring, W)
+    t = time.perf_counter()
+    oracle.attention(lc, start, ring.n_valid, q, ring.pos_next - N)
+    t_attn = time.perf_counter() - t
+    t = time.perf_counter()
+    oracle.write(lc.copy(), 0, ring.pos_next, kn, vn)
+    t_write = time.perf_counter() - t
+    ms = (P * L * t_attn + L * t_write) * 1e3
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    log(f"oracle: attention call {t_attn:.2f} s, layer write {t_write * 1e3:.1f} ms -> {ms:.0f} ms/step")
+    return {"value": round(ms, 1), "unit": "ms/step", "cores": min(threads, cores), "kind": "oracle",
+            "sample": "one full attention call (757 queries x 12 heads x 5788 keys, fp64) and one "
+                      "layer's write, timed on the host, scaled x240 calls and x60 layers "
+                      "(extrapolated)",
+            "attention_call_s": round(t_attn, 3), "layer_write_ms": round(t_write * 1e3, 2)}
+
+
+if __name__ == "__main__":
+    main()

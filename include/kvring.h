@@ -1,0 +1,203 @@
+/*
+ * kvring.h -- C ABI of libkvring.so: write-time RoPE + FP8 ring KV cache,
+ * delta rebase and FP8 window attention for one AMD MI355X (gfx950).
+ *
+ * The method (page references, cited by title and section):
+ *   [AI-cache]   ai.info, "Characters funziona in tempo reale su quattro H100,
+ *                afferma Runway", section "La gestione della cache spostata al
+ *                momento della scrittura": the cache is a circular buffer so the
+ *                window advances without copies; rotary position encoding and
+ *                FP8 quantisation are applied once, when a frame enters the
+ *                cache; positions reset every 42 steps and each reset applies a
+ *                single delta rotation to the stored window.
+ *   [NC-cache]   neurocartel.com blog "Runway Characters ... 4 H100", section
+ *                "Кэш: 240 attention calls и работа на запись": 240 attention
+ *                calls per step, each over 5788 slots of which 757 are new.
+ *   [WC]         wechild.cn news item 1943: the original implementation
+ *                re-applied RoPE, re-quantised and shifted the window on every
+ *                call.
+ *   [AI-latency] same ai.info page, section "Latenza dei turni e altre
+ *                configurazioni GPU": FP8 attention that accepts per-head scales.
+ *
+ * Conventions shared by every entry point
+ *   - All device pointers are caller-owned device memory (hipMalloc or a
+ *     framework allocator); the library never allocates or frees.  Host
+ *     pointers are marked "host".
+ *   - Every launch is asynchronous on `stream` (a hipStream_t; NULL = the
+ *     default stream).  Nothing synchronises; outputs are ready when the
+ *     stream reaches that point.
+ *   - No global mutable state: calls are re-entrant and thread-safe, except
+ *     that calls writing the same buffers must be ordered by the caller.
+ *   - Arguments are validated on the host before any launch; on error nothing
+ *     is launched and a negative status is returned, with a message available
+ *     from kvr_last_error() (thread-local).
+ *   - Cache layout (one K and one V buffer pair per cache):
+ *       codes  uint8  [n_layers][n_heads][window][head_dim]   OCP E4M3 bytes
+ *       scales float  [n_layers][n_heads][window]             dequant factor
+ *     A stored element decodes to e4m3(code) * scale, scale = row absmax / 448.
+ *   - head_dim is 64 or 128; window and n_new are >= 1 and < 2^24.
+ */
+#ifndef KVRING_H
+#define KVRING_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define KVR_OK            0
+#define KVR_EINVAL       -1   /* null pointer, size or range out of bounds        */
+#define KVR_EALIGN       -2   /* pointer not 16-byte aligned                      */
+#define KVR_EUNSUPPORTED -3   /* head_dim not in {64,128}, unknown dtype          */
+#define KVR_ELAUNCH      -4   /* a HIP launch failed (text in kvr_last_error)     */
+
+typedef enum { KVR_F32 = 0, KVR_BF16 = 1 } kvr_dtype;
+
+/* Device cache buffers and their shape.  [AI-cache] */
+typedef struct {
+    uint8_t *k_codes;   /* [L][H][W][D] */
+    uint8_t *v_codes;   /* [L][H][W][D] */
+    float   *k_scales;  /* [L][H][W]    */
+    float   *v_scales;  /* [L][H][W]    */
+    int32_t  n_layers, n_heads, head_dim, window;
+} kvr_cache;
+
+/* Ring state, a host POD shared by all layers of a cache.  [AI-cache]
+ *   head     : slot the next new token goes to
+ *   n_valid  : number of valid slots (<= window); the valid slots, oldest
+ *              first, are (head - n_valid + i) mod window, i < n_valid
+ *   pos_next : rotary position of the next new token                      */
+typedef struct {
+    int32_t head;
+    int32_t n_valid;
+    int64_t pos_next;
+} kvr_ring;
+
+/* Device table of fp32 (cos, sin) pairs of the rotary angles of a range of
+ * positions: cs[(p - pos0) * head_dim/2 + i] = (cos, sin)(p * theta_i) with
+ * theta_i = base^(-2i/head_dim), the angle formed in fp64 and cos/sin
+ * evaluated in fp64 then rounded to fp32.  Filled by kv_rope_table_fill. */
+typedef struct {
+    const float *cs;    /* device, [n_pos][head_dim/2][2] */
+    int64_t      pos0;  /* first position held */
+    int32_t      n_pos; /* number of positions held */
+    int32_t      head_dim;
+    double       base;  /* rotary base, 10000 for the workloads here */
+} kvr_rope_table;
+
+/* ---- (a1) ring bookkeeping: pure host integer code, no GPU ----------------
+ * [AI-cache]: a circular buffer; new token j of a chunk goes to slot
+ * (head + j) mod window; after a chunk of n_new tokens the head advances by
+ * n_new (mod window), n_valid grows to at most window and pos_next grows by
+ * n_new; a position reset by delta lowers pos_next by delta. */
+void    kvr_ring_init(kvr_ring *r);                                  /* all zero */
+/* Slot of new token j (0 <= j < window) of the next chunk; -1 on bad input. */
+int32_t kvr_ring_slot(const kvr_ring *r, int32_t window, int32_t j);
+/* Slot of the oldest valid token, (head - n_valid) mod window; -1 on bad input. */
+int32_t kvr_ring_logical_start(const kvr_ring *r, int32_t window);
+/* Advance the ring past a written chunk.  KVR_EINVAL if n_new not in [1, window]
+ * or the state is out of range. */
+int32_t kvr_ring_after_write(kvr_ring *r, int32_t window, int32_t n_new);
+/* Record a position reset by delta (pos_next -= delta); head and n_valid keep. */
+int32_t kvr_ring_after_rebase(kvr_ring *r, int64_t delta);
+
+/* ---- rotary table --------------------------------------------------------
+ * Fills `cs` (device, n_pos * head_dim/2 float pairs) for positions
+ * pos0 .. pos0 + n_pos - 1 (see kvr_rope_table).  [AI-cache] */
+int32_t kv_rope_table_fill(float *cs, int64_t pos0, int32_t n_pos, int32_t head_dim,
+                           double base, void *stream);
+
+/* ---- (a2) write-time RoPE + FP8 ------------------------------------------
+ * [AI-cache] [NC-cache] [WC].  For layers layer0 .. layer0+n_layers-1 and new
+ * tokens j < n_new: K row (j, h) is rotated at position before->pos_next + j
+ * (pairs (x[2i], x[2i+1]) by angle p * theta_i, fp32, no FMA), then K and V
+ * rows are quantised (a = row absmax; scale = a / 448; code = E4M3 RNE of
+ * y * (448 / a); a == 0 gives scale 0 and zero codes) and stored at slot
+ * (before->head + j) mod window.  The ring itself is not modified: call
+ * kvr_ring_after_write afterwards.
+ *   k_new, v_new : device, per layer [n_new][n_heads][head_dim] of `dtype`,
+ *                  layer l at element offset (l - layer0) * layer_stride_elems;
+ *                  16-byte aligned; layer_stride_elems a multiple of 8.
+ *   rope         : device table covering positions pos_next .. pos_next+n_new-1.
+ * Errors: KVR_EINVAL (null, n_new not in [1, window], layer range, table range,
+ * table shape), KVR_EALIGN, KVR_EUNSUPPORTED. */
+int32_t kv_write_rope_quant(const kvr_cache *cache, const kvr_ring *before,
+                            int32_t layer0, int32_t n_layers,
+                            const void *k_new, const void *v_new, kvr_dtype dtype,
+                            int64_t layer_stride_elems, int32_t n_new,
+                            const kvr_rope_table *rope, void *stream);
+
+/* ---- (a4) delta rebase on a position reset -------------------------------
+ * [AI-cache].  Every valid K row of layers layer0 .. layer0+n_layers-1 (the
+ * ring's n_valid slots) is dequantised (e4m3(code) * scale, fp32), rotated by
+ * -delta (cos/sin of -delta * theta_i formed in fp64, rounded to fp32; fp32
+ * rotation, no FMA) and re-quantised as in kv_write_rope_quant.  V rows are
+ * not touched (V carries no rotation).  Afterwards call kvr_ring_after_rebase.
+ * Errors: KVR_EINVAL, KVR_EUNSUPPORTED. */
+int32_t kv_delta_rebase(const kvr_cache *cache, const kvr_ring *ring, int32_t layer0,
+                        int32_t n_layers, int64_t delta, double rope_base, void *stream);
+
+/* ---- (a3) FP8 window attention -------------------------------------------
+ * [AI-cache] [NC-cache] [AI-latency].  For every head h and query i < n_q:
+ *   O[i][h] = sum_j softmax_j(softmax_scale * q_i . k^_j) v^_j
+ * over the n_valid cached keys of `layer` at slots (slot_start + j) mod window
+ * (non-causal; every query sees every valid key), q_i rotated at position
+ * q_pos_start + i, k^ / v^ the dequantised cache rows.  Keys are visited in
+ * this logical order, so a linear window (slot_start = 0) holding the same
+ * rows gives a bit-identical result.
+ * On the GPU, Q is split into two E4M3 terms (hi + lo, one scale per call
+ * block) and the softmax weights likewise (hi + lo, with the per-key V scale
+ * folded in), so both products run on FP8 matrix cores with fp32
+ * accumulation and an online softmax.
+ *   q       : device [n_q][n_heads][head_dim] of `dtype`, 16-byte aligned.
+ *   out     : device bf16 [n_q][n_heads][head_dim] (uint16 storage).
+ *   n_splits: key-range splits per (head, query block); 0 picks one for the
+ *             shape.  With more than one split, partial results go to `ws`
+ *             and a second kernel combines them in a fixed order.
+ *   ws      : device workspace of attn_fp8_window_workspace_bytes(...) bytes
+ *             (may be NULL when that is 0), 256-byte aligned.
+ * Errors: KVR_EINVAL (null, n_valid not in [1, window], slot_start out of
+ * range, table range, workspace too small), KVR_EALIGN, KVR_EUNSUPPORTED. */
+size_t  attn_fp8_window_workspace_bytes(const kvr_cache *cache, int32_t n_q, int32_t n_valid,
+                                        int32_t n_splits);
+int32_t attn_fp8_window(const kvr_cache *cache, int32_t layer, int32_t slot_start,
+                        int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
+                        int64_t q_pos_start, float softmax_scale, const kvr_rope_table *rope,
+                        uint16_t *out, int32_t n_splits, void *ws, size_t ws_bytes,
+                        void *stream);
+
+/* ---- (a5) naive per-call upkeep (the original implementation) ------------
+ * [WC] [AI-cache] [NC-cache].  Shift the linear, un-rotated window: the new
+ * window is src rows [drop, n_valid_before) followed by the n_new new rows,
+ * drop = max(0, n_valid_before + n_new - window); write it to lin_*_dst, then
+ * rotate every K row at its absolute position (row i at
+ * pos_next_before + n_new - n_after + i, n_after = min(n_valid_before + n_new,
+ * window)) and quantise every K and V row exactly as kv_write_rope_quant does,
+ * into linear codes [n_heads][window][head_dim] and scales [n_heads][window].
+ *   lin_*_src, lin_*_dst : device [n_heads][window][head_dim] of `dtype`;
+ *                          src and dst must not overlap (ping-pong buffers).
+ *   k_new, v_new         : device [n_new][n_heads][head_dim] of `dtype`.
+ *   rope                 : table covering the n_after positions.
+ * Errors: KVR_EINVAL, KVR_EALIGN, KVR_EUNSUPPORTED. */
+int32_t naive_upkeep(const void *lin_k_src, const void *lin_v_src,
+                     const void *k_new, const void *v_new, kvr_dtype dtype, int32_t n_new,
+                     int32_t n_valid_before, int64_t pos_next_before,
+                     int32_t n_heads, int32_t head_dim, int32_t window,
+                     const kvr_rope_table *rope,
+                     void *lin_k_dst, void *lin_v_dst,
+                     uint8_t *k_codes, uint8_t *v_codes, float *k_scales, float *v_scales,
+                     void *stream);
+
+/* Text of the last error on this thread ("" if none). */
+const char *kvr_last_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char *kvr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVRING_H */

@@ -1,0 +1,72 @@
+// kvr_internal.h -- launch helpers shared by the host entry points and the
+// HIP kernels of libkvring.  Not part of the public ABI (include/kvring.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvring.h"
+
+namespace kvr {
+
+constexpr int kMaxHalfDim = 64;      // head_dim <= 128
+
+struct ThetaTable {                  // theta_i = base^(-2i/D), fp64, formed on the host
+    double t[kMaxHalfDim];
+};
+
+struct CosSinTable {                 // (cos, sin) pairs of one rotation, fp32
+    float cs[2 * kMaxHalfDim];
+};
+
+// ---- upkeep.hip ----------------------------------------------------------
+hipError_t launch_rope_table(float *cs, int64_t pos0, int32_t n_pos, int32_t head_dim,
+                             const ThetaTable &theta, hipStream_t s);
+
+struct WriteArgs {
+    uint8_t *k_codes, *v_codes;
+    float *k_scales, *v_scales;
+    const void *k_new, *v_new;
+    int64_t layer_stride;            // elements between consecutive layers of k_new/v_new
+    const float *cs;                 // rotary table row of position pos_next (pair-major)
+    int32_t n_heads, window, head, n_new, layer0, n_layers;
+    int32_t dtype;
+};
+hipError_t launch_write(const WriteArgs &a, int head_dim, hipStream_t s);
+
+struct RebaseArgs {
+    uint8_t *k_codes;
+    float *k_scales;
+    int32_t n_heads, window, start, n_valid, layer0, n_layers;
+};
+hipError_t launch_rebase(const RebaseArgs &a, const CosSinTable &rot, int head_dim, hipStream_t s);
+
+struct NaiveArgs {
+    const void *k_src, *v_src, *k_new, *v_new;
+    void *k_dst, *v_dst;
+    uint8_t *k_codes, *v_codes;
+    float *k_scales, *v_scales;
+    const float *cs;                 // rotary table row of the window's first position
+    int32_t n_heads, window, n_new, n_after, kept, drop;
+    int32_t dtype;
+};
+hipError_t launch_naive(const NaiveArgs &a, int head_dim, hipStream_t s);
+
+// ---- attention.hip -------------------------------------------------------
+struct AttnArgs {
+    const uint8_t *k_codes, *v_codes; // this layer: [H][W][D]
+    const float *k_scales, *v_scales; // this layer: [H][W]
+    const void *q;                    // [n_q][H][D]
+    const float *cs;                  // rotary table row of position q_pos_start
+    uint16_t *out;                    // [n_q][H][D] bf16
+    float *part_o;                    // [splits][n_q][H][D]
+    float *part_ml;                   // [splits][n_q][H][2]
+    int32_t n_heads, window, slot_start, n_valid, n_q, dtype;
+    int32_t n_splits, tiles_per_split;
+    float softmax_scale;
+};
+int attn_default_splits(int n_heads, int n_q, int n_valid);
+size_t attn_workspace_bytes(int n_heads, int head_dim, int n_q, int n_splits);
+hipError_t launch_attention(const AttnArgs &a, int head_dim, hipStream_t s);
+
+}  // namespace kvr

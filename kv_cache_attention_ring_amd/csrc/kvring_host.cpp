@@ -1,0 +1,365 @@
+// kvring_host.cpp -- host side of libkvring: ring bookkeeping, argument
+// validation and kernel launches for the entry points of include/kvring.h.
+//
+// Page references (cited by title and section):
+//   [AI-cache] ai.info, "Characters funziona in tempo reale su quattro H100,
+//              afferma Runway", section "La gestione della cache spostata al
+//              momento della scrittura" (circular buffer, write-time RoPE and
+//              FP8, one delta rotation per position reset).
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kvr_internal.h"
+#include "kvring.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int32_t fail(int32_t code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int32_t ok() {
+    g_err[0] = '\0';
+    return KVR_OK;
+}
+
+int32_t launch_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(KVR_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int32_t kMaxExtent = 1 << 24;
+
+int32_t check_head_dim(int32_t D) {
+    if (D != 64 && D != 128) return fail(KVR_EUNSUPPORTED, "head_dim %d not in {64,128}", D);
+    return KVR_OK;
+}
+
+int32_t check_cache(const kvr_cache *c) {
+    if (!c) return fail(KVR_EINVAL, "cache is NULL");
+    if (int32_t r = check_head_dim(c->head_dim)) return r;
+    if (!c->k_codes || !c->v_codes || !c->k_scales || !c->v_scales)
+        return fail(KVR_EINVAL, "cache buffer pointer is NULL");
+    if (!aligned16(c->k_codes) || !aligned16(c->v_codes) || !aligned16(c->k_scales) ||
+        !aligned16(c->v_scales))
+        return fail(KVR_EALIGN, "cache buffers must be 16-byte aligned");
+    if (c->n_layers < 1 || c->n_heads < 1 || c->window < 1 || c->window >= kMaxExtent ||
+        c->n_heads >= kMaxExtent || c->n_layers >= kMaxExtent)
+        return fail(KVR_EINVAL, "cache shape out of range (L=%d H=%d W=%d)", c->n_layers,
+                    c->n_heads, c->window);
+    return KVR_OK;
+}
+
+int32_t check_ring(const kvr_ring *r, int32_t W) {
+    if (!r) return fail(KVR_EINVAL, "ring is NULL");
+    if (r->head < 0 || r->head >= W) return fail(KVR_EINVAL, "ring head %d not in [0,%d)", r->head, W);
+    if (r->n_valid < 0 || r->n_valid > W)
+        return fail(KVR_EINVAL, "ring n_valid %d not in [0,%d]", r->n_valid, W);
+    return KVR_OK;
+}
+
+int32_t check_dtype(kvr_dtype dt) {
+    if (dt != KVR_F32 && dt != KVR_BF16) return fail(KVR_EUNSUPPORTED, "unknown dtype %d", (int)dt);
+    return KVR_OK;
+}
+
+// Table rows for positions [p0, p0 + n) must exist; returns the row pointer.
+int32_t table_rows(const kvr_rope_table *t, int32_t D, int64_t p0, int64_t n, const float **row) {
+    if (!t || !t->cs) return fail(KVR_EINVAL, "rotary table is NULL");
+    if (t->head_dim != D)
+        return fail(KVR_EINVAL, "rotary table head_dim %d != %d", t->head_dim, D);
+    if (!aligned16(t->cs)) return fail(KVR_EALIGN, "rotary table must be 16-byte aligned");
+    if (p0 < t->pos0 || p0 + n > t->pos0 + (int64_t)t->n_pos)
+        return fail(KVR_EINVAL, "positions [%lld,%lld) outside rotary table [%lld,%lld)",
+                    (long long)p0, (long long)(p0 + n), (long long)t->pos0,
+                    (long long)(t->pos0 + t->n_pos));
+    *row = t->cs + (p0 - t->pos0) * D;
+    return KVR_OK;
+}
+
+kvr::ThetaTable make_theta(int32_t D, double base) {
+    kvr::ThetaTable th{};
+    for (int i = 0; i < D / 2; ++i) th.t[i] = pow(base, -2.0 * (double)i / (double)D);
+    return th;
+}
+
+// Number of key-range splits actually used: the requested count (0 = the
+// shape's default) clamped to the number of 64-key tiles, then reduced so
+// that no split is empty.  *tps receives the tiles per split.
+int32_t effective_splits(int32_t n_heads, int32_t n_q, int32_t n_valid, int32_t requested,
+                         int32_t *tps) {
+    const int32_t tiles = (n_valid + 63) / 64;
+    int32_t s = requested > 0 ? requested : kvr::attn_default_splits(n_heads, n_q, n_valid);
+    if (s > tiles) s = tiles;
+    if (s < 1) s = 1;
+    *tps = (tiles + s - 1) / s;
+    return (tiles + *tps - 1) / *tps;
+}
+
+int32_t mod_w(int64_t x, int32_t W) {
+    int64_t r = x % W;
+    return (int32_t)(r < 0 ? r + W : r);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kvr_last_error(void) { return g_err; }
+
+const char *kvr_version(void) { return "0.1.0"; }
+
+// ---- (a1) ring bookkeeping [AI-cache] -----------------------------------
+void kvr_ring_init(kvr_ring *r) {
+    if (r) {
+        r->head = 0;
+        r->n_valid = 0;
+        r->pos_next = 0;
+    }
+}
+
+int32_t kvr_ring_slot(const kvr_ring *r, int32_t window, int32_t j) {
+    if (!r || window < 1 || j < 0 || j >= window || r->head < 0 || r->head >= window) return -1;
+    return mod_w((int64_t)r->head + j, window);
+}
+
+int32_t kvr_ring_logical_start(const kvr_ring *r, int32_t window) {
+    if (!r || window < 1 || r->head < 0 || r->head >= window || r->n_valid < 0 ||
+        r->n_valid > window)
+        return -1;
+    return mod_w((int64_t)r->head - r->n_valid, window);
+}
+
+int32_t kvr_ring_after_write(kvr_ring *r, int32_t window, int32_t n_new) {
+    if (window < 1) return fail(KVR_EINVAL, "window %d < 1", window);
+    if (int32_t e = check_ring(r, window)) return e;
+    if (n_new < 1 || n_new > window) return fail(KVR_EINVAL, "n_new %d not in [1,%d]", n_new, window);
+    r->head = mod_w((int64_t)r->head + n_new, window);
+    r->n_valid = r->n_valid + n_new < window ? r->n_valid + n_new : window;
+    r->pos_next += n_new;
+    return ok();
+}
+
+int32_t kvr_ring_after_rebase(kvr_ring *r, int64_t delta) {
+    if (!r) return fail(KVR_EINVAL, "ring is NULL");
+    r->pos_next -= delta;
+    return ok();
+}
+
+// ---- rotary table -------------------------------------------------------
+int32_t kv_rope_table_fill(float *cs, int64_t pos0, int32_t n_pos, int32_t head_dim, double base,
+                           void *stream) {
+    if (int32_t e = check_head_dim(head_dim)) return e;
+    if (!cs) return fail(KVR_EINVAL, "table pointer is NULL");
+    if (!aligned16(cs)) return fail(KVR_EALIGN, "table must be 16-byte aligned");
+    if (n_pos < 1) return fail(KVR_EINVAL, "n_pos %d < 1", n_pos);
+    if (!(base > 1.0) || !isfinite(base)) return fail(KVR_EINVAL, "rotary base must be > 1");
+    return launch_status(kvr::launch_rope_table(cs, pos0, n_pos, head_dim,
+                                                make_theta(head_dim, base),
+                                                static_cast<hipStream_t>(stream)),
+                         "rope table");
+}
+
+// ---- (a2) write-time RoPE + FP8 [AI-cache] -------------------------------
+int32_t kv_write_rope_quant(const kvr_cache *cache, const kvr_ring *before, int32_t layer0,
+                            int32_t n_layers, const void *k_new, const void *v_new,
+                            kvr_dtype dtype, int64_t layer_stride_elems, int32_t n_new,
+                            const kvr_rope_table *rope, void *stream) {
+    if (int32_t e = check_cache(cache)) return e;
+    const int32_t W = cache->window, D = cache->head_dim;
+    if (int32_t e = check_ring(before, W)) return e;
+    if (int32_t e = check_dtype(dtype)) return e;
+    if (!k_new || !v_new) return fail(KVR_EINVAL, "k_new/v_new is NULL");
+    if (!aligned16(k_new) || !aligned16(v_new)) return fail(KVR_EALIGN, "k_new/v_new not 16-byte aligned");
+    if (n_new < 1 || n_new > W) return fail(KVR_EINVAL, "n_new %d not in [1,%d]", n_new, W);
+    if (layer0 < 0 || n_layers < 1 || layer0 + n_layers > cache->n_layers)
+        return fail(KVR_EINVAL, "layers [%d,%d) outside cache of %d", layer0, layer0 + n_layers,
+                    cache->n_layers);
+    const int64_t per_layer = (int64_t)n_new * cache->n_heads * D;
+    if (n_layers > 1 && (layer_stride_elems < per_layer || layer_stride_elems % 8 != 0))
+        return fail(KVR_EINVAL, "layer_stride_elems %lld must be >= %lld and a multiple of 8",
+                    (long long)layer_stride_elems, (long long)per_layer);
+    const float *cs;
+    if (int32_t e = table_rows(rope, D, before->pos_next, n_new, &cs)) return e;
+    kvr::WriteArgs a{};
+    a.k_codes = cache->k_codes;
+    a.v_codes = cache->v_codes;
+    a.k_scales = cache->k_scales;
+    a.v_scales = cache->v_scales;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.layer_stride = n_layers > 1 ? layer_stride_elems : 0;
+    a.cs = cs;
+    a.n_heads = cache->n_heads;
+    a.window = W;
+    a.head = before->head;
+    a.n_new = n_new;
+    a.layer0 = layer0;
+    a.n_layers = n_layers;
+    a.dtype = dtype;
+    return launch_status(kvr::launch_write(a, D, static_cast<hipStream_t>(stream)), "write");
+}
+
+// ---- (a4) delta rebase [AI-cache] ---------------------------------------
+int32_t kv_delta_rebase(const kvr_cache *cache, const kvr_ring *ring, int32_t layer0,
+                        int32_t n_layers, int64_t delta, double rope_base, void *stream) {
+    if (int32_t e = check_cache(cache)) return e;
+    const int32_t W = cache->window, D = cache->head_dim;
+    if (int32_t e = check_ring(ring, W)) return e;
+    if (layer0 < 0 || n_layers < 1 || layer0 + n_layers > cache->n_layers)
+        return fail(KVR_EINVAL, "layers [%d,%d) outside cache of %d", layer0, layer0 + n_layers,
+                    cache->n_layers);
+    if (!(rope_base > 1.0) || !isfinite(rope_base)) return fail(KVR_EINVAL, "rotary base must be > 1");
+    if (ring->n_valid == 0) return ok();
+    // cos/sin of -delta * theta_i: fp64 angle and trig, rounded to fp32
+    kvr::CosSinTable rot{};
+    const kvr::ThetaTable th = make_theta(D, rope_base);
+    for (int i = 0; i < D / 2; ++i) {
+        const double ang = (double)(-delta) * th.t[i];
+        rot.cs[2 * i] = (float)cos(ang);
+        rot.cs[2 * i + 1] = (float)sin(ang);
+    }
+    kvr::RebaseArgs a{};
+    a.k_codes = cache->k_codes;
+    a.k_scales = cache->k_scales;
+    a.n_heads = cache->n_heads;
+    a.window = W;
+    a.start = kvr_ring_logical_start(ring, W);
+    a.n_valid = ring->n_valid;
+    a.layer0 = layer0;
+    a.n_layers = n_layers;
+    return launch_status(kvr::launch_rebase(a, rot, D, static_cast<hipStream_t>(stream)), "rebase");
+}
+
+// ---- (a3) FP8 window attention --------------------------------------------
+size_t attn_fp8_window_workspace_bytes(const kvr_cache *cache, int32_t n_q, int32_t n_valid,
+                                       int32_t n_splits) {
+    if (!cache || n_q < 1 || n_valid < 1 || n_splits < 0) return 0;
+    int32_t tps;
+    n_splits = effective_splits(cache->n_heads, n_q, n_valid, n_splits, &tps);
+    return kvr::attn_workspace_bytes(cache->n_heads, cache->head_dim, n_q, n_splits);
+}
+
+int32_t attn_fp8_window(const kvr_cache *cache, int32_t layer, int32_t slot_start,
+                        int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
+                        int64_t q_pos_start, float softmax_scale, const kvr_rope_table *rope,
+                        uint16_t *out, int32_t n_splits, void *ws, size_t ws_bytes,
+                        void *stream) {
+    if (int32_t e = check_cache(cache)) return e;
+    const int32_t W = cache->window, D = cache->head_dim;
+    if (int32_t e = check_dtype(dtype)) return e;
+    if (layer < 0 || layer >= cache->n_layers)
+        return fail(KVR_EINVAL, "layer %d outside cache of %d", layer, cache->n_layers);
+    if (n_valid < 1 || n_valid > W) return fail(KVR_EINVAL, "n_valid %d not in [1,%d]", n_valid, W);
+    if (slot_start < 0 || slot_start >= W)
+        return fail(KVR_EINVAL, "slot_start %d not in [0,%d)", slot_start, W);
+    if (n_q < 1 || n_q >= kMaxExtent) return fail(KVR_EINVAL, "n_q %d out of range", n_q);
+    if (!q || !out) return fail(KVR_EINVAL, "q/out is NULL");
+    if (!aligned16(q) || !aligned16(out)) return fail(KVR_EALIGN, "q/out not 16-byte aligned");
+    if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale))
+        return fail(KVR_EINVAL, "softmax_scale must be positive and finite");
+    const float *cs;
+    if (int32_t e = table_rows(rope, D, q_pos_start, n_q, &cs)) return e;
+    if (n_splits < 0) return fail(KVR_EINVAL, "n_splits %d < 0", n_splits);
+    int32_t tps;
+    n_splits = effective_splits(cache->n_heads, n_q, n_valid, n_splits, &tps);
+    const size_t need = kvr::attn_workspace_bytes(cache->n_heads, D, n_q, n_splits);
+    if (need > 0) {
+        if (!ws) return fail(KVR_EINVAL, "workspace of %zu bytes required", need);
+        if (ws_bytes < need) return fail(KVR_EINVAL, "workspace %zu < %zu bytes", ws_bytes, need);
+        if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+            return fail(KVR_EALIGN, "workspace must be 256-byte aligned");
+    }
+    kvr::AttnArgs a{};
+    const int64_t lay = (int64_t)layer * cache->n_heads * W;
+    a.k_codes = cache->k_codes + lay * D;
+    a.v_codes = cache->v_codes + lay * D;
+    a.k_scales = cache->k_scales + lay;
+    a.v_scales = cache->v_scales + lay;
+    a.q = q;
+    a.cs = cs;
+    a.out = out;
+    a.n_heads = cache->n_heads;
+    a.window = W;
+    a.slot_start = slot_start;
+    a.n_valid = n_valid;
+    a.n_q = n_q;
+    a.dtype = dtype;
+    a.n_splits = n_splits;
+    a.tiles_per_split = tps;
+    a.softmax_scale = softmax_scale;
+    if (n_splits > 1) {
+        a.part_o = static_cast<float *>(ws);
+        a.part_ml = a.part_o + (size_t)n_splits * n_q * cache->n_heads * D;
+    }
+    return launch_status(kvr::launch_attention(a, D, static_cast<hipStream_t>(stream)), "attention");
+}
+
+// ---- (a5) naive per-call upkeep -------------------------------------------
+int32_t naive_upkeep(const void *lin_k_src, const void *lin_v_src, const void *k_new,
+                     const void *v_new, kvr_dtype dtype, int32_t n_new, int32_t n_valid_before,
+                     int64_t pos_next_before, int32_t n_heads, int32_t head_dim, int32_t window,
+                     const kvr_rope_table *rope, void *lin_k_dst, void *lin_v_dst,
+                     uint8_t *k_codes, uint8_t *v_codes, float *k_scales, float *v_scales,
+                     void *stream) {
+    if (int32_t e = check_head_dim(head_dim)) return e;
+    if (int32_t e = check_dtype(dtype)) return e;
+    if (window < 1 || window >= kMaxExtent || n_heads < 1 || n_heads >= kMaxExtent)
+        return fail(KVR_EINVAL, "shape out of range (H=%d W=%d)", n_heads, window);
+    if (n_new < 1 || n_new > window) return fail(KVR_EINVAL, "n_new %d not in [1,%d]", n_new, window);
+    if (n_valid_before < 0 || n_valid_before > window)
+        return fail(KVR_EINVAL, "n_valid_before %d not in [0,%d]", n_valid_before, window);
+    const void *ptrs[] = {lin_k_src, lin_v_src, k_new, v_new, lin_k_dst, lin_v_dst,
+                          k_codes, v_codes, k_scales, v_scales};
+    for (const void *p : ptrs) {
+        if (!p) return fail(KVR_EINVAL, "naive_upkeep: NULL buffer");
+        if (!aligned16(p)) return fail(KVR_EALIGN, "naive_upkeep: buffer not 16-byte aligned");
+    }
+    const size_t esz = dtype == KVR_BF16 ? 2 : 4;
+    const size_t win_bytes = (size_t)n_heads * window * head_dim * esz;
+    auto overlap = [&](const void *a, const void *b) {
+        const char *x = static_cast<const char *>(a), *y = static_cast<const char *>(b);
+        return x < y + win_bytes && y < x + win_bytes;
+    };
+    if (overlap(lin_k_src, lin_k_dst) || overlap(lin_v_src, lin_v_dst))
+        return fail(KVR_EINVAL, "naive_upkeep: src and dst windows overlap");
+    const int32_t n_after = n_valid_before + n_new < window ? n_valid_before + n_new : window;
+    const int32_t drop = n_valid_before + n_new - n_after;
+    const float *cs;
+    if (int32_t e = table_rows(rope, head_dim, pos_next_before + n_new - n_after, n_after, &cs))
+        return e;
+    kvr::NaiveArgs a{};
+    a.k_src = lin_k_src;
+    a.v_src = lin_v_src;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_dst = lin_k_dst;
+    a.v_dst = lin_v_dst;
+    a.k_codes = k_codes;
+    a.v_codes = v_codes;
+    a.k_scales = k_scales;
+    a.v_scales = v_scales;
+    a.cs = cs;
+    a.n_heads = n_heads;
+    a.window = window;
+    a.n_new = n_new;
+    a.n_after = n_after;
+    a.kept = n_valid_before - drop;
+    a.drop = drop;
+    a.dtype = dtype;
+    return launch_status(kvr::launch_naive(a, head_dim, static_cast<hipStream_t>(stream)), "naive");
+}
+
+}  // extern "C"

@@ -1,0 +1,340 @@
+// upkeep.hip -- memory-bound cache upkeep kernels for gfx950 (CDNA4):
+//   rotary (cos, sin) table, write-time RoPE + FP8 of a new chunk, the delta
+//   rebase of the stored K window, and the naive per-call window rebuild.
+//
+// Page references (cited by title and section):
+//   [AI-cache] ai.info, "Characters funziona in tempo reale su quattro H100,
+//              afferma Runway", section "La gestione della cache spostata al
+//              momento della scrittura".
+//   [WC]       wechild.cn news item 1943 (original per-call upkeep).
+//
+// Every row of head_dim elements is handled by 8 consecutive lanes, each lane
+// owning head_dim/8 contiguous elements (16-byte loads and stores); the row
+// absmax is a 3-step butterfly across those 8 lanes.  The arithmetic order
+// of one element is fixed (rotation: x0*c - x1*s, x0*s + x1*c, each product
+// and sum rounded to fp32; quantisation: y * (448 / absmax) rounded to fp32,
+// then E4M3 round-to-nearest-even via v_cvt_pk_fp8_f32), and this file is
+// built with -ffp-contract=off so no FMA merges those roundings.  The write,
+// rebase and naive kernels share these device helpers, so the ring cache and
+// the naive linear window are bit-identical.
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "kvr_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace kvr {
+namespace {
+
+constexpr int kRowLanes = 8;          // lanes per row
+constexpr int kBlock = 256;           // threads per workgroup
+constexpr int kRowsPerIter = kBlock / kRowLanes;
+constexpr int kTokBlock = 16;         // new tokens per write workgroup
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// A lane's chunk of EPT elements in its storage type, as 16-byte vectors.
+template <int EPT, bool BF16>
+struct RawChunk {
+    static constexpr int kVecs = EPT * (BF16 ? 2 : 4) / 16;
+    uint4 v[kVecs];
+
+    __device__ __forceinline__ void load(const void *base, int64_t elem_off) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(
+            reinterpret_cast<const char *>(base) + elem_off * (BF16 ? 2 : 4));
+#pragma unroll
+        for (int k = 0; k < kVecs; ++k) v[k] = p[k];
+    }
+    __device__ __forceinline__ void store(void *base, int64_t elem_off) const {
+        uint4 *p = reinterpret_cast<uint4 *>(reinterpret_cast<char *>(base) +
+                                             elem_off * (BF16 ? 2 : 4));
+#pragma unroll
+        for (int k = 0; k < kVecs; ++k) p[k] = v[k];
+    }
+    __device__ __forceinline__ void to_f32(float (&x)[EPT]) const {
+#pragma unroll
+        for (int k = 0; k < kVecs; ++k) {
+            const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+            if constexpr (BF16) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    x[8 * k + 2 * q] = bf16_to_f32(w[q] & 0xFFFFu);
+                    x[8 * k + 2 * q + 1] = bf16_to_f32(w[q] >> 16);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) x[4 * k + q] = __uint_as_float(w[q]);
+            }
+        }
+    }
+};
+
+// y = R(angle) x on the EPT/2 interleaved pairs; cs holds (cos, sin) per pair.
+template <int EPT>
+__device__ __forceinline__ void rotate_pairs(float (&x)[EPT], const float *cs) {
+#pragma unroll
+    for (int i = 0; i < EPT / 2; ++i) {
+        const float c = cs[2 * i], s = cs[2 * i + 1];
+        const float x0 = x[2 * i], x1 = x[2 * i + 1];
+        const float a = x0 * c;
+        const float b = x1 * s;
+        const float e = x0 * s;
+        const float f = x1 * c;
+        x[2 * i] = a - b;
+        x[2 * i + 1] = e + f;
+    }
+}
+
+// Row quantisation: absmax over the 8 lanes of the row, scale = a / 448,
+// codes = E4M3_RNE(y * (448 / a)).  Writes EPT codes and (lane 0) the scale.
+template <int EPT>
+__device__ __forceinline__ void quantize_store(const float (&y)[EPT], uint8_t *codes_dst,
+                                               float *scale_dst, bool lane0) {
+    float a = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) a = fmaxf(a, fabsf(y[e]));
+    a = fmaxf(a, __shfl_xor(a, 1, kRowLanes));
+    a = fmaxf(a, __shfl_xor(a, 2, kRowLanes));
+    a = fmaxf(a, __shfl_xor(a, 4, kRowLanes));
+    uint32_t w[EPT / 4];
+    float scale;
+    if (a == 0.0f) {
+        scale = 0.0f;
+#pragma unroll
+        for (int k = 0; k < EPT / 4; ++k) w[k] = 0u;
+    } else {
+        scale = a / 448.0f;
+        const float inv = 448.0f / a;
+#pragma unroll
+        for (int k = 0; k < EPT / 4; ++k) {
+            const float t0 = y[4 * k] * inv, t1 = y[4 * k + 1] * inv;
+            const float t2 = y[4 * k + 2] * inv, t3 = y[4 * k + 3] * inv;
+            int pk = __builtin_amdgcn_cvt_pk_fp8_f32(t0, t1, 0, false);
+            pk = __builtin_amdgcn_cvt_pk_fp8_f32(t2, t3, pk, true);
+            w[k] = (uint32_t)pk;
+        }
+    }
+    if constexpr (EPT == 16) {
+        *reinterpret_cast<uint4 *>(codes_dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+        *reinterpret_cast<uint2 *>(codes_dst) = make_uint2(w[0], w[1]);
+    }
+    if (lane0) *scale_dst = scale;
+}
+
+// Dequantise EPT codes with the row scale (fp32 product, exact decode).
+template <int EPT>
+__device__ __forceinline__ void dequant_chunk(const uint8_t *src, float scale, float (&x)[EPT]) {
+    uint32_t w[EPT / 4];
+    if constexpr (EPT == 16) {
+        uint4 u = *reinterpret_cast<const uint4 *>(src);
+        w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+    } else {
+        uint2 u = *reinterpret_cast<const uint2 *>(src);
+        w[0] = u.x; w[1] = u.y;
+    }
+#pragma unroll
+    for (int k = 0; k < EPT / 4; ++k) {
+        auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
+        auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
+        x[4 * k] = lo[0] * scale;
+        x[4 * k + 1] = lo[1] * scale;
+        x[4 * k + 2] = hi[0] * scale;
+        x[4 * k + 3] = hi[1] * scale;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Rotary table: cs[p][i] = (cos, sin)(p * theta_i), fp64 angle and trig.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kBlock) rope_table_kernel(float2 *cs, int64_t pos0,
+                                                            int32_t n_pos, int32_t half,
+                                                            ThetaTable th) {
+    const int64_t idx = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (idx >= (int64_t)n_pos * half) return;
+    const int64_t p = idx / half;
+    const int i = (int)(idx - p * half);
+    const double ang = (double)(pos0 + p) * th.t[i];
+    double s, c;
+    sincos(ang, &s, &c);
+    cs[idx] = make_float2((float)c, (float)s);
+}
+
+// ---------------------------------------------------------------------------
+// Write-time RoPE + FP8 [AI-cache].  grid = (ceil(n_new / 16), n_layers).
+// Rows of a workgroup: (kv, head, token) with the token fastest, so lanes of a
+// wave touch consecutive slots (contiguous scale stores).
+// ---------------------------------------------------------------------------
+template <int D, bool BF16>
+__global__ void __launch_bounds__(kBlock) write_kernel(WriteArgs a) {
+    constexpr int EPT = D / kRowLanes;
+    __shared__ float s_cs[kTokBlock * D];          // (cos, sin) per token and pair
+
+    const int j0 = blockIdx.x * kTokBlock;
+    const int layer = a.layer0 + blockIdx.y;
+    const int ntok = min(kTokBlock, a.n_new - j0);
+    for (int t = threadIdx.x; t < ntok * D; t += kBlock) s_cs[t] = a.cs[(int64_t)j0 * D + t];
+    __syncthreads();
+
+    const int lane8 = threadIdx.x % kRowLanes;
+    const int rows = 2 * a.n_heads * kTokBlock;
+    const int64_t lay_in = (int64_t)blockIdx.y * a.layer_stride;
+    const int64_t lay_cache = (int64_t)layer * a.n_heads * a.window;
+    for (int r = threadIdx.x / kRowLanes; r < rows; r += kRowsPerIter) {
+        const int tok = r % kTokBlock;
+        const int h = (r / kTokBlock) % a.n_heads;
+        const int kv = r / (kTokBlock * a.n_heads);
+        if (tok >= ntok) continue;
+        const int j = j0 + tok;
+        const void *src = kv ? a.v_new : a.k_new;
+        RawChunk<EPT, BF16> raw;
+        raw.load(src, lay_in + ((int64_t)j * a.n_heads + h) * D + lane8 * EPT);
+        float x[EPT];
+        raw.to_f32(x);
+        if (kv == 0) rotate_pairs<EPT>(x, &s_cs[tok * D + lane8 * EPT]);
+        int slot = a.head + j;
+        if (slot >= a.window) slot -= a.window;
+        const int64_t row = lay_cache + (int64_t)h * a.window + slot;
+        uint8_t *codes = kv ? a.v_codes : a.k_codes;
+        float *scales = kv ? a.v_scales : a.k_scales;
+        quantize_store<EPT>(x, codes + row * D + lane8 * EPT, scales + row, lane8 == 0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Delta rebase [AI-cache]: every valid K row dequantised, rotated by -delta,
+// re-quantised.  Grid-stride over rows in memory order.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(kBlock) rebase_kernel(RebaseArgs a, CosSinTable rot) {
+    constexpr int EPT = D / kRowLanes;
+    const int lane8 = threadIdx.x % kRowLanes;
+    float cs[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) cs[e] = rot.cs[lane8 * EPT + e];
+
+    const int64_t per_lh = a.n_valid;
+    const int64_t total = (int64_t)a.n_layers * a.n_heads * per_lh;
+    const int64_t stride = (int64_t)gridDim.x * kRowsPerIter;
+    for (int64_t r = (int64_t)blockIdx.x * kRowsPerIter + threadIdx.x / kRowLanes; r < total;
+         r += stride) {
+        const int64_t lh = r / per_lh;
+        const int i = (int)(r - lh * per_lh);
+        int slot = a.start + i;
+        if (slot >= a.window) slot -= a.window;
+        const int64_t row = ((int64_t)a.layer0 * a.n_heads + lh) * a.window + slot;
+        float x[EPT];
+        dequant_chunk<EPT>(a.k_codes + row * D + lane8 * EPT, a.k_scales[row], x);
+        rotate_pairs<EPT>(x, cs);
+        quantize_store<EPT>(x, a.k_codes + row * D + lane8 * EPT, a.k_scales + row, lane8 == 0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Naive per-call upkeep [WC]: rebuild the shifted linear window and
+// re-rotate / re-quantise all of it.  Rows (kv, head, i), i fastest.
+// ---------------------------------------------------------------------------
+template <int D, bool BF16>
+__global__ void __launch_bounds__(kBlock) naive_kernel(NaiveArgs a) {
+    constexpr int EPT = D / kRowLanes;
+    const int lane8 = threadIdx.x % kRowLanes;
+    const int64_t per_h = a.n_after;
+    const int64_t total = 2 * (int64_t)a.n_heads * per_h;
+    const int64_t stride = (int64_t)gridDim.x * kRowsPerIter;
+    for (int64_t r = (int64_t)blockIdx.x * kRowsPerIter + threadIdx.x / kRowLanes; r < total;
+         r += stride) {
+        const int64_t kvh = r / per_h;  // (kv, head) pair
+        const int i = (int)(r - kvh * per_h);
+        const int kv = (int)(kvh / a.n_heads);
+        const int h = (int)(kvh - (int64_t)kv * a.n_heads);
+        const void *src;
+        int64_t src_off;
+        if (i < a.kept) {
+            src = kv ? a.v_src : a.k_src;
+            src_off = ((int64_t)h * a.window + i + a.drop) * D + lane8 * EPT;
+        } else {
+            src = kv ? a.v_new : a.k_new;
+            src_off = ((int64_t)(i - a.kept) * a.n_heads + h) * D + lane8 * EPT;
+        }
+        const int64_t row = (int64_t)h * a.window + i;
+        RawChunk<EPT, BF16> raw;
+        raw.load(src, src_off);
+        raw.store(kv ? a.v_dst : a.k_dst, row * D + lane8 * EPT);
+        float x[EPT];
+        raw.to_f32(x);
+        if (kv == 0) {
+            float cs[EPT];
+            const float4 *t = reinterpret_cast<const float4 *>(a.cs + (int64_t)i * D + lane8 * EPT);
+#pragma unroll
+            for (int v = 0; v < EPT / 4; ++v) {
+                float4 f = t[v];
+                cs[4 * v] = f.x; cs[4 * v + 1] = f.y; cs[4 * v + 2] = f.z; cs[4 * v + 3] = f.w;
+            }
+            rotate_pairs<EPT>(x, cs);
+        }
+        uint8_t *codes = kv ? a.v_codes : a.k_codes;
+        float *scales = kv ? a.v_scales : a.k_scales;
+        quantize_store<EPT>(x, codes + row * D + lane8 * EPT, scales + row, lane8 == 0);
+    }
+}
+
+int grid_for_rows(int64_t rows) {
+    int64_t g = (rows + kRowsPerIter - 1) / kRowsPerIter;
+    const int64_t cap = 256 * 16;      // 16 workgroups per CU on 256 CUs
+    return (int)(g < cap ? (g > 0 ? g : 1) : cap);
+}
+
+}  // namespace
+
+hipError_t launch_rope_table(float *cs, int64_t pos0, int32_t n_pos, int32_t head_dim,
+                             const ThetaTable &theta, hipStream_t s) {
+    const int half = head_dim / 2;
+    const int64_t n = (int64_t)n_pos * half;
+    const int grid = (int)((n + kBlock - 1) / kBlock);
+    hipLaunchKernelGGL(rope_table_kernel, dim3(grid), dim3(kBlock), 0, s,
+                       reinterpret_cast<float2 *>(cs), pos0, n_pos, half, theta);
+    return hipGetLastError();
+}
+
+hipError_t launch_write(const WriteArgs &a, int head_dim, hipStream_t s) {
+    dim3 grid((a.n_new + kTokBlock - 1) / kTokBlock, a.n_layers);
+    const bool bf = a.dtype == KVR_BF16;
+    if (head_dim == 128 && bf)
+        hipLaunchKernelGGL((write_kernel<128, true>), grid, dim3(kBlock), 0, s, a);
+    else if (head_dim == 128)
+        hipLaunchKernelGGL((write_kernel<128, false>), grid, dim3(kBlock), 0, s, a);
+    else if (bf)
+        hipLaunchKernelGGL((write_kernel<64, true>), grid, dim3(kBlock), 0, s, a);
+    else
+        hipLaunchKernelGGL((write_kernel<64, false>), grid, dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_rebase(const RebaseArgs &a, const CosSinTable &rot, int head_dim,
+                         hipStream_t s) {
+    const int grid = grid_for_rows((int64_t)a.n_layers * a.n_heads * a.n_valid);
+    if (head_dim == 128)
+        hipLaunchKernelGGL(rebase_kernel<128>, dim3(grid), dim3(kBlock), 0, s, a, rot);
+    else
+        hipLaunchKernelGGL(rebase_kernel<64>, dim3(grid), dim3(kBlock), 0, s, a, rot);
+    return hipGetLastError();
+}
+
+hipError_t launch_naive(const NaiveArgs &a, int head_dim, hipStream_t s) {
+    const int grid = grid_for_rows(2 * (int64_t)a.n_heads * a.n_after);
+    const bool bf = a.dtype == KVR_BF16;
+    if (head_dim == 128 && bf)
+        hipLaunchKernelGGL((naive_kernel<128, true>), dim3(grid), dim3(kBlock), 0, s, a);
+    else if (head_dim == 128)
+        hipLaunchKernelGGL((naive_kernel<128, false>), dim3(grid), dim3(kBlock), 0, s, a);
+    else if (bf)
+        hipLaunchKernelGGL((naive_kernel<64, true>), dim3(grid), dim3(kBlock), 0, s, a);
+    else
+        hipLaunchKernelGGL((naive_kernel<64, false>), dim3(grid), dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace kvr

@@ -1,0 +1,286 @@
+"""ctypes binding of libkvring.so (declared in include/kvring.h).
+
+Argument marshalling only: every function here passes raw device pointers
+(``tensor.data_ptr()``) and the current HIP stream to the C entry point of
+the same name; all arithmetic of the cache path runs in the library's HIP
+kernels.  PyTorch supplies device memory and streams.  When the library is
+missing this module raises at load time; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvring.so")
+
+KVR_OK, KVR_EINVAL, KVR_EALIGN, KVR_EUNSUPPORTED, KVR_ELAUNCH = 0, -1, -2, -3, -4
+KVR_F32, KVR_BF16 = 0, 1
+
+
+class KVRError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"kvring status {status}: {msg}")
+        self.status = status
+
+
+class kvr_ring(ctypes.Structure):
+    """Ring state (host POD): head, n_valid, pos_next."""
+    _fields_ = [("head", ctypes.c_int32), ("n_valid", ctypes.c_int32), ("pos_next", ctypes.c_int64)]
+
+    def __repr__(self):
+        return f"kvr_ring(head={self.head}, n_valid={self.n_valid}, pos_next={self.pos_next})"
+
+    def copy(self) -> "kvr_ring":
+        return kvr_ring(self.head, self.n_valid, self.pos_next)
+
+
+class kvr_cache(ctypes.Structure):
+    _fields_ = [("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+                ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
+                ("n_layers", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("window", ctypes.c_int32)]
+
+
+class kvr_rope_table(ctypes.Structure):
+    _fields_ = [("cs", ctypes.c_void_p), ("pos0", ctypes.c_int64), ("n_pos", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("base", ctypes.c_double)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32, _I64, _F32, _F64, _SZ = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
+
+_SIGS = {
+    "kvr_ring_init": (None, [ctypes.POINTER(kvr_ring)]),
+    "kvr_ring_slot": (_I32, [ctypes.POINTER(kvr_ring), _I32, _I32]),
+    "kvr_ring_logical_start": (_I32, [ctypes.POINTER(kvr_ring), _I32]),
+    "kvr_ring_after_write": (_I32, [ctypes.POINTER(kvr_ring), _I32, _I32]),
+    "kvr_ring_after_rebase": (_I32, [ctypes.POINTER(kvr_ring), _I64]),
+    "kv_rope_table_fill": (_I32, [_P, _I64, _I32, _I32, _F64, _P]),
+    "kv_write_rope_quant": (_I32, [ctypes.POINTER(kvr_cache), ctypes.POINTER(kvr_ring), _I32, _I32,
+                                   _P, _P, _I32, _I64, _I32, ctypes.POINTER(kvr_rope_table), _P]),
+    "kv_delta_rebase": (_I32, [ctypes.POINTER(kvr_cache), ctypes.POINTER(kvr_ring), _I32, _I32,
+                               _I64, _F64, _P]),
+    "attn_fp8_window_workspace_bytes": (_SZ, [ctypes.POINTER(kvr_cache), _I32, _I32, _I32]),
+    "attn_fp8_window": (_I32, [ctypes.POINTER(kvr_cache), _I32, _I32, _I32, _P, _I32, _I32, _I64,
+                               _F32, ctypes.POINTER(kvr_rope_table), _P, _I32, _P, _SZ, _P]),
+    "naive_upkeep": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32,
+                            ctypes.POINTER(kvr_rope_table), _P, _P, _P, _P, _P, _P, _P]),
+    "kvr_last_error": (ctypes.c_char_p, []),
+    "kvr_version": (ctypes.c_char_p, []),
+}
+
+#: every symbol include/kvring.h declares
+EXPORTED = tuple(_SIGS)
+
+
+def lib():
+    """Load libkvring.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m kv_cache_attention_ring_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != KVR_OK:
+        raise KVRError(status, lib().kvr_last_error().decode())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KVR_BF16
+    if t.dtype == torch.float32:
+        return KVR_F32
+    raise KVRError(KVR_EUNSUPPORTED, f"dtype {t.dtype} not supported (bf16, fp32)")
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise KVRError(KVR_EINVAL, f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise KVRError(KVR_EINVAL, f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+# ---------------------------------------------------------------------------
+# device-memory holders (allocation is the caller's, i.e. torch's)
+# ---------------------------------------------------------------------------
+class KVCache:
+    """FP8 K/V codes [L][H][W][D] (uint8) and fp32 scales [L][H][W], on a device."""
+
+    def __init__(self, n_layers: int, n_heads: int, head_dim: int, window: int, device="cuda"):
+        self.shape = (n_layers, n_heads, window, head_dim)
+        self.k_codes = torch.zeros(self.shape, dtype=torch.uint8, device=device)
+        self.v_codes = torch.zeros(self.shape, dtype=torch.uint8, device=device)
+        self.k_scales = torch.zeros(self.shape[:3], dtype=torch.float32, device=device)
+        self.v_scales = torch.zeros(self.shape[:3], dtype=torch.float32, device=device)
+        self.n_layers, self.n_heads, self.head_dim, self.window = n_layers, n_heads, head_dim, window
+
+    def desc(self) -> kvr_cache:
+        return kvr_cache(self.k_codes.data_ptr(), self.v_codes.data_ptr(),
+                         self.k_scales.data_ptr(), self.v_scales.data_ptr(),
+                         self.n_layers, self.n_heads, self.head_dim, self.window)
+
+    @property
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size()
+                   for t in (self.k_codes, self.v_codes, self.k_scales, self.v_scales))
+
+
+class RopeTable:
+    """Device (cos, sin) table of positions pos0 .. pos0+n_pos-1 (kv_rope_table_fill)."""
+
+    def __init__(self, pos0: int, n_pos: int, head_dim: int, base: float = 10000.0, device="cuda",
+                 stream=None):
+        self.cs = torch.empty((n_pos, head_dim // 2, 2), dtype=torch.float32, device=device)
+        self.pos0, self.n_pos, self.head_dim, self.base = int(pos0), int(n_pos), head_dim, float(base)
+        kv_rope_table_fill(self.cs, self.pos0, self.n_pos, head_dim, self.base, stream)
+
+    def desc(self) -> kvr_rope_table:
+        return kvr_rope_table(self.cs.data_ptr(), self.pos0, self.n_pos, self.head_dim, self.base)
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+def kvr_ring_init() -> kvr_ring:
+    r = kvr_ring()
+    lib().kvr_ring_init(ctypes.byref(r))
+    return r
+
+
+def kvr_ring_slot(r: kvr_ring, window: int, j: int) -> int:
+    return int(lib().kvr_ring_slot(ctypes.byref(r), window, j))
+
+
+def kvr_ring_logical_start(r: kvr_ring, window: int) -> int:
+    return int(lib().kvr_ring_logical_start(ctypes.byref(r), window))
+
+
+def kvr_ring_after_write(r: kvr_ring, window: int, n_new: int) -> None:
+    _check(lib().kvr_ring_after_write(ctypes.byref(r), window, n_new))
+
+
+def kvr_ring_after_rebase(r: kvr_ring, delta: int) -> None:
+    _check(lib().kvr_ring_after_rebase(ctypes.byref(r), int(delta)))
+
+
+def kv_rope_table_fill(cs: torch.Tensor, pos0: int, n_pos: int, head_dim: int, base: float,
+                       stream=None) -> None:
+    _check(lib().kv_rope_table_fill(_dev(cs, "cs"), int(pos0), int(n_pos), int(head_dim),
+                                    float(base), _stream(stream)))
+
+
+def kv_write_rope_quant(cache: KVCache, before: kvr_ring, layer0: int, k_new: torch.Tensor,
+                        v_new: torch.Tensor, rope: RopeTable, stream=None) -> None:
+    """k_new / v_new: [N][H][D] (one layer) or [n_layers][N][H][D] (layers layer0..)."""
+    if k_new.shape != v_new.shape or k_new.dtype != v_new.dtype:
+        raise KVRError(KVR_EINVAL, "k_new and v_new must match in shape and dtype")
+    if k_new.dim() == 3:
+        n_layers, (n_new, _, _) = 1, k_new.shape
+        stride = k_new.numel()
+    elif k_new.dim() == 4:
+        n_layers, n_new = k_new.shape[0], k_new.shape[1]
+        stride = k_new[0].numel()
+    else:
+        raise KVRError(KVR_EINVAL, "k_new must be [N][H][D] or [L][N][H][D]")
+    if k_new.shape[-2:] != (cache.n_heads, cache.head_dim):
+        raise KVRError(KVR_EINVAL, f"k_new trailing shape {tuple(k_new.shape[-2:])} != "
+                                   f"({cache.n_heads}, {cache.head_dim})")
+    c = cache.desc()
+    t = rope.desc()
+    _check(lib().kv_write_rope_quant(ctypes.byref(c), ctypes.byref(before), layer0, n_layers,
+                                     _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dtype_code(k_new),
+                                     stride, n_new, ctypes.byref(t), _stream(stream)))
+
+
+def kv_delta_rebase(cache: KVCache, ring: kvr_ring, layer0: int, n_layers: int, delta: int,
+                    rope_base: float = 10000.0, stream=None) -> None:
+    c = cache.desc()
+    _check(lib().kv_delta_rebase(ctypes.byref(c), ctypes.byref(ring), layer0, n_layers, int(delta),
+                                 float(rope_base), _stream(stream)))
+
+
+def attn_fp8_window_workspace_bytes(cache: KVCache, n_q: int, n_valid: int, n_splits: int = 0) -> int:
+    c = cache.desc()
+    return int(lib().attn_fp8_window_workspace_bytes(ctypes.byref(c), n_q, n_valid, n_splits))
+
+
+def attn_fp8_window(cache: KVCache, layer: int, slot_start: int, n_valid: int, q: torch.Tensor,
+                    q_pos_start: int, rope: RopeTable, out: torch.Tensor | None = None,
+                    n_splits: int = 0, ws: torch.Tensor | None = None,
+                    softmax_scale: float | None = None, stream=None) -> torch.Tensor:
+    """q: [n_q][H][D] bf16/fp32 -> out: [n_q][H][D] bf16."""
+    n_q = q.shape[0]
+    if q.dim() != 3 or q.shape[1:] != (cache.n_heads, cache.head_dim):
+        raise KVRError(KVR_EINVAL, f"q shape {tuple(q.shape)} does not match the cache")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    if out.dtype != torch.bfloat16 or out.shape != q.shape:
+        raise KVRError(KVR_EINVAL, "out must be bf16 with q's shape")
+    need = attn_fp8_window_workspace_bytes(cache, n_q, n_valid, n_splits)
+    if need and ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(ws, "ws") if ws is not None else None
+    ws_len = ws.numel() * ws.element_size() if ws is not None else 0
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(cache.head_dim)
+    c = cache.desc()
+    t = rope.desc()
+    _check(lib().attn_fp8_window(ctypes.byref(c), layer, slot_start, n_valid, _dev(q, "q"),
+                                 _dtype_code(q), n_q, int(q_pos_start), float(softmax_scale),
+                                 ctypes.byref(t), _dev(out, "out"), int(n_splits), ws_ptr, ws_len,
+                                 _stream(stream)))
+    return out
+
+
+def naive_upkeep(lin_k_src: torch.Tensor, lin_v_src: torch.Tensor, k_new: torch.Tensor,
+                 v_new: torch.Tensor, n_valid_before: int, pos_next_before: int, rope: RopeTable,
+                 lin_k_dst: torch.Tensor, lin_v_dst: torch.Tensor, k_codes: torch.Tensor,
+                 v_codes: torch.Tensor, k_scales: torch.Tensor, v_scales: torch.Tensor,
+                 stream=None) -> None:
+    """Linear windows [H][W][D]; new rows [N][H][D]; codes [H][W][D]; scales [H][W]."""
+    H, W, D = lin_k_src.shape
+    n_new = k_new.shape[0]
+    for name, t in (("lin_v_src", lin_v_src), ("lin_k_dst", lin_k_dst), ("lin_v_dst", lin_v_dst)):
+        if t.shape != lin_k_src.shape or t.dtype != lin_k_src.dtype:
+            raise KVRError(KVR_EINVAL, f"{name} must match lin_k_src")
+    if k_new.dtype != lin_k_src.dtype or k_new.shape[1:] != (H, D) or v_new.shape != k_new.shape:
+        raise KVRError(KVR_EINVAL, "new rows must be [N][H][D] in the window dtype")
+    if k_codes.shape != (H, W, D) or v_codes.shape != (H, W, D) or k_scales.shape != (H, W) \
+            or v_scales.shape != (H, W):
+        raise KVRError(KVR_EINVAL, "codes [H][W][D] and scales [H][W] expected")
+    t = rope.desc()
+    _check(lib().naive_upkeep(_dev(lin_k_src, "lin_k_src"), _dev(lin_v_src, "lin_v_src"),
+                              _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dtype_code(k_new), n_new,
+                              int(n_valid_before), int(pos_next_before), H, D, W, ctypes.byref(t),
+                              _dev(lin_k_dst, "lin_k_dst"), _dev(lin_v_dst, "lin_v_dst"),
+                              _dev(k_codes, "k_codes"), _dev(v_codes, "v_codes"),
+                              _dev(k_scales, "k_scales"), _dev(v_scales, "v_scales"),
+                              _stream(stream)))
+
+
+def kvr_last_error() -> str:
+    return lib().kvr_last_error().decode()
+
+
+def kvr_version() -> str:
+    return lib().kvr_version().decode()

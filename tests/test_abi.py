@@ -1,0 +1,224 @@
+"""C-ABI contract tests that need no GPU.
+
+* libkvring.so loads and exports every function include/kvring.h declares.
+* The ring bookkeeping (pure host code in the library) is bit-exact against the
+  oracle's brute-force deque of the last W tokens.
+* Invalid arguments are rejected on the host, before any launch, with the
+  documented status codes.  Every case below fails validation, so no kernel is
+  ever launched with the fake device addresses used here.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from kv_cache_attention_ring_amd import kvring as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "kvring.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    L = K.lib()
+    declared = _declared_functions()
+    assert len(declared) >= 12
+    for name in declared:
+        assert hasattr(L, name), name
+    assert sorted(K.EXPORTED) == declared
+    assert K.kvr_version() == "0.1.0"
+
+
+# ---------------------------------------------------------------------------
+# ring bookkeeping vs brute force
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("W,N", [(1, 1), (5, 2), (16, 16), (31, 7), (96, 16), (100, 16), (128, 45),
+                                 (5788, 757)])
+def test_ring_bookkeeping_matches_deque(W, N):
+    r = K.kvr_ring_init()
+    dq = oracle.RingDeque(W)
+    steps = 3 * W // N + 2 if W < 1000 else 12
+    pos = 0
+    for _ in range(steps):
+        assert r.head == dq.next_slot
+        want = dq.write(N)
+        got = [K.kvr_ring_slot(r, W, j) for j in range(N)]
+        assert got == want
+        K.kvr_ring_after_write(r, W, N)
+        pos += N
+        assert r.n_valid == dq.n_valid and r.pos_next == pos
+        assert K.kvr_ring_logical_start(r, W) == dq.logical_slots()[0]
+
+
+def test_ring_rebase_moves_positions_only():
+    r = K.kvr_ring_init()
+    for _ in range(5):
+        K.kvr_ring_after_write(r, 96, 16)
+    before = r.copy()
+    K.kvr_ring_after_rebase(r, 64)
+    assert (r.head, r.n_valid, r.pos_next) == (before.head, before.n_valid, before.pos_next - 64)
+
+
+def test_ring_rejects_bad_sizes():
+    r = K.kvr_ring_init()
+    with pytest.raises(K.KVRError) as e:
+        K.kvr_ring_after_write(r, 96, 97)
+    assert e.value.status == K.KVR_EINVAL
+    with pytest.raises(K.KVRError):
+        K.kvr_ring_after_write(r, 96, 0)
+    assert K.kvr_ring_slot(r, 96, 96) == -1
+    bad = K.kvr_ring(200, 0, 0)
+    assert K.kvr_ring_logical_start(bad, 96) == -1
+
+
+# ---------------------------------------------------------------------------
+# host validation (nothing is launched)
+# ---------------------------------------------------------------------------
+FAKE = 0x7F0000000000           # 16-byte aligned, never dereferenced
+
+# These tests hand fake device addresses to the library.  Each case is built to
+# fail host validation, but a wrong case would launch a kernel on them, so they
+# only run where no GPU is visible (device_count does not initialise HIP).
+no_gpu = pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,
+                            reason="fake-address validation tests run only without a GPU")
+
+
+def _cache(D=128, W=5788, L=1, H=12, base=FAKE):
+    return K.kvr_cache(base, base + 0x1000000, base + 0x2000000, base + 0x3000000, L, H, D, W)
+
+
+def _table(pos0=0, n=10000, D=128, base=FAKE + 0x4000000):
+    return K.kvr_rope_table(base, pos0, n, D, 10000.0)
+
+
+def _write(cache, ring, n_new, table, layer0=0, n_layers=1, k=FAKE + 0x5000000, v=FAKE + 0x6000000,
+           dtype=K.KVR_BF16, stride=0):
+    return K.lib().kv_write_rope_quant(ctypes.byref(cache), ctypes.byref(ring), layer0, n_layers,
+                                       k, v, dtype, stride, n_new, ctypes.byref(table), None)
+
+
+@no_gpu
+def test_write_validation():
+    c, t, r = _cache(), _table(), K.kvr_ring_init()
+    assert _write(_cache(D=96), r, 757, t) == K.KVR_EUNSUPPORTED
+    assert _write(c, r, 0, t) == K.KVR_EINVAL
+    assert _write(c, r, 5789, t) == K.KVR_EINVAL
+    assert _write(c, r, 757, t, layer0=1) == K.KVR_EINVAL
+    assert _write(c, r, 757, t, k=FAKE + 8) == K.KVR_EALIGN
+    assert _write(c, r, 757, t, k=0) == K.KVR_EINVAL
+    assert _write(c, r, 757, t, dtype=7) == K.KVR_EUNSUPPORTED
+    assert _write(c, K.kvr_ring(5788, 0, 0), 757, t) == K.KVR_EINVAL
+    assert _write(c, K.kvr_ring(0, 5789, 0), 757, t) == K.KVR_EINVAL
+    # positions not covered by the rotary table
+    assert _write(c, K.kvr_ring(0, 0, 9500), 757, t) == K.KVR_EINVAL
+    assert "rotary table" in K.kvr_last_error()
+    assert _write(c, r, 757, _table(D=64)) == K.KVR_EINVAL
+    assert _write(_cache(L=60), r, 757, t, n_layers=60, stride=5) == K.KVR_EINVAL
+    assert _write(_cache(base=FAKE + 4), r, 757, t) == K.KVR_EALIGN
+
+
+@no_gpu
+def test_rebase_validation():
+    c = _cache()
+    lib = K.lib()
+    r = K.kvr_ring(0, 5788, 100)
+    assert lib.kv_delta_rebase(ctypes.byref(c), ctypes.byref(r), 0, 2, 5, 10000.0, None) == K.KVR_EINVAL
+    assert lib.kv_delta_rebase(ctypes.byref(c), ctypes.byref(r), 0, 1, 5, 0.5, None) == K.KVR_EINVAL
+    bad = K.kvr_ring(0, 6000, 100)
+    assert lib.kv_delta_rebase(ctypes.byref(c), ctypes.byref(bad), 0, 1, 5, 1e4, None) == K.KVR_EINVAL
+    c64 = _cache(D=32)
+    assert lib.kv_delta_rebase(ctypes.byref(c64), ctypes.byref(r), 0, 1, 5, 1e4, None) == K.KVR_EUNSUPPORTED
+
+
+def _attn(cache, n_valid, slot_start=0, n_q=757, q=FAKE + 0x7000000, out=FAKE + 0x8000000,
+          table=None, ws=None, ws_bytes=0, n_splits=1, scale=0.088, layer=0, qpos=0):
+    table = table or _table()
+    return K.lib().attn_fp8_window(ctypes.byref(cache), layer, slot_start, n_valid, q, K.KVR_BF16,
+                                   n_q, qpos, scale, ctypes.byref(table), out, n_splits, ws,
+                                   ws_bytes, None)
+
+
+@no_gpu
+def test_attention_validation():
+    c = _cache()
+    assert _attn(c, 0) == K.KVR_EINVAL
+    assert _attn(c, 5789) == K.KVR_EINVAL
+    assert _attn(c, 5788, slot_start=5788) == K.KVR_EINVAL
+    assert _attn(c, 5788, n_q=0) == K.KVR_EINVAL
+    assert _attn(c, 5788, q=FAKE + 2) == K.KVR_EALIGN
+    assert _attn(c, 5788, out=0) == K.KVR_EINVAL
+    assert _attn(c, 5788, scale=0.0) == K.KVR_EINVAL
+    assert _attn(c, 5788, layer=1) == K.KVR_EINVAL
+    assert _attn(c, 5788, qpos=9500) == K.KVR_EINVAL
+    # more than one split needs a workspace of the advertised size
+    need = K.lib().attn_fp8_window_workspace_bytes(ctypes.byref(c), 757, 5788, 4)
+    assert need == 4 * 757 * 12 * (128 + 2) * 4
+    assert _attn(c, 5788, n_splits=4) == K.KVR_EINVAL
+    assert _attn(c, 5788, n_splits=4, ws=FAKE + 0x9000000, ws_bytes=need - 4) == K.KVR_EINVAL
+    assert _attn(c, 5788, n_splits=4, ws=FAKE + 0x9000010, ws_bytes=need) == K.KVR_EALIGN
+    assert _attn(_cache(D=256), 5788) == K.KVR_EUNSUPPORTED
+
+
+def test_workspace_sizes_and_split_clamping():
+    c = _cache(D=64, W=96, H=2)
+    lib = K.lib()
+    # one split needs no workspace
+    assert lib.attn_fp8_window_workspace_bytes(ctypes.byref(c), 16, 96, 1) == 0
+    # 96 keys are two 64-key tiles: a request for 8 splits is clamped to 2
+    assert lib.attn_fp8_window_workspace_bytes(ctypes.byref(c), 16, 96, 8) == 2 * 16 * 2 * 66 * 4
+    # 9 tiles in 4 requested splits -> 3 tiles per split -> 3 splits, none empty
+    c2 = _cache(D=64, W=576, H=1)
+    assert lib.attn_fp8_window_workspace_bytes(ctypes.byref(c2), 1, 576, 4) == 3 * 1 * 1 * 66 * 4
+
+
+@no_gpu
+def test_naive_validation():
+    lib = K.lib()
+    t = _table()
+    p = [FAKE + i * 0x1000000 for i in range(10)]
+
+    def call(n_new=757, n_valid=5788, H=12, D=128, W=5788, ptrs=p, dtype=K.KVR_BF16, table=t, pos=0):
+        return lib.naive_upkeep(ptrs[0], ptrs[1], ptrs[2], ptrs[3], dtype, n_new, n_valid, pos, H, D,
+                                W, ctypes.byref(table), ptrs[4], ptrs[5], ptrs[6], ptrs[7], ptrs[8],
+                                ptrs[9], None)
+    assert call(n_new=0) == K.KVR_EINVAL
+    assert call(n_valid=5789) == K.KVR_EINVAL
+    assert call(D=80) == K.KVR_EUNSUPPORTED
+    bad = list(p)
+    bad[4] = p[0] + 256            # dst overlaps src
+    assert call(ptrs=bad) == K.KVR_EINVAL
+    bad = list(p)
+    bad[6] = p[6] + 1
+    assert call(ptrs=bad) == K.KVR_EALIGN
+    assert call(pos=9500) == K.KVR_EINVAL      # window positions end at 10257 > 10000
+
+
+@no_gpu
+def test_rope_table_validation():
+    lib = K.lib()
+    assert lib.kv_rope_table_fill(FAKE, 0, 0, 128, 1e4, None) == K.KVR_EINVAL
+    assert lib.kv_rope_table_fill(FAKE, 0, 10, 100, 1e4, None) == K.KVR_EUNSUPPORTED
+    assert lib.kv_rope_table_fill(FAKE + 4, 0, 10, 128, 1e4, None) == K.KVR_EALIGN
+    assert lib.kv_rope_table_fill(FAKE, 0, 10, 128, 1.0, None) == K.KVR_EINVAL
+
+
+def test_page_shape_constants_fixture():
+    from kv_cache_attention_ring_amd import inputs
+    vals = {}
+    for line in open(os.path.join(ROOT, "tests", "golden", "page_shape_constants.txt")):
+        if line.strip() and not line.startswith("#"):
+            k, v = line.split()
+            vals[k] = int(v)
+    s = inputs.PAGE_STEP
+    assert vals["blocks"] == s.n_layers and vals["passes"] == s.passes
+    assert vals["calls_per_step"] == s.n_layers * s.passes
+    assert vals["window_slots"] == s.window and vals["new_slots"] == s.n_new
+    assert vals["reset_period_steps"] == inputs.RESET_PERIOD

@@ -1,0 +1,400 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every case feeds both sides the same seeded inputs and compares element by
+element with the bars in tests/_parity.py.  Cases:
+  * rotary table, E4M3 conversion sweep (ties, subnormals, saturation edge);
+  * the small workload end to end (1 layer, 2 heads, D 64, W 96, N 16; 8 steps,
+    reset by 64 after step 4), ring and naive paths, 4 attention passes per
+    step, one and two key splits; a W = 100 variant whose chunks wrap mid-chunk;
+  * one attention layer at the production shape (12 heads, D 128, W 5788,
+    N 757): all writes, 4 passes on sampled queries of every head, default and
+    single split, determinism, the naive path, the rebase;
+  * the 60-layer batched write of a full step (sampled layers);
+  * edge cases: ring not yet full, one valid key, one query, ragged query
+    counts, fp32 inputs at D 128, all-zero rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_attention_ring_amd import inputs
+from kv_cache_attention_ring_amd import kvring as K
+
+from _parity import assert_attention, assert_codes, assert_scales, logical_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    K.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _f32(t):
+    return t.detach().float().cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+def test_rope_table_matches_oracle():
+    for D in (64, 128):
+        _say(f"rope table D={D}")
+        pos0, n = -200, 40000
+        t = K.RopeTable(pos0, n, D)
+        torch.cuda.synchronize()
+        got = _np(t.cs)
+        sel = np.concatenate([np.arange(0, 400), np.random.default_rng(D).integers(0, n, 3000)])
+        want = oracle.rope_cs(pos0 + sel, D)
+        g = got[sel]
+        same = (g.view(np.uint32) == want.view(np.uint32)).mean()
+        ulps = np.abs(g.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+        assert same >= 0.9999 and ulps.max() <= 1, (same, ulps.max())
+
+
+def test_e4m3_conversion_sweep_through_write():
+    """V rows whose absmax is 448 are encoded without scaling (448/448 = 1)."""
+    _say("e4m3 sweep")
+    codes = np.arange(0x7F, dtype=np.uint8)
+    tv = np.sort(oracle.e4m3_decode(codes)).astype(np.float32)
+    mids = ((tv[1:].astype(np.float64) + tv[:-1]) / 2).astype(np.float32)
+    vals = np.concatenate([tv, mids, np.nextafter(mids, np.float32(1e9)),
+                           np.nextafter(mids, np.float32(-1e9)),
+                           np.random.default_rng(3).uniform(-448, 448, 4000).astype(np.float32),
+                           np.array([1e-12, 2e-4, 447.99, 448.0], np.float32)])
+    vals = np.concatenate([vals, -vals])
+    D = 128
+    per = D - 1
+    n = (vals.size + per - 1) // per
+    rows = np.zeros((n, per), np.float32)
+    rows.ravel()[: vals.size] = vals
+    v = np.concatenate([np.full((n, 1), 448.0, np.float32), rows], axis=1)      # [n][D]
+    H, W = 1, n
+    cache = K.KVCache(1, H, D, W)
+    rope = K.RopeTable(0, n, D)
+    k = torch.zeros((n, H, D), dtype=torch.float32, device="cuda")
+    vt = torch.from_numpy(v).view(n, H, D).cuda()
+    K.kv_write_rope_quant(cache, K.kvr_ring_init(), 0, k, vt, rope)
+    torch.cuda.synchronize()
+    got = _np(cache.v_codes)[0, 0]
+    want = oracle.e4m3_encode(v)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5]
+    assert np.all(_np(cache.v_scales) == np.float32(1.0))
+    # all-zero K rows: scale 0, zero codes
+    assert not _np(cache.k_codes).any() and not _np(cache.k_scales).any()
+
+
+# ---------------------------------------------------------------------------
+class SmallRun:
+    """Ring path, naive path and oracle side by side on one layer."""
+
+    def __init__(self, shape, dtype=torch.float32, table=(-256, 4096)):
+        self.s = shape
+        H, D, W = shape.n_heads, shape.head_dim, shape.window
+        self.dtype = dtype
+        self.cache = K.KVCache(1, H, D, W)
+        self.ring = K.kvr_ring_init()
+        self.rope = K.RopeTable(table[0], table[1], D)
+        self.lin = [torch.zeros((H, W, D), dtype=dtype, device="cuda") for _ in range(4)]
+        self.ping = 0
+        self.lc = torch.zeros((H, W, D), dtype=torch.uint8, device="cuda")
+        self.lv = torch.zeros((H, W, D), dtype=torch.uint8, device="cuda")
+        self.lks = torch.zeros((H, W), dtype=torch.float32, device="cuda")
+        self.lvs = torch.zeros((H, W), dtype=torch.float32, device="cuda")
+        self.orc = oracle.LayerCache(H, D, W)
+        self.total = 0
+
+    def step(self, k, v):
+        """k, v: fp32 numpy [N][H][D]."""
+        s = self.s
+        kd = torch.from_numpy(k).to(self.dtype).cuda()
+        vd = torch.from_numpy(v).to(self.dtype).cuda()
+        kf, vf = _f32(kd), _f32(vd)
+        src_k, src_v = self.lin[2 * self.ping], self.lin[2 * self.ping + 1]
+        dst_k, dst_v = self.lin[2 * (1 - self.ping)], self.lin[2 * (1 - self.ping) + 1]
+        K.naive_upkeep(src_k, src_v, kd, vd, self.ring.n_valid, self.ring.pos_next, self.rope,
+                       dst_k, dst_v, self.lc, self.lv, self.lks, self.lvs)
+        self.ping = 1 - self.ping
+        K.kv_write_rope_quant(self.cache, self.ring, 0, kd, vd, self.rope)
+        oracle.write(self.orc, self.total, self.ring.pos_next, kf, vf)
+        K.kvr_ring_after_write(self.ring, s.window, k.shape[0])
+        self.total += k.shape[0]
+
+    def rebase(self, delta):
+        start = K.kvr_ring_logical_start(self.ring, self.s.window)
+        K.kv_delta_rebase(self.cache, self.ring, 0, 1, delta)
+        oracle.rebase(self.orc, start, self.ring.n_valid, delta)
+        K.kvr_ring_after_rebase(self.ring, delta)
+
+    def check_cache(self, what, naive_too=True):
+        torch.cuda.synchronize()
+        for name in ("k", "v"):
+            assert_codes(_np(getattr(self.cache, f"{name}_codes"))[0],
+                         getattr(self.orc, f"{name}_codes"), f"{what} ring {name} codes")
+            assert_scales(_np(getattr(self.cache, f"{name}_scales"))[0],
+                          getattr(self.orc, f"{name}_scales"), f"{what} ring {name} scales")
+        if naive_too:
+            W, n = self.s.window, self.ring.n_valid
+            start = K.kvr_ring_logical_start(self.ring, W)
+            for ring_t, lin_t in ((self.cache.k_codes, self.lc), (self.cache.v_codes, self.lv),
+                                  (self.cache.k_scales, self.lks), (self.cache.v_scales, self.lvs)):
+                r = logical_rows(_np(ring_t)[0], start, n, W)
+                l = _np(lin_t)[:, :n]
+                assert np.array_equal(np.ascontiguousarray(r).view(np.uint8),
+                                      np.ascontiguousarray(l).view(np.uint8)), f"{what}: ring != naive"
+
+    def attention(self, q, n_splits=0, naive_too=True):
+        """q fp32 numpy [n_q][H][D]; returns (gpu bf16 as fp32, oracle fp64)."""
+        W = self.s.window
+        qd = torch.from_numpy(q).to(self.dtype).cuda()
+        n_q = q.shape[0]
+        qpos = self.ring.pos_next - n_q
+        start = K.kvr_ring_logical_start(self.ring, W)
+        out = K.attn_fp8_window(self.cache, 0, start, self.ring.n_valid, qd, qpos, self.rope,
+                                n_splits=n_splits)
+        if naive_too:
+            lin_cache = K.KVCache(1, self.s.n_heads, self.s.head_dim, W)
+            lin_cache.k_codes[0].copy_(self.lc)
+            lin_cache.v_codes[0].copy_(self.lv)
+            lin_cache.k_scales[0].copy_(self.lks)
+            lin_cache.v_scales[0].copy_(self.lvs)
+            out_lin = K.attn_fp8_window(lin_cache, 0, 0, self.ring.n_valid, qd, qpos, self.rope,
+                                        n_splits=n_splits)
+            torch.cuda.synchronize()
+            assert torch.equal(out, out_lin), "ring and naive attention differ"
+        torch.cuda.synchronize()
+        ref = oracle.attention(self.orc, start, self.ring.n_valid, _f32(qd), qpos)
+        return _f32(out), ref
+
+
+def test_small_workload_end_to_end():
+    shp = inputs.TINY
+    run = SmallRun(shp)
+    for step in range(8):
+        _say(f"small step {step}")
+        k, v = inputs.np_chunk(shp, step)
+        run.step(k, v)
+        run.check_cache(f"step {step}", naive_too=step < 4)
+        for p in range(shp.passes):
+            q = inputs.np_queries(shp, step, p)
+            got, ref = run.attention(q, n_splits=1 + (p % 2), naive_too=step < 4)
+            assert_attention(got, ref, f"step {step} pass {p}")
+        if step == 3:
+            _say("small rebase by 64")
+            run.rebase(64)
+            run.check_cache("after rebase", naive_too=False)
+
+
+def test_wrap_mid_chunk():
+    shp = inputs.TINY_WRAP
+    run = SmallRun(shp)
+    for step in range(16):
+        _say(f"wrap step {step}")
+        k, v = inputs.np_chunk(shp, step)
+        run.step(k, v)
+        run.check_cache(f"wrap step {step}")
+        if step in (0, 6, 7, 15):
+            got, ref = run.attention(inputs.np_queries(shp, step, 0), n_splits=0)
+            assert_attention(got, ref, f"wrap step {step}")
+
+
+def test_edge_cases_small():
+    shp = inputs.TINY_WRAP
+    run = SmallRun(shp)
+    k, v = inputs.np_chunk(shp, 0)
+    k[3] = 0.0                                         # an all-zero K and V row
+    v[5, 1] = 0.0
+    run.step(k, v)
+    run.check_cache("zero rows")
+    assert float(run.cache.k_scales[0, 0, 3]) == 0.0 and float(run.cache.v_scales[0, 1, 5]) == 0.0
+    for n_q in (1, 3, 16):
+        _say(f"edge n_q={n_q}")
+        q = inputs.np_queries(shp, 0, 0)[:n_q].copy()
+        qpos = run.ring.pos_next - n_q
+        out = K.attn_fp8_window(run.cache, 0, 0, run.ring.n_valid, torch.from_numpy(q).cuda(), qpos,
+                                run.rope)
+        torch.cuda.synchronize()
+        assert_attention(_f32(out), oracle.attention(run.orc, 0, run.ring.n_valid, q, qpos),
+                         f"n_q={n_q}")
+    # a single valid key: the output is that key's dequantised value row
+    _say("edge n_valid=1")
+    q = inputs.np_queries(shp, 0, 1)
+    qd = torch.from_numpy(q).cuda()
+    out = K.attn_fp8_window(run.cache, 0, 0, 1, qd, 0, run.rope)
+    torch.cuda.synchronize()
+    ref = oracle.attention(run.orc, 0, 1, q, 0)
+    assert_attention(_f32(out), ref, "n_valid=1")
+    # zero queries: uniform weights
+    out0 = K.attn_fp8_window(run.cache, 0, 0, 16, torch.zeros_like(qd), 0, run.rope)
+    torch.cuda.synchronize()
+    assert_attention(_f32(out0), oracle.attention(run.orc, 0, 16, np.zeros_like(q), 0), "q=0")
+
+
+def test_fp32_inputs_head_dim_128():
+    shp = inputs.Shape("test", 1, 3, 128, 300, 70)
+    run = SmallRun(shp, dtype=torch.float32)
+    for step in range(6):
+        _say(f"fp32 D128 step {step}")
+        k, v = inputs.np_chunk(shp, step)
+        run.step(k * 1.7, v * 0.6)
+        run.check_cache(f"fp32 D128 step {step}")
+        got, ref = run.attention(inputs.np_queries(shp, step, 0), n_splits=(step % 3) + 1)
+        assert_attention(got, ref, f"fp32 D128 step {step}")
+
+
+def test_bf16_ragged_queries_head_dim_64():
+    shp = inputs.Shape("test", 1, 4, 64, 1000, 161)
+    run = SmallRun(shp, dtype=torch.bfloat16)
+    for step in range(8):
+        _say(f"bf16 D64 step {step}")
+        k, v = inputs.np_chunk(shp, step)
+        run.step(k, v)
+        if step in (0, 6, 7):
+            run.check_cache(f"bf16 D64 step {step}")
+            got, ref = run.attention(inputs.np_queries(shp, step, 1))
+            assert_attention(got, ref, f"bf16 D64 step {step}")
+
+
+# ---------------------------------------------------------------------------
+# production shape: one layer, 12 heads, D 128, W 5788, N 757
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def page_layer():
+    shp = inputs.PAGE_LAYER
+    H, D, W, N = shp.n_heads, shp.head_dim, shp.window, shp.n_new
+    cache = K.KVCache(1, H, D, W)
+    rope = K.RopeTable(-40000, 100000, D)
+    ring = K.kvr_ring_init()
+    orc = oracle.LayerCache(H, D, W)
+    total = 0
+    for step in range(8):
+        _say(f"page write step {step}")
+        k, v = inputs.torch_chunk(shp, step, 0, "cpu")
+        K.kv_write_rope_quant(cache, ring, 0, k[0].cuda(), v[0].cuda(), rope)
+        oracle.write(orc, total, ring.pos_next, _f32(k[0]), _f32(v[0]))
+        K.kvr_ring_after_write(ring, W, N)
+        total += N
+    torch.cuda.synchronize()
+    return dict(shape=shp, cache=cache, rope=rope, ring=ring, orc=orc)
+
+
+def test_page_write_parity(page_layer):
+    _say("page write parity")
+    c, o = page_layer["cache"], page_layer["orc"]
+    assert page_layer["ring"].head == (8 * 757) % 5788          # the 8th chunk wrapped
+    for name in ("k", "v"):
+        assert_codes(_np(getattr(c, f"{name}_codes"))[0], getattr(o, f"{name}_codes"), f"page {name}")
+        assert_scales(_np(getattr(c, f"{name}_scales"))[0], getattr(o, f"{name}_scales"), f"page {name}")
+
+
+def _page_rows(n_q, H, seed=0, per_head=40):
+    rng = np.random.default_rng(seed)
+    qs = np.unique(np.concatenate([[0, 31, 32, 127, 128, n_q - 1], rng.integers(0, n_q, per_head)]))
+    return [(int(i), h) for h in range(H) for i in qs]
+
+
+def test_page_attention_parity(page_layer):
+    shp, c, rope, ring, orc = (page_layer[k] for k in ("shape", "cache", "rope", "ring", "orc"))
+    W = shp.window
+    start = K.kvr_ring_logical_start(ring, W)
+    for p in range(shp.passes):
+        _say(f"page attention pass {p}")
+        q = inputs.torch_queries(shp, 8, p, 0, "cpu")
+        qd = q.cuda()
+        rows = _page_rows(shp.n_new, shp.n_heads, seed=p)
+        ref = oracle.attention(orc, start, ring.n_valid, _f32(q), ring.pos_next - shp.n_new, rows=rows)
+        for n_splits in ((0, 1) if p == 0 else (0,)):
+            out = K.attn_fp8_window(c, 0, start, ring.n_valid, qd, ring.pos_next - shp.n_new, rope,
+                                    n_splits=n_splits)
+            torch.cuda.synchronize()
+            got = _f32(out)
+            g = np.stack([got[i, h] for i, h in rows])
+            mx, mean = assert_attention(g, ref, f"page pass {p} splits {n_splits}")
+            _say(f"  splits={n_splits} max-abs {mx:.4g} mean-abs {mean:.4g}")
+            assert np.isfinite(got).all()
+        if p == 0:
+            again = K.attn_fp8_window(c, 0, start, ring.n_valid, qd, ring.pos_next - shp.n_new, rope)
+            torch.cuda.synchronize()
+            assert torch.equal(out, again), "attention is not deterministic"
+
+
+def test_page_rebase_parity(page_layer):
+    shp, c, ring, orc = (page_layer[k] for k in ("shape", "cache", "ring", "orc"))
+    delta = inputs.rebase_delta()
+    _say(f"page rebase delta={delta}")
+    c2 = K.KVCache(1, shp.n_heads, shp.head_dim, shp.window)
+    for n in ("k_codes", "v_codes", "k_scales", "v_scales"):
+        getattr(c2, n).copy_(getattr(c, n))
+    o2 = orc.copy()
+    start = K.kvr_ring_logical_start(ring, shp.window)
+    K.kv_delta_rebase(c2, ring, 0, 1, delta)
+    oracle.rebase(o2, start, ring.n_valid, delta)
+    torch.cuda.synchronize()
+    assert_codes(_np(c2.k_codes)[0], o2.k_codes, "rebase k")
+    assert_scales(_np(c2.k_scales)[0], o2.k_scales, "rebase k")
+    assert torch.equal(c2.v_codes, c.v_codes) and torch.equal(c2.v_scales, c.v_scales)
+
+
+def test_page_naive_matches_ring():
+    """Naive per-call upkeep at production shape: identical caches and outputs."""
+    shp = inputs.PAGE_LAYER
+    H, D, W, N = shp.n_heads, shp.head_dim, shp.window, shp.n_new
+    cache = K.KVCache(1, H, D, W)
+    rope = K.RopeTable(0, 16 * N, D)
+    ring = K.kvr_ring_init()
+    lin = [torch.zeros((H, W, D), dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    lc = K.KVCache(1, H, D, W)
+    ping = 0
+    for step in range(9):
+        _say(f"page naive step {step}")
+        k, v = inputs.torch_chunk(shp, step, 0, "cuda")
+        K.naive_upkeep(lin[2 * ping], lin[2 * ping + 1], k[0], v[0], ring.n_valid, ring.pos_next,
+                       rope, lin[2 - 2 * ping], lin[3 - 2 * ping], lc.k_codes[0], lc.v_codes[0],
+                       lc.k_scales[0], lc.v_scales[0])
+        ping = 1 - ping
+        K.kv_write_rope_quant(cache, ring, 0, k[0], v[0], rope)
+        K.kvr_ring_after_write(ring, W, N)
+    start = K.kvr_ring_logical_start(ring, W)
+    idx = torch.from_numpy((start + np.arange(W)) % W).cuda()
+    for n in ("k_codes", "v_codes", "k_scales", "v_scales"):
+        assert torch.equal(getattr(cache, n)[0][:, idx], getattr(lc, n)[0]), n
+    q = inputs.torch_queries(shp, 9, 0, 0, "cuda")
+    a = K.attn_fp8_window(cache, 0, start, W, q, ring.pos_next - N, rope)
+    b = K.attn_fp8_window(lc, 0, 0, W, q, ring.pos_next - N, rope)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_step_batched_write_60_layers():
+    """The 60-layer write of one denoise step in one launch (sampled layers)."""
+    shp = inputs.PAGE_STEP
+    H, D, W, N, L = shp.n_heads, shp.head_dim, shp.window, shp.n_new, shp.n_layers
+    cache = K.KVCache(L, H, D, W)
+    rope = K.RopeTable(0, 8000, D)
+    ring = K.kvr_ring(5299, 5788, 5299)          # full ring, the chunk wraps at the end
+    k, v = inputs.torch_chunk(shp, 0, 0, "cpu", n_layers=L)
+    _say("60-layer batched write")
+    K.kv_write_rope_quant(cache, ring, 0, k.cuda(), v.cuda(), rope)
+    torch.cuda.synchronize()
+    for layer in (0, 17, 59):
+        orc = oracle.LayerCache(H, D, W)
+        oracle.write(orc, 5299, 5299, _f32(k[layer]), _f32(v[layer]))
+        slots = (5299 + np.arange(N)) % W
+        for n in ("k", "v"):
+            assert_codes(_np(getattr(cache, f"{n}_codes"))[layer][:, slots],
+                         getattr(orc, f"{n}_codes")[:, slots], f"layer {layer} {n}")
+            assert_scales(_np(getattr(cache, f"{n}_scales"))[layer][:, slots],
+                          getattr(orc, f"{n}_scales")[:, slots], f"layer {layer} {n}")
+    # slots outside the chunk were not touched
+    untouched = np.setdiff1d(np.arange(W), (5299 + np.arange(N)) % W)
+    assert not _np(cache.k_codes)[:, :, untouched].any()
