@@ -57,7 +57,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kKT = 64;           // keys per tile
 constexpr int kQW = 32;           // queries per wave
-constexpr int kNW = 4;            // waves per workgroup
+constexpr int kNW = 8;            // waves per workgroup (two per SIMD)
 constexpr int kThreads = 64 * kNW;
 constexpr int kQB = kQW * kNW;    // queries per workgroup
 constexpr float kTau = 2.0f;      // lazy-rescale threshold (log2 units)
@@ -71,7 +71,10 @@ struct Lds {
     static constexpr int V_BYTES = kKT * D;
     static constexpr int F_OFF = K_BYTES + V_BYTES;
     static constexpr int BUF = F_OFF + 2 * kKT * 4;
-    static constexpr int TOTAL = 2 * BUF;
+    // Q operands of one wave: [slice][hi/lo][16-byte part][lane] x 16 bytes
+    static constexpr int Q_WAVE = (D / 64) * 2 * 2 * 64 * 16;
+    static constexpr int Q_OFF = 3 * BUF;        // tiles are triple buffered
+    static constexpr int TOTAL = Q_OFF + kNW * Q_WAVE;
 };
 
 // Chunk swizzles: K rows are gathered 8 at a time in the pattern
@@ -123,11 +126,11 @@ __device__ __forceinline__ void issue_tile(const AttnArgs &a, int head, int tile
                                            int wave) {
     using L = Lds<D>;
     constexpr int CH = L::CH;
-    constexpr int PER = kKT * CH / kThreads;         // 16-byte chunks per thread per tensor
+    constexpr int WAVES = kKT * CH / 64;             // waves that load (one 1 KB block each)
+    static_assert(WAVES <= kNW, "tile larger than one load per wave");
     const int lane = threadIdx.x % 64;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int p0 = kThreads * i + 64 * wave;      // first position of this wave's block
+    if (wave < WAVES) {
+        const int p0 = 64 * wave;                     // first position of this wave's block
         const int p = p0 + lane;
         const int row = p / CH, pos = p % CH;
         const int64_t rbase = ((int64_t)head * a.window + slot_of(a, tile * kKT + row)) * D;
@@ -189,8 +192,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     const int qi = qb * kQB + wave * kQW + col;         // this lane's query
     const bool q_ok = qi < a.n_q;
 
-    // start streaming the first tile while Q is prepared
-    if (t0 < t1) issue_tile<D>(a, head, t0, smem, wave);
+    // start streaming the first two tiles while Q is prepared
+    issue_tile<D>(a, head, t0, smem, wave);
+    if (t0 + 1 < t1) issue_tile<D>(a, head, t0 + 1, smem + L::BUF, wave);
 
     // ---- Q: load, rotate (fp32), block absmax -------------------------------
     float qv[NH][32];
@@ -267,19 +271,24 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     const float qfac = (qmax > 0.0f ? qmax / 448.0f : 1.0f) * a.softmax_scale * kLog2e;
     const float inv_cv = cv > 0.0f ? 1.0f / cv : 0.0f;
 
-    // ---- Q -> hi/lo E4M3 B operands ------------------------------------------
-    v8i qhi[NH], qlo[NH];
+    // ---- Q -> hi/lo E4M3 B operands, kept in this wave's LDS area ------------
+    uint8_t *qbase = smem + L::Q_OFF + wave * L::Q_WAVE;
 #pragma unroll
-    for (int h = 0; h < NH; ++h) {
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
-        for (int w = 0; w < 8; ++w) {
-            uint32_t hi, lo;
-            split4(qv[h][4 * w] * qscale, qv[h][4 * w + 1] * qscale, qv[h][4 * w + 2] * qscale,
-                   qv[h][4 * w + 3] * qscale, hi, lo);
-            qhi[h][w] = (int)hi;
-            qlo[h][w] = (int)lo;
+        for (int part = 0; part < 2; ++part) {
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int e = 16 * part + 4 * w;
+                split4(qv[h][e] * qscale, qv[h][e + 1] * qscale, qv[h][e + 2] * qscale,
+                       qv[h][e + 3] * qscale, hi[w], lo[w]);
+            }
+            *reinterpret_cast<u32x4 *>(qbase + ((4 * h + part) * 64 + lane) * 16) =
+                u32x4{hi[0], hi[1], hi[2], hi[3]};
+            *reinterpret_cast<u32x4 *>(qbase + ((4 * h + 2 + part) * 64 + lane) * 16) =
+                u32x4{lo[0], lo[1], lo[2], lo[3]};
         }
-    }
 
     // Lane-constant LDS offsets.  K A-operand: A-row i (= col) of block kb is
     // key 32kb + kk with kk = 16((i>>2)&1) + 4(i>>3) + (i&3); this lane reads
@@ -310,53 +319,75 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
             voff[db][c] = L::K_BYTES + row * D + 16 * (chunk ^ (swz_v(row) & (CH - 1))) + 8 * (j % 2);
         }
 
-    // ---- main loop over key tiles ----------------------------------------------
+    // S^T = K . Q^T of one tile (Q hi and lo terms) for both 32-key blocks
+    auto qk = [&](const uint8_t *buf, v16f (&s)[2]) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s[kb] = v16f{};
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            v8i qop[2];
+#pragma unroll
+            for (int hl = 0; hl < 2; ++hl) {
+                const u32x4 u0 = *reinterpret_cast<const u32x4 *>(qbase + ((4 * h + 2 * hl) * 64 + lane) * 16);
+                const u32x4 u1 = *reinterpret_cast<const u32x4 *>(qbase + ((4 * h + 2 * hl + 1) * 64 + lane) * 16);
+                qop[hl] = v8i{(int)u0[0], (int)u0[1], (int)u0[2], (int)u0[3],
+                              (int)u1[0], (int)u1[1], (int)u1[2], (int)u1[3]};
+            }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const u32x4 u0 = *reinterpret_cast<const u32x4 *>(buf + koff[kb][h][0]);
+                const u32x4 u1 = *reinterpret_cast<const u32x4 *>(buf + koff[kb][h][1]);
+                const v8i ka = {(int)u0[0], (int)u0[1], (int)u0[2], (int)u0[3],
+                                (int)u1[0], (int)u1[1], (int)u1[2], (int)u1[3]};
+                s[kb] = mfma(ka, qop[0], s[kb]);
+                s[kb] = mfma(ka, qop[1], s[kb]);
+            }
+        }
+    };
+
+    // ---- software-pipelined main loop ---------------------------------------------
+    // Tiles are triple buffered: while tile t is consumed, t+1 is resident and
+    // t+2 is in flight.  QK^T of tile t+1 is issued before the softmax of tile
+    // t so the matrix cores work while the VALU does the softmax.
     v16f o[ND];
 #pragma unroll
     for (int d = 0; d < ND; ++d) o[d] = v16f{};
     float lsum = 0.0f;      // this lane's share of the softmax denominator
     float cofs = 0.0f;      // kShift - running max (log2 units)
-    bool started = false;
 
-    if (t0 < t1) {
-        const float f = load_factor(a, head, t0, qfac, inv_cv);
+    {
+        const float f0 = load_factor(a, head, t0, qfac, inv_cv);
+        const float f1 = t0 + 1 < t1 ? load_factor(a, head, t0 + 1, qfac, inv_cv) : 0.0f;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        store_factor<D>(smem, f);
+        store_factor<D>(smem, f0);
+        if (t0 + 1 < t1) store_factor<D>(smem + L::BUF, f1);
     }
     __syncthreads();
+    v16f s_cur[2];
+    qk(smem, s_cur);
 
     for (int t = t0; t < t1; ++t) {
-        uint8_t *buf = smem + ((t - t0) & 1) * L::BUF;
-        uint8_t *nbuf = smem + ((t + 1 - t0) & 1) * L::BUF;
-        const bool more = t + 1 < t1;
-        float nf = 0.0f;
-        if (more) {
-            issue_tile<D>(a, head, t + 1, nbuf, wave);
-            nf = load_factor(a, head, t + 1, qfac, inv_cv);
-        }
+        const int r0 = t - t0;
+        uint8_t *buf = smem + (r0 % 3) * L::BUF;
+        uint8_t *buf1 = smem + ((r0 + 1) % 3) * L::BUF;
+        uint8_t *buf2 = smem + ((r0 + 2) % 3) * L::BUF;
         const float *fa = reinterpret_cast<const float *>(buf + L::F_OFF);
 
-        // S^T = K . Q^T for the two 32-key blocks
-        v16f s[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = v16f{};
-#pragma unroll
-            for (int h = 0; h < NH; ++h) {
-                const u32x4 u0 = *reinterpret_cast<const u32x4 *>(buf + koff[kb][h][0]);
-                const u32x4 u1 = *reinterpret_cast<const u32x4 *>(buf + koff[kb][h][1]);
-                const v8i ka = {(int)u0[0], (int)u0[1], (int)u0[2], (int)u0[3],
-                                (int)u1[0], (int)u1[1], (int)u1[2], (int)u1[3]};
-                s[kb] = mfma(ka, qhi[h], s[kb]);
-                s[kb] = mfma(ka, qlo[h], s[kb]);
-            }
+        // tile t+2 into the buffer of tile t-1 (every wave is past it)
+        const bool more2 = t + 2 < t1;
+        float nf = 0.0f;
+        if (more2) {
+            issue_tile<D>(a, head, t + 2, buf2, wave);
+            nf = load_factor(a, head, t + 2, qfac, inv_cv);
         }
+        v16f s_nxt[2];
+        if (t + 1 < t1) qk(buf1, s_nxt);                  // tile t+1 is resident
 
         // scores (log2 units, shifted by cofs); register r of block kb is key
         // 32kb + 16g + r of the tile
         float mx = -INFINITY;
-        const bool partial = (t + 1) * kKT > a.n_valid;
-        if (!partial) {
+        const int lim = a.n_valid - t * kKT;              // valid keys of this tile
+        if (lim >= kKT) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -364,13 +395,12 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
                     const f32x4 f = *reinterpret_cast<const f32x4 *>(fa + 32 * kb + 16 * g + 4 * q);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float v = s[kb][4 * q + r] * f[r] + cofs;
-                        s[kb][4 * q + r] = v;
+                        const float v = s_cur[kb][4 * q + r] * f[r] + cofs;
+                        s_cur[kb][4 * q + r] = v;
                         mx = fmaxf(mx, v);
                     }
                 }
         } else {
-            const int lim = a.n_valid - t * kKT;          // valid keys of this tile
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -378,20 +408,21 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
                     const f32x4 f = *reinterpret_cast<const f32x4 *>(fa + 32 * kb + 16 * g + 4 * q);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        float v = s[kb][4 * q + r] * f[r] + cofs;
+                        float v = s_cur[kb][4 * q + r] * f[r] + cofs;
                         v = (32 * kb + 16 * g + 4 * q + r < lim) ? v : -INFINITY;
-                        s[kb][4 * q + r] = v;
+                        s_cur[kb][4 * q + r] = v;
                         mx = fmaxf(mx, v);
                     }
                 }
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const bool need = !started || mx > kShift + kTau;
-        if (__any(need)) {
+        const bool first = t == t0;
+        const bool over = mx > kShift + kTau;
+        if (__any(first || over)) {
             float shift = 0.0f;                  // new cofs = cofs - shift
-            if (!started) {
+            if (first) {
                 shift = mx - kShift;
-            } else if (mx > kShift + kTau) {
+            } else if (over) {
                 shift = mx - kShift;
                 const float alpha = __builtin_amdgcn_exp2f(-shift);
                 lsum *= alpha;
@@ -400,8 +431,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
             }
             cofs -= shift;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) s[kb] -= shift;
-            started = true;
+            for (int kb = 0; kb < 2; ++kb) s_cur[kb] -= shift;
         }
 
         // weights p = 2^x, denominator, V-scale fold, hi/lo split -> B operands
@@ -414,7 +444,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
                 float pw[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(s[kb][4 * q + r]);
+                    const float p = __builtin_amdgcn_exp2f(s_cur[kb][4 * q + r]);
                     lsum += p;
                     pw[r] = p * w[r];
                 }
@@ -438,11 +468,15 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
             o[d] = mfma(va, plo, o[d]);
         }
 
-        if (more) {
+        // tile t+2 (loads issued above) is visible to every wave after this
+        // barrier, and every wave is done with tile t
+        if (more2) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            store_factor<D>(nbuf, nf);
+            store_factor<D>(buf2, nf);
         }
         __syncthreads();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
     }
 
     // ---- epilogue ------------------------------------------------------------
@@ -478,7 +512,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
         }
         if (g == 0) {
             // running max in log2 units is kShift - cofs
-            a.part_ml[2 * row] = started ? kShift - cofs : -INFINITY;
+            a.part_ml[2 * row] = kShift - cofs;
             a.part_ml[2 * row + 1] = ltot;
         }
     }
@@ -517,7 +551,7 @@ int attn_default_splits(int n_heads, int n_q, int n_valid) {
     const int n_qb = (n_q + kQB - 1) / kQB;
     const int tiles = (n_valid + kKT - 1) / kKT;
     const int units = n_heads * n_qb;
-    int s = (2 * 256 + units / 2) / units;       // about two workgroups per CU
+    int s = (256 + units / 2) / units;           // about one workgroup per CU
     if (s < 1) s = 1;
     if (s > tiles) s = tiles;
     return s;
