@@ -52,6 +52,7 @@ typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -196,56 +197,58 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     issue_tile<D>(a, head, t0, smem, wave);
     if (t0 + 1 < t1) issue_tile<D>(a, head, t0 + 1, smem + L::BUF, wave);
 
-    // ---- Q: load, rotate (fp32), block absmax -------------------------------
-    float qv[NH][32];
+    // ---- Q: coalesced load, rotate (fp32), block absmax -----------------------
+    // The wave's 32 query rows are read in chunks of 8 elements: lane L takes
+    // chunk L % (D/8) of row (64i + L) / (D/8), so every load instruction reads
+    // whole rows of Q and of the rotary table.
+    constexpr int QCH = D / 8;                            // 8-element chunks per row
+    constexpr int QIT = 32 * QCH / 64;                    // chunks per lane
+    float qv[QIT][8];
 #pragma unroll
-    for (int h = 0; h < NH; ++h) {
-        const int d0 = 64 * h + 32 * g;
-        if (q_ok) {
-            const int64_t off = ((int64_t)qi * a.n_heads + head) * D + d0;
+    for (int i = 0; i < QIT; ++i) {
+        const int r = (i * 64 + lane) / QCH, c = (i * 64 + lane) % QCH;
+        const int qr = qb * kQB + wave * kQW + r;
+        if (qr < a.n_q) {
+            const int64_t off = ((int64_t)qr * a.n_heads + head) * D + 8 * c;
             if (a.dtype == KVR_BF16) {
-                const u32x4 *p = reinterpret_cast<const u32x4 *>(
+                const u32x4 u = *reinterpret_cast<const u32x4 *>(
                     reinterpret_cast<const uint16_t *>(a.q) + off);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const u32x4 u = p[v];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        qv[h][8 * v + 2 * e] = __uint_as_float(u[e] << 16);
-                        qv[h][8 * v + 2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    qv[i][2 * e] = __uint_as_float(u[e] << 16);
+                    qv[i][2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
                 }
             } else {
                 const f32x4 *p = reinterpret_cast<const f32x4 *>(
                     reinterpret_cast<const float *>(a.q) + off);
+                const f32x4 f0 = p[0], f1 = p[1];
 #pragma unroll
-                for (int v = 0; v < 8; ++v) {
-                    const f32x4 f = p[v];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) qv[h][4 * v + e] = f[e];
+                for (int e = 0; e < 4; ++e) {
+                    qv[i][e] = f0[e];
+                    qv[i][4 + e] = f1[e];
                 }
             }
-            const f32x4 *cs = reinterpret_cast<const f32x4 *>(a.cs + (int64_t)qi * D + d0);
+            const f32x4 *cs = reinterpret_cast<const f32x4 *>(a.cs + (int64_t)qr * D + 8 * c);
 #pragma unroll
-            for (int v = 0; v < 8; ++v) {           // two pairs per entry: (c0, s0, c1, s1)
-                const f32x4 c = cs[v];
-                const float x0 = qv[h][4 * v], x1 = qv[h][4 * v + 1];
-                const float x2 = qv[h][4 * v + 2], x3 = qv[h][4 * v + 3];
-                qv[h][4 * v] = x0 * c[0] - x1 * c[1];
-                qv[h][4 * v + 1] = x0 * c[1] + x1 * c[0];
-                qv[h][4 * v + 2] = x2 * c[2] - x3 * c[3];
-                qv[h][4 * v + 3] = x2 * c[3] + x3 * c[2];
+            for (int v = 0; v < 2; ++v) {                 // two pairs per entry: (c0, s0, c1, s1)
+                const f32x4 cc = cs[v];
+                const float x0 = qv[i][4 * v], x1 = qv[i][4 * v + 1];
+                const float x2 = qv[i][4 * v + 2], x3 = qv[i][4 * v + 3];
+                qv[i][4 * v] = x0 * cc[0] - x1 * cc[1];
+                qv[i][4 * v + 1] = x0 * cc[1] + x1 * cc[0];
+                qv[i][4 * v + 2] = x2 * cc[2] - x3 * cc[3];
+                qv[i][4 * v + 3] = x2 * cc[3] + x3 * cc[2];
             }
         } else {
 #pragma unroll
-            for (int e = 0; e < 32; ++e) qv[h][e] = 0.0f;
+            for (int e = 0; e < 8; ++e) qv[i][e] = 0.0f;
         }
     }
     float am = 0.0f;
 #pragma unroll
-    for (int h = 0; h < NH; ++h)
+    for (int i = 0; i < QIT; ++i)
 #pragma unroll
-        for (int e = 0; e < 32; ++e) am = fmaxf(am, fabsf(qv[h][e]));
+        for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(qv[i][e]));
     am = wave_max(am);
 
     // ---- max V scale over this split's keys (folds sv_j into the weights) ---
@@ -272,23 +275,20 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     const float inv_cv = cv > 0.0f ? 1.0f / cv : 0.0f;
 
     // ---- Q -> hi/lo E4M3 B operands, kept in this wave's LDS area ------------
+    // Layout [slice h][hi/lo][16-byte part][lane' = 32g + row] x 16 bytes: lane'
+    // of the MFMA B operand holds d in [64h + 32g, +32) of query row (lane' % 32).
     uint8_t *qbase = smem + L::Q_OFF + wave * L::Q_WAVE;
 #pragma unroll
-    for (int h = 0; h < NH; ++h)
-#pragma unroll
-        for (int part = 0; part < 2; ++part) {
-            uint32_t hi[4], lo[4];
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const int e = 16 * part + 4 * w;
-                split4(qv[h][e] * qscale, qv[h][e + 1] * qscale, qv[h][e + 2] * qscale,
-                       qv[h][e + 3] * qscale, hi[w], lo[w]);
-            }
-            *reinterpret_cast<u32x4 *>(qbase + ((4 * h + part) * 64 + lane) * 16) =
-                u32x4{hi[0], hi[1], hi[2], hi[3]};
-            *reinterpret_cast<u32x4 *>(qbase + ((4 * h + 2 + part) * 64 + lane) * 16) =
-                u32x4{lo[0], lo[1], lo[2], lo[3]};
-        }
+    for (int i = 0; i < QIT; ++i) {
+        const int r = (i * 64 + lane) / QCH, c = (i * 64 + lane) % QCH;
+        const int h = c / 8, gg = (c / 4) % 2, part = (c / 2) % 2;
+        uint32_t hi0, lo0, hi1, lo1;
+        split4(qv[i][0] * qscale, qv[i][1] * qscale, qv[i][2] * qscale, qv[i][3] * qscale, hi0, lo0);
+        split4(qv[i][4] * qscale, qv[i][5] * qscale, qv[i][6] * qscale, qv[i][7] * qscale, hi1, lo1);
+        const int pos = (32 * gg + r) * 16 + 8 * (c % 2);
+        *reinterpret_cast<v2i *>(qbase + (4 * h + part) * 1024 + pos) = v2i{(int)hi0, (int)hi1};
+        *reinterpret_cast<v2i *>(qbase + (4 * h + 2 + part) * 1024 + pos) = v2i{(int)lo0, (int)lo1};
+    }
 
     // Lane-constant LDS offsets.  K A-operand: A-row i (= col) of block kb is
     // key 32kb + kk with kk = 16((i>>2)&1) + 4(i>>3) + (i&3); this lane reads
@@ -480,69 +480,90 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     }
 
     // ---- epilogue ------------------------------------------------------------
+    // Normalised rows o = O * cv / l go through this wave's LDS area (the Q
+    // operands are no longer needed), rows of 2*D bytes whose 8-byte units are
+    // XOR-swizzled by an even function of the row, then out to HBM in whole
+    // 16-byte chunks:
+    // bf16 outputs when there is one split, fp16 partials plus (max, sum) else.
     const float ltot = lsum + __shfl_xor(lsum, 32);
-    if (!q_ok) return;
-    if (a.n_splits == 1) {
-        const float f = ltot > 0.0f ? cv / ltot : 0.0f;
-        uint16_t *dst = a.out + ((int64_t)qi * a.n_heads + head) * D;
+    const float f = ltot > 0.0f ? cv / ltot : 0.0f;
+    const bool to_out = a.n_splits == 1;
+    uint8_t *ob = qbase;
 #pragma unroll
-        for (int d = 0; d < ND; ++d) {
+    for (int d = 0; d < ND; ++d)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int dd = 32 * d + 8 * q + 4 * g;
-                const uint32_t w0 = f32_to_bf16_rne(o[d][4 * q] * f) |
-                                    ((uint32_t)f32_to_bf16_rne(o[d][4 * q + 1] * f) << 16);
-                const uint32_t w1 = f32_to_bf16_rne(o[d][4 * q + 2] * f) |
-                                    ((uint32_t)f32_to_bf16_rne(o[d][4 * q + 3] * f) << 16);
-                *reinterpret_cast<v2i *>(dst + dd) = v2i{(int)w0, (int)w1};
+        for (int q = 0; q < 4; ++q) {
+            const int u = 8 * d + 2 * q + g;              // 8-byte unit of d = 4u .. 4u+3
+            const float x0 = o[d][4 * q] * f, x1 = o[d][4 * q + 1] * f;
+            const float x2 = o[d][4 * q + 2] * f, x3 = o[d][4 * q + 3] * f;
+            uint32_t w0, w1;
+            if (to_out) {
+                w0 = f32_to_bf16_rne(x0) | ((uint32_t)f32_to_bf16_rne(x1) << 16);
+                w1 = f32_to_bf16_rne(x2) | ((uint32_t)f32_to_bf16_rne(x3) << 16);
+            } else {
+                w0 = __builtin_bit_cast(uint32_t, h2{(_Float16)x0, (_Float16)x1});
+                w1 = __builtin_bit_cast(uint32_t, h2{(_Float16)x2, (_Float16)x3});
             }
+            *reinterpret_cast<v2i *>(ob + col * (2 * D) + 8 * (u ^ ((2 * col) & (D / 4 - 2)))) =
+                v2i{(int)w0, (int)w1};
         }
-    } else {
+    if (!to_out && g == 0 && q_ok) {
         const int64_t row = ((int64_t)split * a.n_q + qi) * a.n_heads + head;
-        float *dst = a.part_o + row * D;
+        a.part_ml[2 * row] = kShift - cofs;             // running max, log2 units
+        a.part_ml[2 * row + 1] = ltot;
+    }
+    // the rows were written by other lanes of this wave: wait for the LDS
+    // writes and keep the compiler from moving the reads above them
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    constexpr int RCH = D / 8;                            // 16-byte chunks per row
 #pragma unroll
-        for (int d = 0; d < ND; ++d) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int dd = 32 * d + 8 * q + 4 * g;
-                *reinterpret_cast<f32x4 *>(dst + dd) =
-                    f32x4{o[d][4 * q] * cv, o[d][4 * q + 1] * cv, o[d][4 * q + 2] * cv,
-                          o[d][4 * q + 3] * cv};
-            }
-        }
-        if (g == 0) {
-            // running max in log2 units is kShift - cofs
-            a.part_ml[2 * row] = kShift - cofs;
-            a.part_ml[2 * row + 1] = ltot;
-        }
+    for (int i = 0; i < 32 * RCH / 64; ++i) {
+        const int r = (i * 64 + lane) / RCH, k = (i * 64 + lane) % RCH;
+        const int qr = qb * kQB + wave * kQW + r;
+        if (qr >= a.n_q) continue;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(ob + r * (2 * D) + 8 * ((2 * k) ^ ((2 * r) & (D / 4 - 2))));
+        uint16_t *dst = to_out ? a.out + ((int64_t)qr * a.n_heads + head) * D
+                               : a.part_o + (((int64_t)split * a.n_q + qr) * a.n_heads + head) * D;
+        *reinterpret_cast<u32x4 *>(dst + 8 * k) = v;
     }
 }
 
-// Merge the split partials of (query, head) rows in split order.  D/4 lanes
-// per row, four elements per lane, 256 / (D/4) rows per workgroup.
+// Merge the split partials of (query, head) rows in split order: each split
+// s holds a normalised row o_s (fp16) with its running max m_s (log2 units)
+// and denominator l_s; out = sum_s w_s o_s / sum_s w_s, w_s = l_s 2^(m_s - M).
+// D/8 lanes per row, eight elements per lane.
 template <int D>
 __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
-    constexpr int LPR = D / 4;                       // lanes per row
+    constexpr int LPR = D / 8;                       // lanes per row
     constexpr int RPB = 256 / LPR;                   // rows per workgroup
     const int64_t rows = (int64_t)a.n_q * a.n_heads;
     const int64_t qh = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
     if (qh >= rows) return;
-    const int e = 4 * (threadIdx.x % LPR);
+    const int e = 8 * (threadIdx.x % LPR);
     float m = -INFINITY;
     for (int s = 0; s < a.n_splits; ++s) m = fmaxf(m, a.part_ml[2 * (s * rows + qh)]);
     float l = 0.0f;
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
     for (int s = 0; s < a.n_splits; ++s) {
         const int64_t row = s * rows + qh;
-        const float ms = a.part_ml[2 * row];
-        const float wgt = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - m);
-        l += wgt * a.part_ml[2 * row + 1];
-        acc += wgt * *reinterpret_cast<const f32x4 *>(a.part_o + row * D + e);
+        const float ls = a.part_ml[2 * row + 1];
+        const float wgt = ls > 0.0f ? ls * __builtin_amdgcn_exp2f(a.part_ml[2 * row] - m) : 0.0f;
+        l += wgt;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(a.part_o + row * D + e);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t word = v[k];                  // (bit_cast of a vector element
+            const h2 x = __builtin_bit_cast(h2, word);   //  reference is not reliable)
+            acc[2 * k] += wgt * (float)x[0];
+            acc[2 * k + 1] += wgt * (float)x[1];
+        }
     }
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    const uint32_t w0 = f32_to_bf16_rne(acc[0] * inv) | ((uint32_t)f32_to_bf16_rne(acc[1] * inv) << 16);
-    const uint32_t w1 = f32_to_bf16_rne(acc[2] * inv) | ((uint32_t)f32_to_bf16_rne(acc[3] * inv) << 16);
-    *reinterpret_cast<v2i *>(a.out + qh * D + e) = v2i{(int)w0, (int)w1};
+    u32x4 w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        w[k] = f32_to_bf16_rne(acc[2 * k] * inv) | ((uint32_t)f32_to_bf16_rne(acc[2 * k + 1] * inv) << 16);
+    *reinterpret_cast<u32x4 *>(a.out + qh * D + e) = w;
 }
 
 }  // namespace
@@ -560,7 +581,8 @@ int attn_default_splits(int n_heads, int n_q, int n_valid) {
 size_t attn_workspace_bytes(int n_heads, int head_dim, int n_q, int n_splits) {
     if (n_splits <= 1) return 0;
     const size_t rows = (size_t)n_splits * n_q * n_heads;
-    return rows * head_dim * sizeof(float) + rows * 2 * sizeof(float);
+    const size_t o_bytes = (rows * head_dim * sizeof(uint16_t) + 255) / 256 * 256;
+    return o_bytes + rows * 2 * sizeof(float);
 }
 
 hipError_t launch_attention(const AttnArgs &a, int head_dim, hipStream_t s) {
@@ -570,11 +592,11 @@ hipError_t launch_attention(const AttnArgs &a, int head_dim, hipStream_t s) {
     if (head_dim == 128) {
         hipLaunchKernelGGL(attn_kernel<128>, dim3(grid), dim3(kThreads), Lds<128>::TOTAL, s, a);
         if (a.n_splits > 1)
-            hipLaunchKernelGGL(combine_kernel<128>, dim3((rows + 7) / 8), dim3(256), 0, s, a);
+            hipLaunchKernelGGL(combine_kernel<128>, dim3((rows + 15) / 16), dim3(256), 0, s, a);
     } else {
         hipLaunchKernelGGL(attn_kernel<64>, dim3(grid), dim3(kThreads), Lds<64>::TOTAL, s, a);
         if (a.n_splits > 1)
-            hipLaunchKernelGGL(combine_kernel<64>, dim3((rows + 15) / 16), dim3(256), 0, s, a);
+            hipLaunchKernelGGL(combine_kernel<64>, dim3((rows + 31) / 32), dim3(256), 0, s, a);
     }
     return hipGetLastError();
 }

@@ -59,7 +59,7 @@ struct AttnArgs {
     const void *q;                    // [n_q][H][D]
     const float *cs;                  // rotary table row of position q_pos_start
     uint16_t *out;                    // [n_q][H][D] bf16
-    float *part_o;                    // [splits][n_q][H][D]
+    uint16_t *part_o;                 // [splits][n_q][H][D] fp16, normalised rows
     float *part_ml;                   // [splits][n_q][H][2]
     int32_t n_heads, window, slot_start, n_valid, n_q, dtype;
     int32_t n_splits, tiles_per_split;

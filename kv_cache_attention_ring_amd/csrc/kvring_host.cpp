@@ -301,8 +301,10 @@ int32_t attn_fp8_window(const kvr_cache *cache, int32_t layer, int32_t slot_star
     a.tiles_per_split = tps;
     a.softmax_scale = softmax_scale;
     if (n_splits > 1) {
-        a.part_o = static_cast<float *>(ws);
-        a.part_ml = a.part_o + (size_t)n_splits * n_q * cache->n_heads * D;
+        const size_t rows = (size_t)n_splits * n_q * cache->n_heads;
+        const size_t o_bytes = (rows * D * sizeof(uint16_t) + 255) / 256 * 256;
+        a.part_o = static_cast<uint16_t *>(ws);
+        a.part_ml = reinterpret_cast<float *>(static_cast<char *>(ws) + o_bytes);
     }
     return launch_status(kvr::launch_attention(a, D, static_cast<hipStream_t>(stream)), "attention");
 }

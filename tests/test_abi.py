@@ -160,11 +160,16 @@ def test_attention_validation():
     assert _attn(c, 5788, qpos=9500) == K.KVR_EINVAL
     # more than one split needs a workspace of the advertised size
     need = K.lib().attn_fp8_window_workspace_bytes(ctypes.byref(c), 757, 5788, 4)
-    assert need == 4 * 757 * 12 * (128 + 2) * 4
+    assert need == _ws_bytes(4 * 757 * 12, 128)
     assert _attn(c, 5788, n_splits=4) == K.KVR_EINVAL
     assert _attn(c, 5788, n_splits=4, ws=FAKE + 0x9000000, ws_bytes=need - 4) == K.KVR_EINVAL
     assert _attn(c, 5788, n_splits=4, ws=FAKE + 0x9000010, ws_bytes=need) == K.KVR_EALIGN
     assert _attn(_cache(D=256), 5788) == K.KVR_EUNSUPPORTED
+
+
+def _ws_bytes(rows, D):
+    # fp16 normalised partial rows (padded to 256 bytes) + fp32 (max, sum) per row
+    return (rows * D * 2 + 255) // 256 * 256 + rows * 2 * 4
 
 
 def test_workspace_sizes_and_split_clamping():
@@ -173,10 +178,10 @@ def test_workspace_sizes_and_split_clamping():
     # one split needs no workspace
     assert lib.attn_fp8_window_workspace_bytes(ctypes.byref(c), 16, 96, 1) == 0
     # 96 keys are two 64-key tiles: a request for 8 splits is clamped to 2
-    assert lib.attn_fp8_window_workspace_bytes(ctypes.byref(c), 16, 96, 8) == 2 * 16 * 2 * 66 * 4
+    assert lib.attn_fp8_window_workspace_bytes(ctypes.byref(c), 16, 96, 8) == _ws_bytes(2 * 16 * 2, 64)
     # 9 tiles in 4 requested splits -> 3 tiles per split -> 3 splits, none empty
     c2 = _cache(D=64, W=576, H=1)
-    assert lib.attn_fp8_window_workspace_bytes(ctypes.byref(c2), 1, 576, 4) == 3 * 1 * 1 * 66 * 4
+    assert lib.attn_fp8_window_workspace_bytes(ctypes.byref(c2), 1, 576, 4) == _ws_bytes(3, 64)
 
 
 @no_gpu
