@@ -89,7 +89,7 @@ def main():
 
     def attend(layer, pss, start):
         K.attn_fp8_window(cache, layer, start, ring.n_valid, qpool[pss * L + layer], ring.pos_next - N,
-                          rope, out=outs[layer], n_splits=args.splits, ws=ws)
+                          rope.base, out=outs[layer], n_splits=args.splits, ws=ws)
 
     def step(step_idx):
         write(step_idx)
@@ -230,7 +230,7 @@ def run_naive(args, K, inputs, shp, rope, chunks, qpool, outs, ws, torch, dev, p
     def upkeep(layer, k, v):
         a = wins[layer]
         s = ping[0]
-        K.naive_upkeep(a[2 * s], a[2 * s + 1], k[layer], v[layer], ring.n_valid, ring.pos_next, rope,
+        K.naive_upkeep(a[2 * s], a[2 * s + 1], k[layer], v[layer], ring.n_valid, ring.pos_next, rope.base,
                        a[2 - 2 * s], a[3 - 2 * s], lin.k_codes[layer], lin.v_codes[layer],
                        lin.k_scales[layer], lin.v_scales[layer])
 
@@ -249,7 +249,7 @@ def run_naive(args, K, inputs, shp, rope, chunks, qpool, outs, ws, torch, dev, p
             for layer in range(L):
                 upkeep(layer, k, v)
                 if with_attn:
-                    K.attn_fp8_window(lin, layer, 0, n_valid, qpool[p * L + layer], ring.pos_next, rope,
+                    K.attn_fp8_window(lin, layer, 0, n_valid, qpool[p * L + layer], ring.pos_next, rope.base,
                                       out=outs[layer], n_splits=args.splits, ws=ws)
         ping[0] = 1 - ping[0]
         K.kvr_ring_after_write(ring, W, N)

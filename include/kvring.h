@@ -145,7 +145,8 @@ int32_t kv_delta_rebase(const kvr_cache *cache, const kvr_ring *ring, int32_t la
  *   O[i][h] = sum_j softmax_j(softmax_scale * q_i . k^_j) v^_j
  * over the n_valid cached keys of `layer` at slots (slot_start + j) mod window
  * (non-causal; every query sees every valid key), q_i rotated at position
- * q_pos_start + i, k^ / v^ the dequantised cache rows.  Keys are visited in
+ * q_pos_start + i with frequencies rope_base^(-2i/head_dim), k^ / v^ the
+ * dequantised cache rows.  Keys are visited in
  * this logical order, so a linear window (slot_start = 0) holding the same
  * rows gives a bit-identical result.
  * On the GPU, Q is split into two E4M3 terms (hi + lo, one scale per call
@@ -160,12 +161,12 @@ int32_t kv_delta_rebase(const kvr_cache *cache, const kvr_ring *ring, int32_t la
  *   ws      : device workspace of attn_fp8_window_workspace_bytes(...) bytes
  *             (may be NULL when that is 0), 256-byte aligned.
  * Errors: KVR_EINVAL (null, n_valid not in [1, window], slot_start out of
- * range, table range, workspace too small), KVR_EALIGN, KVR_EUNSUPPORTED. */
+ * range, rope_base <= 1, workspace too small), KVR_EALIGN, KVR_EUNSUPPORTED. */
 size_t  attn_fp8_window_workspace_bytes(const kvr_cache *cache, int32_t n_q, int32_t n_valid,
                                         int32_t n_splits);
 int32_t attn_fp8_window(const kvr_cache *cache, int32_t layer, int32_t slot_start,
                         int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
-                        int64_t q_pos_start, float softmax_scale, const kvr_rope_table *rope,
+                        int64_t q_pos_start, float softmax_scale, double rope_base,
                         uint16_t *out, int32_t n_splits, void *ws, size_t ws_bytes,
                         void *stream);
 

@@ -254,7 +254,7 @@ size_t attn_fp8_window_workspace_bytes(const kvr_cache *cache, int32_t n_q, int3
 
 int32_t attn_fp8_window(const kvr_cache *cache, int32_t layer, int32_t slot_start,
                         int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
-                        int64_t q_pos_start, float softmax_scale, const kvr_rope_table *rope,
+                        int64_t q_pos_start, float softmax_scale, double rope_base,
                         uint16_t *out, int32_t n_splits, void *ws, size_t ws_bytes,
                         void *stream) {
     if (int32_t e = check_cache(cache)) return e;
@@ -270,8 +270,7 @@ int32_t attn_fp8_window(const kvr_cache *cache, int32_t layer, int32_t slot_star
     if (!aligned16(q) || !aligned16(out)) return fail(KVR_EALIGN, "q/out not 16-byte aligned");
     if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale))
         return fail(KVR_EINVAL, "softmax_scale must be positive and finite");
-    const float *cs;
-    if (int32_t e = table_rows(rope, D, q_pos_start, n_q, &cs)) return e;
+    if (!(rope_base > 1.0) || !isfinite(rope_base)) return fail(KVR_EINVAL, "rotary base must be > 1");
     if (n_splits < 0) return fail(KVR_EINVAL, "n_splits %d < 0", n_splits);
     int32_t tps;
     n_splits = effective_splits(cache->n_heads, n_q, n_valid, n_splits, &tps);
@@ -289,7 +288,8 @@ int32_t attn_fp8_window(const kvr_cache *cache, int32_t layer, int32_t slot_star
     a.k_scales = cache->k_scales + lay;
     a.v_scales = cache->v_scales + lay;
     a.q = q;
-    a.cs = cs;
+    a.theta = make_theta(D, rope_base);
+    a.q_pos0 = q_pos_start;
     a.out = out;
     a.n_heads = cache->n_heads;
     a.window = W;

@@ -67,7 +67,7 @@ _SIGS = {
                                _I64, _F64, _P]),
     "attn_fp8_window_workspace_bytes": (_SZ, [ctypes.POINTER(kvr_cache), _I32, _I32, _I32]),
     "attn_fp8_window": (_I32, [ctypes.POINTER(kvr_cache), _I32, _I32, _I32, _P, _I32, _I32, _I64,
-                               _F32, ctypes.POINTER(kvr_rope_table), _P, _I32, _P, _SZ, _P]),
+                               _F32, _F64, _P, _I32, _P, _SZ, _P]),
     "naive_upkeep": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32,
                             ctypes.POINTER(kvr_rope_table), _P, _P, _P, _P, _P, _P, _P]),
     "kvr_last_error": (ctypes.c_char_p, []),
@@ -225,7 +225,7 @@ def attn_fp8_window_workspace_bytes(cache: KVCache, n_q: int, n_valid: int, n_sp
 
 
 def attn_fp8_window(cache: KVCache, layer: int, slot_start: int, n_valid: int, q: torch.Tensor,
-                    q_pos_start: int, rope: RopeTable, out: torch.Tensor | None = None,
+                    q_pos_start: int, rope_base: float = 10000.0, out: torch.Tensor | None = None,
                     n_splits: int = 0, ws: torch.Tensor | None = None,
                     softmax_scale: float | None = None, stream=None) -> torch.Tensor:
     """q: [n_q][H][D] bf16/fp32 -> out: [n_q][H][D] bf16."""
@@ -244,10 +244,9 @@ def attn_fp8_window(cache: KVCache, layer: int, slot_start: int, n_valid: int, q
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(cache.head_dim)
     c = cache.desc()
-    t = rope.desc()
     _check(lib().attn_fp8_window(ctypes.byref(c), layer, slot_start, n_valid, _dev(q, "q"),
                                  _dtype_code(q), n_q, int(q_pos_start), float(softmax_scale),
-                                 ctypes.byref(t), _dev(out, "out"), int(n_splits), ws_ptr, ws_len,
+                                 float(rope_base), _dev(out, "out"), int(n_splits), ws_ptr, ws_len,
                                  _stream(stream)))
     return out
 

@@ -139,11 +139,9 @@ def test_rebase_validation():
 
 
 def _attn(cache, n_valid, slot_start=0, n_q=757, q=FAKE + 0x7000000, out=FAKE + 0x8000000,
-          table=None, ws=None, ws_bytes=0, n_splits=1, scale=0.088, layer=0, qpos=0):
-    table = table or _table()
+          base=10000.0, ws=None, ws_bytes=0, n_splits=1, scale=0.088, layer=0, qpos=0):
     return K.lib().attn_fp8_window(ctypes.byref(cache), layer, slot_start, n_valid, q, K.KVR_BF16,
-                                   n_q, qpos, scale, ctypes.byref(table), out, n_splits, ws,
-                                   ws_bytes, None)
+                                   n_q, qpos, scale, base, out, n_splits, ws, ws_bytes, None)
 
 
 @no_gpu
@@ -157,7 +155,7 @@ def test_attention_validation():
     assert _attn(c, 5788, out=0) == K.KVR_EINVAL
     assert _attn(c, 5788, scale=0.0) == K.KVR_EINVAL
     assert _attn(c, 5788, layer=1) == K.KVR_EINVAL
-    assert _attn(c, 5788, qpos=9500) == K.KVR_EINVAL
+    assert _attn(c, 5788, base=1.0) == K.KVR_EINVAL
     # more than one split needs a workspace of the advertised size
     need = K.lib().attn_fp8_window_workspace_bytes(ctypes.byref(c), 757, 5788, 4)
     assert need == _ws_bytes(4 * 757 * 12, 128)

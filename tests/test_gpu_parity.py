@@ -160,7 +160,7 @@ class SmallRun:
         n_q = q.shape[0]
         qpos = self.ring.pos_next - n_q
         start = K.kvr_ring_logical_start(self.ring, W)
-        out = K.attn_fp8_window(self.cache, 0, start, self.ring.n_valid, qd, qpos, self.rope,
+        out = K.attn_fp8_window(self.cache, 0, start, self.ring.n_valid, qd, qpos, self.rope.base,
                                 n_splits=n_splits)
         if naive_too:
             lin_cache = K.KVCache(1, self.s.n_heads, self.s.head_dim, W)
@@ -168,7 +168,7 @@ class SmallRun:
             lin_cache.v_codes[0].copy_(self.lv)
             lin_cache.k_scales[0].copy_(self.lks)
             lin_cache.v_scales[0].copy_(self.lvs)
-            out_lin = K.attn_fp8_window(lin_cache, 0, 0, self.ring.n_valid, qd, qpos, self.rope,
+            out_lin = K.attn_fp8_window(lin_cache, 0, 0, self.ring.n_valid, qd, qpos, self.rope.base,
                                         n_splits=n_splits)
             torch.cuda.synchronize()
             assert torch.equal(out, out_lin), "ring and naive attention differ"
@@ -222,7 +222,7 @@ def test_edge_cases_small():
         q = inputs.np_queries(shp, 0, 0)[:n_q].copy()
         qpos = run.ring.pos_next - n_q
         out = K.attn_fp8_window(run.cache, 0, 0, run.ring.n_valid, torch.from_numpy(q).cuda(), qpos,
-                                run.rope)
+                                run.rope.base)
         torch.cuda.synchronize()
         assert_attention(_f32(out), oracle.attention(run.orc, 0, run.ring.n_valid, q, qpos),
                          f"n_q={n_q}")
@@ -230,12 +230,12 @@ def test_edge_cases_small():
     _say("edge n_valid=1")
     q = inputs.np_queries(shp, 0, 1)
     qd = torch.from_numpy(q).cuda()
-    out = K.attn_fp8_window(run.cache, 0, 0, 1, qd, 0, run.rope)
+    out = K.attn_fp8_window(run.cache, 0, 0, 1, qd, 0, run.rope.base)
     torch.cuda.synchronize()
     ref = oracle.attention(run.orc, 0, 1, q, 0)
     assert_attention(_f32(out), ref, "n_valid=1")
     # zero queries: uniform weights
-    out0 = K.attn_fp8_window(run.cache, 0, 0, 16, torch.zeros_like(qd), 0, run.rope)
+    out0 = K.attn_fp8_window(run.cache, 0, 0, 16, torch.zeros_like(qd), 0, run.rope.base)
     torch.cuda.synchronize()
     assert_attention(_f32(out0), oracle.attention(run.orc, 0, 16, np.zeros_like(q), 0), "q=0")
 
@@ -314,7 +314,7 @@ def test_page_attention_parity(page_layer):
         rows = _page_rows(shp.n_new, shp.n_heads, seed=p)
         ref = oracle.attention(orc, start, ring.n_valid, _f32(q), ring.pos_next - shp.n_new, rows=rows)
         for n_splits in ((0, 1) if p == 0 else (0,)):
-            out = K.attn_fp8_window(c, 0, start, ring.n_valid, qd, ring.pos_next - shp.n_new, rope,
+            out = K.attn_fp8_window(c, 0, start, ring.n_valid, qd, ring.pos_next - shp.n_new, rope.base,
                                     n_splits=n_splits)
             torch.cuda.synchronize()
             got = _f32(out)
@@ -324,7 +324,7 @@ def test_page_attention_parity(page_layer):
             assert np.isfinite(got).all()
         if p == 0:
             # the same call twice (same split count) gives bit-identical outputs
-            again = K.attn_fp8_window(c, 0, start, ring.n_valid, qd, ring.pos_next - shp.n_new, rope,
+            again = K.attn_fp8_window(c, 0, start, ring.n_valid, qd, ring.pos_next - shp.n_new, rope.base,
                                       n_splits=n_splits)
             torch.cuda.synchronize()
             assert torch.equal(out, again), "attention is not deterministic"
@@ -371,8 +371,8 @@ def test_page_naive_matches_ring():
     for n in ("k_codes", "v_codes", "k_scales", "v_scales"):
         assert torch.equal(getattr(cache, n)[0][:, idx], getattr(lc, n)[0]), n
     q = inputs.torch_queries(shp, 9, 0, 0, "cuda")
-    a = K.attn_fp8_window(cache, 0, start, W, q, ring.pos_next - N, rope)
-    b = K.attn_fp8_window(lc, 0, 0, W, q, ring.pos_next - N, rope)
+    a = K.attn_fp8_window(cache, 0, start, W, q, ring.pos_next - N, rope.base)
+    b = K.attn_fp8_window(lc, 0, 0, W, q, ring.pos_next - N, rope.base)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
 
