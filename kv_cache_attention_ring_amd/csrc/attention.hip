@@ -77,21 +77,25 @@ constexpr int kQB = kQW * kNW;    // queries per workgroup
 constexpr float kTau = 16.0f;     // lazy-rescale threshold (log2 units)
 constexpr float kShift = 0.0f;    // weights are 2^(x - m + kShift) <= 2^(kShift + kTau)
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kNBuf = 5;          // FP8 tile buffers (tiles in flight + the one consumed)
 
 template <int D>
 struct Lds {
     static constexpr int CH = D / 16;            // 16-byte chunks per row
+    // dequantised V^T of one tile: [d][64 keys] bf16, 128-byte rows, triple buffered
+    static constexpr int VT_BYTES = D * kKT * 2;
+    // one FP8 tile buffer: K rows, V rows, then the per-key factors, 64 floats
+    // per wave of which the first 16 are used: wave w < 4 holds a_j of keys
+    // 16w .. 16w+15, wave w >= 4 sv_j of keys 16(w-4) .. +15
     static constexpr int K_BYTES = kKT * D;
     static constexpr int V_BYTES = kKT * D;
     static constexpr int F_OFF = K_BYTES + V_BYTES;
-    static constexpr int BUF = F_OFF + 2 * kKT * 4;
-    // dequantised V^T of one tile: [d][64 keys] bf16, 128-byte rows
-    static constexpr int VT_BYTES = D * kKT * 2;
-    static constexpr int VT_OFF = 3 * BUF;       // FP8 tiles are triple buffered
-    // Q operands of one wave: [slice][hi/lo][16-byte part][lane] x 16 bytes
-    static constexpr int Q_WAVE = (D / 64) * 2 * 2 * 64 * 16;
-    static constexpr int Q_OFF = VT_OFF + 2 * VT_BYTES;   // V^T double buffered
-    static constexpr int TOTAL = Q_OFF + kNW * Q_WAVE;
+    static constexpr int BUF = F_OFF + kNW * 64 * 4;
+    static constexpr int TILE_OFF = 3 * VT_BYTES;
+    static constexpr int TOTAL = TILE_OFF + kNBuf * BUF;
+    // after the loop the tile buffers stage the output rows (2D bytes each)
+    static constexpr int OUT_WAVE = kQW * 2 * D;
+    static_assert(kNW * OUT_WAVE <= kNBuf * BUF, "output staging fits the tile buffers");
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
@@ -138,6 +142,46 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// ds_read_b64_tr_b8 issued from inline assembly.  The compiler treats a
+// transposing read of a direct-to-LDS (global_load_lds) target as aliasing
+// every load still in flight and waits for all of them (vmcnt(0)) first,
+// which would serialise the tile prefetch; here the read's own completion is
+// waited for explicitly with lds_wait(), which also orders the uses of the
+// result after the wait.  Loads the compiler does not see only make its
+// own lgkmcnt waits more conservative, never insufficient, since LDS
+// operations complete in issue order.
+__device__ __forceinline__ v2i lds_read_tr8(const uint8_t *p) {
+    v2i r;
+    const uint32_t addr = (uint32_t)(uintptr_t)(LDS_AS const void *)p;
+    asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(r) : "v"(addr));
+    return r;
+}
+__device__ __forceinline__ void lds_wait(v2i &r) { asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r)); }
+
+// Q words are loaded with inline assembly and waited for explicitly: the
+// compiler's own wait before their first use would be vmcnt(0) once tile
+// loads (global_load_lds) have been issued behind them, i.e. it would wait
+// for the whole tile prefetch.  qwait<N> leaves the N newest loads in flight.
+__device__ __forceinline__ u32x4 gload16(const void *p) {
+    u32x4 r;
+    asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p));
+    return r;
+}
+template <int N, int W>
+__device__ __forceinline__ void qwait(u32x4 (&q)[W]) {
+    asm volatile("s_waitcnt vmcnt(%1)" : "+v"(q[0]) : "n"(N));
+#pragma unroll
+    for (int i = 1; i < W; ++i) asm volatile("" : "+v"(q[i]));
+}
+
+// Workgroup barrier for LDS traffic only.  __syncthreads() also orders
+// global memory, and because a global_load_lds counts as an outstanding
+// memory write the compiler would put s_waitcnt vmcnt(0) in front of it,
+// i.e. wait for every tile still streaming in.  Tiles are made visible by
+// each wave's own vmcnt wait before the barrier instead.  The "memory"
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -150,54 +194,87 @@ __device__ __forceinline__ int slot_of(const AttnArgs &a, int idx) {
     return s >= a.window ? s - a.window : s;
 }
 
-// Issue the direct global -> LDS loads of one K and one V tile; the four
-// waves 0..3 load it (1 KB blocks, 16 bytes a lane).  LDS chunk position p
-// (row p / CH) receives global chunk (p % CH) ^ swizzle(row).
-constexpr int kLoadWaves = 4;
+// Tile streaming.  Every wave loads its eighth of each tile straight into
+// LDS (global_load_lds, no VGPR staging), with all 64 lanes active so the
+// loads carry no control flow: 16-byte chunks of K and V rows (D = 128: each
+// wave 1 KB of K and 1 KB of V; D = 64: waves 0..3 1 KB of K, 4..7 1 KB of
+// V), where LDS chunk position p of row p / CH receives global chunk
+// (p % CH) ^ swizzle(row); and the per-key scales, 4 bytes a lane (lanes
+// 16..63 repeat lanes 0..15).  That is a fixed number of loads per wave and
+// tile, so a wave's vmcnt says how many of its tiles are still in flight;
+// each wave waits for its own part of a tile before the barrier that
+// publishes it.
 template <int D>
-__device__ __forceinline__ void issue_tile(const AttnArgs &a, int head, int tile, uint8_t *buf,
-                                           int wave) {
+constexpr int ops_per_tile() { return D == 128 ? 3 : 2; }
+
+template <int D>
+__device__ __forceinline__ void issue_tile(const AttnArgs &a, const uint8_t *kh, const uint8_t *vh,
+                                           const float *scales_h, int tile, uint8_t *buf, int wave) {
     using L = Lds<D>;
     constexpr int CH = L::CH;
-    constexpr int BLOCKS = kKT * CH / 64;            // 1 KB blocks per K (or V) tile
-    static_assert(BLOCKS % kLoadWaves == 0, "whole blocks per loading wave");
     const int lane = threadIdx.x % 64;
-#pragma unroll
-    for (int i = 0; i < BLOCKS / kLoadWaves; ++i) {
-        const int p0 = 64 * (wave + kLoadWaves * i);  // first position of this block
+    if constexpr (D == 128) {
+        const int p0 = 64 * wave;
         const int p = p0 + lane;
         const int row = p / CH, pos = p % CH;
-        const int64_t rbase = ((int64_t)head * a.window + slot_of(a, tile * kKT + row)) * D;
-        const uint8_t *gk = a.k_codes + rbase + 16 * (pos ^ (swz_k(row) & (CH - 1)));
-        const uint8_t *gv = a.v_codes + rbase + 16 * (pos ^ (swz_v(row) & (CH - 1)));
-        __builtin_amdgcn_global_load_lds(gk, (LDS_AS void *)(buf + 16 * p0), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(gv, (LDS_AS void *)(buf + L::K_BYTES + 16 * p0), 16, 0, 0);
+        const uint32_t srow = (uint32_t)slot_of(a, tile * kKT + row) * D;
+        const uint32_t offk = srow + 16 * (pos ^ (swz_k(row) & (CH - 1)));
+        const uint32_t offv = srow + 16 * (pos ^ (swz_v(row) & (CH - 1)));
+        __builtin_amdgcn_global_load_lds(kh + offk, (LDS_AS void *)(buf + 16 * p0), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vh + offv, (LDS_AS void *)(buf + L::K_BYTES + 16 * p0), 16, 0, 0);
+    } else {
+        const bool is_k = wave < 4;
+        const int p0 = 64 * (wave % 4);
+        const int p = p0 + lane;
+        const int row = p / CH, pos = p % CH;
+        const uint32_t off = (uint32_t)slot_of(a, tile * kKT + row) * D +
+                             16 * (pos ^ ((is_k ? swz_k(row) : swz_v(row)) & (CH - 1)));
+        __builtin_amdgcn_global_load_lds((is_k ? kh : vh) + off,
+                                         (LDS_AS void *)(buf + (is_k ? 0 : L::K_BYTES) + 16 * p0), 16, 0, 0);
+    }
+    const int key = 16 * (wave % 4) + lane % 16;
+    __builtin_amdgcn_global_load_lds(scales_h + slot_of(a, tile * kKT + key),
+                                     (LDS_AS void *)(buf + L::F_OFF + 256 * wave), 4, 0, 0);
+}
+
+// factor slot of key k (0..63): K a_j or V sv_j
+__device__ __forceinline__ int fk_index(int k) { return 64 * (k >> 4) + (k & 15); }
+__device__ __forceinline__ int fv_index(int k) { return 64 * (4 + (k >> 4)) + (k & 15); }
+
+// After its part of a tile has landed, each wave finishes its 16 factors in
+// place: K scales times the query-block factor, zero for keys past n_valid.
+template <int D>
+__device__ __forceinline__ void finish_factors(const AttnArgs &a, uint8_t *buf, int tile, int wave,
+                                               float qfac) {
+    const int lane = threadIdx.x % 64;
+    if (lane < 16) {
+        float *f = reinterpret_cast<float *>(buf + Lds<D>::F_OFF) + 64 * wave + lane;
+        const int key = 16 * (wave % 4) + lane;
+        const float v = *f;
+        *f = tile * kKT + key < a.n_valid ? (wave < 4 ? v * qfac : v) : 0.0f;
     }
 }
 
-// Per-key scales of a tile: wave 0 loads sk_j, wave 1 sv_j from `scales`
-// (chosen once per wave); raw, so the load is not waited for until the
-// scale is stored.
-__device__ __forceinline__ float load_factor(const AttnArgs &a, const float *scales, int head,
-                                             int tile) {
-    const int idx = tile * kKT + (int)(threadIdx.x % 64);
-    if (idx >= a.n_valid) return 0.0f;
-    return scales[(int64_t)head * a.window + slot_of(a, idx)];
+// Wait until at most `later` of this wave's tiles issued after the awaited
+// one are still in flight (the count must be an immediate).
+template <int D>
+__device__ __forceinline__ void wait_tiles(int later) {
+    constexpr int OPT = ops_per_tile<D>();
+    static_assert(OPT * (kNBuf - 2) <= 63, "vmcnt range");
+    if (later <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(OPT) : "memory");
+    else if (later == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * OPT) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * OPT) : "memory");
 }
 
-// Stores the factors of a tile: a_j = sk_j * qfac (threads 0..63), sv_j (64..127).
-template <int D>
-__device__ __forceinline__ void store_factor(uint8_t *buf, float f, float qfac) {
-    if (threadIdx.x < 2 * kKT)
-        reinterpret_cast<float *>(buf + Lds<D>::F_OFF)[threadIdx.x] = threadIdx.x < kKT ? f * qfac : f;
-}
-
-template <int D>
+template <int D, bool BF16>
 __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     using L = Lds<D>;
     constexpr int CH = L::CH;
     constexpr int NH = D / 64;          // 64-wide d slices of the QK^T contraction
     constexpr int ND = D / 32;          // 32-row d blocks of O^T
+    constexpr int P = kNBuf - 1;        // tiles in flight ahead of the one consumed
+    static_assert(P - 1 <= 3, "wait_tiles covers up to three later tiles");
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ float red[kNW];
 
@@ -220,99 +297,106 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     const int n_tiles = (a.n_valid + kKT - 1) / kKT;
     const int t0 = split * a.tiles_per_split;
     const int t1 = min(n_tiles, t0 + a.tiles_per_split);
+    const int n = t1 - t0;
 
     const int tid = threadIdx.x, lane = tid % 64;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int g = lane / 32, col = lane % 32;
     const int qi = qb * kQB + wave * kQW + col;         // this lane's query
     const bool q_ok = qi < a.n_q;
+    const bool lead = wave < kNW / 2;
+    const int64_t hoff = (int64_t)head * a.window;
+    const uint8_t *kh = a.k_codes + hoff * D, *vh = a.v_codes + hoff * D;
+    const float *scales_h = (wave < 4 ? a.k_scales : a.v_scales) + hoff;
+    uint8_t *tiles = smem + L::TILE_OFF;
+    uint8_t *vt_base = smem + 0;
 
-    // start streaming the first two tiles while Q is prepared
-    const bool lead = wave < kLoadWaves;
-    const float *my_scales = wave == 0 ? a.k_scales : a.v_scales;   // used by waves 0, 1
-    if (lead) {
-        issue_tile<D>(a, head, t0, smem, wave);
-        if (t0 + 1 < t1) issue_tile<D>(a, head, t0 + 1, smem + L::BUF, wave);
+    // ---- Q straight into MFMA B-operand order ----------------------------------
+    // Lane (query, g) holds d in [64h + 32g, +32) of its query for each slice h:
+    // 64 contiguous bytes (bf16) per slice.  The raw words are loaded first
+    // (rows past n_q read row n_q-1 and are zeroed later), the tiles are
+    // issued behind them, and only then are the words unpacked, so the wait
+    // for Q does not hold back the tile stream.
+    constexpr int QV = NH * 32;                           // Q elements per lane
+    constexpr int QW = BF16 ? QV / 8 : QV / 4;            // 16-byte words per lane
+    u32x4 qraw[QW];
+    {
+        const int64_t row = ((int64_t)min(qi, a.n_q - 1) * a.n_heads + head) * D;
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            const int d0 = 64 * h + 32 * g;
+            const u32x4 *src = BF16 ? reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(a.q) + row + d0)
+                                    : reinterpret_cast<const u32x4 *>(reinterpret_cast<const float *>(a.q) + row + d0);
+#pragma unroll
+            for (int c = 0; c < QW / NH; ++c) qraw[(QW / NH) * h + c] = gload16(src + c);
+        }
     }
 
-    // ---- Q: coalesced load, rotate (fp32), block absmax -----------------------
-    // The wave's 32 query rows are read in chunks of 8 elements: lane L takes
-    // chunk L % (D/8) of row (64i + L) / (D/8), so every load instruction reads
-    // whole rows of Q and of the rotary table.
-    constexpr int QCH = D / 8;                            // 8-element chunks per row
-    constexpr int QIT = 32 * QCH / 64;                    // chunks per lane
-    float qv[QIT][8];
+    // start streaming the first P tiles (and their scales); always P of them,
+    // so the compiler can count them in its wait for Q (a split shorter than
+    // P tiles reloads its last tile into the spare buffers)
 #pragma unroll
-    for (int i = 0; i < QIT; ++i) {
-        const int r = (i * 64 + lane) / QCH, c = (i * 64 + lane) % QCH;
-        const int qr = qb * kQB + wave * kQW + r;
-        if (qr < a.n_q) {
-            const int64_t off = ((int64_t)qr * a.n_heads + head) * D + 8 * c;
-            if (a.dtype == KVR_BF16) {
-                const u32x4 u = *reinterpret_cast<const u32x4 *>(
-                    reinterpret_cast<const uint16_t *>(a.q) + off);
+    for (int k = 0; k < P; ++k)
+        issue_tile<D>(a, kh, vh, scales_h, min(t0 + k, t1 - 1), tiles + k * L::BUF, wave);
+    qwait<P * ops_per_tile<D>()>(qraw);
+
+    float qv[QV];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    qv[i][2 * e] = __uint_as_float(u[e] << 16);
-                    qv[i][2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
-                }
+    for (int w = 0; w < QW; ++w)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (BF16) {
+                qv[8 * w + 2 * e] = q_ok ? __uint_as_float(qraw[w][e] << 16) : 0.0f;
+                qv[8 * w + 2 * e + 1] = q_ok ? __uint_as_float(qraw[w][e] & 0xFFFF0000u) : 0.0f;
             } else {
-                const f32x4 *p = reinterpret_cast<const f32x4 *>(
-                    reinterpret_cast<const float *>(a.q) + off);
-                const f32x4 f0 = p[0], f1 = p[1];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    qv[i][e] = f0[e];
-                    qv[i][4 + e] = f1[e];
-                }
+                qv[4 * w + e] = q_ok ? __uint_as_float(qraw[w][e]) : 0.0f;
             }
-            // rotation angle p * theta_i in fp64, reduced to [-1/2, 1/2]
-            // revolutions, then the hardware sin/cos (revolution input)
-            const double pos = (double)(a.q_pos0 + qr);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const double rev = pos * a.theta.t[4 * c + e] * 0.15915494309189535;
-                const float fr = (float)(rev - __builtin_rint(rev));
-                const float cc = __builtin_amdgcn_cosf(fr), ss = __builtin_amdgcn_sinf(fr);
-                const float x0 = qv[i][2 * e], x1 = qv[i][2 * e + 1];
-                qv[i][2 * e] = x0 * cc - x1 * ss;
-                qv[i][2 * e + 1] = x0 * ss + x1 * cc;
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qv[i][e] = 0.0f;
         }
+
+    // rotate: pair i of the lane's slice h has frequency index 32h + 16g + i; the
+    // angle (position times theta_i / 2pi, revolutions) is formed in fp64 and
+    // reduced to [-1/2, 1/2] before the hardware sine and cosine.  theta for
+    // the g = 1 half is theta_{32h+i} * base^(-32/D) (exact to an ulp of fp64).
+    {
+        const double pos = (double)(a.q_pos0 + qi);
+        const double gmul = g ? a.rev_step : 1.0;
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const double rv = a.rev.t[32 * h + i] * gmul;
+                const double r = pos * rv;
+                const float fr = (float)(r - __builtin_rint(r));
+                const float cc = __builtin_amdgcn_cosf(fr), ss = __builtin_amdgcn_sinf(fr);
+                const float x0 = qv[32 * h + 2 * i], x1 = qv[32 * h + 2 * i + 1];
+                qv[32 * h + 2 * i] = x0 * cc - x1 * ss;
+                qv[32 * h + 2 * i + 1] = x0 * ss + x1 * cc;
+            }
     }
     float am = 0.0f;
 #pragma unroll
-    for (int i = 0; i < QIT; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(qv[i][e]));
+    for (int e = 0; e < QV; ++e) am = fmaxf(am, fabsf(qv[e]));
     am = wave_max(am);
-
     if (lane == 0) red[wave] = am;
-    __syncthreads();
+    lds_barrier();
     float qmax = 0.0f;
 #pragma unroll
     for (int w = 0; w < kNW; ++w) qmax = fmaxf(qmax, red[w]);
     const float qscale = qmax > 0.0f ? 448.0f / qmax : 1.0f;
     const float qfac = (qmax > 0.0f ? qmax / 448.0f : 1.0f) * a.softmax_scale * kLog2e;
 
-    // ---- Q -> hi/lo E4M3 B operands, kept in this wave's LDS area ------------
-    // Layout [slice h][hi/lo][16-byte part][lane' = 32g + row] x 16 bytes: lane'
-    // of the MFMA B operand holds d in [64h + 32g, +32) of query row (lane' % 32).
-    uint8_t *qbase = smem + L::Q_OFF + wave * L::Q_WAVE;
+    // Q hi/lo E4M3 operands: byte k of qop[h][hl] is element k of the lane's slice h
+    v8i qop[NH][2];
 #pragma unroll
-    for (int i = 0; i < QIT; ++i) {
-        const int r = (i * 64 + lane) / QCH, c = (i * 64 + lane) % QCH;
-        const int h = c / 8, gg = (c / 4) % 2, part = (c / 2) % 2;
-        uint32_t hi0, lo0, hi1, lo1;
-        split4(qv[i][0] * qscale, qv[i][1] * qscale, qv[i][2] * qscale, qv[i][3] * qscale, hi0, lo0);
-        split4(qv[i][4] * qscale, qv[i][5] * qscale, qv[i][6] * qscale, qv[i][7] * qscale, hi1, lo1);
-        const int pos = (32 * gg + r) * 16 + 8 * (c % 2);
-        *reinterpret_cast<v2i *>(qbase + (4 * h + part) * 1024 + pos) = v2i{(int)hi0, (int)hi1};
-        *reinterpret_cast<v2i *>(qbase + (4 * h + 2 + part) * 1024 + pos) = v2i{(int)lo0, (int)lo1};
-    }
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int w4 = 0; w4 < 8; ++w4) {
+            uint32_t hi, lo;
+            const float *x = qv + 32 * h + 4 * w4;
+            split4(x[0] * qscale, x[1] * qscale, x[2] * qscale, x[3] * qscale, hi, lo);
+            qop[h][0][w4] = (int)hi;
+            qop[h][1][w4] = (int)lo;
+        }
 
     // Lane-constant LDS offsets.  K A-operand: A-row i (= col) of block kb is
     // key 32kb + kk with kk = 16((i>>2)&1) + 4(i>>3) + (i&3); this lane reads
@@ -347,12 +431,17 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     }
     static_assert(NBLK % (4 * kNW) == 0, "whole dequantisation rounds");
     auto convert_v = [&](const uint8_t *buf, uint8_t *vt) {
-        const float *fv = reinterpret_cast<const float *>(buf + L::F_OFF) + kKT;
+        const float *fv = reinterpret_cast<const float *>(buf + L::F_OFF);
+        v2i ut[NCV];
+#pragma unroll
+        for (int i = 0; i < NCV; ++i) ut[i] = lds_read_tr8(buf + cv_src[i]);
+#pragma unroll
+        for (int i = 0; i < NCV; ++i) lds_wait(ut[i]);
 #pragma unroll
         for (int i = 0; i < NCV; ++i) {
-            const v2i u = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDS_AS v2i *)(buf + cv_src[i]));
-            const f32x4 s0 = *reinterpret_cast<const f32x4 *>(fv + 8 * cv_kg[i]);
-            const f32x4 s1 = *reinterpret_cast<const f32x4 *>(fv + 8 * cv_kg[i] + 4);
+            const v2i u = ut[i];
+            const f32x4 s0 = *reinterpret_cast<const f32x4 *>(fv + fv_index(8 * cv_kg[i]));
+            const f32x4 s1 = *reinterpret_cast<const f32x4 *>(fv + fv_index(8 * cv_kg[i] + 4));
             const auto x0 = __builtin_amdgcn_cvt_pk_f32_fp8(u[0], false);
             const auto x1 = __builtin_amdgcn_cvt_pk_f32_fp8(u[0], true);
             const auto x2 = __builtin_amdgcn_cvt_pk_f32_fp8(u[1], false);
@@ -362,54 +451,59 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
             *reinterpret_cast<u32x4 *>(vt + cv_dst[i]) = w;
         }
     };
-    uint8_t *vt_base = smem + L::VT_OFF;
 
     // ---- main loop: two wave groups in ping-pong --------------------------------
     // Per tile t a wave runs two half-steps:
     //   V(t): scores, running max, weights p = 2^x and their sum -> bf16 B operands
     //   M(t): O^T += V^T(t) . P^T(t); S^T(t+1) = K(t+1) . Q^T; dequantise V(t+1)
     // in the order M(t0-1) V(t0) M(t0) V(t0+1) ... M(t1-1), where M(t0-1) only
-    // holds the tile-t0 parts.  The group of waves 0..3 runs one half-step
-    // ahead of waves 4..7, and half-steps are separated by workgroup barriers,
-    // so at any time the two waves sharing a SIMD are in different half-steps:
-    // one keeps the matrix core busy while the other uses the VALU.
-    // Buffers: FP8 tile t+2 is loaded in the odd interval 2(t-t0)+1 and is
-    // waited for at the end of the next one; FP8 tiles are triple buffered
-    // (the lead group reads a tile's K and V in M(t-1), the trailing group
-    // reads its K factors in V(t), two intervals later); V^T is double
+    // holds the tile-t0 parts.  Half-steps are separated by workgroup barriers,
+    // and waves 4..7 run one half-step behind waves 0..3, so the two waves
+    // sharing a SIMD are in different half-steps: one keeps the matrix core
+    // busy while the other uses the VALU.
+    // Buffers: tile t0+k sits in tile buffer k mod kNBuf.  The lead group
+    // issues tile u+P (relative to t0) in interval 2u+1 and lands tile u+1
+    // (waits for it, finishes its factors) at the end of interval 2u, just
+    // before its first use; the last reader of a tile is the trailing group's
+    // V half-step, one interval before the buffer is reloaded.  V^T is double
     // buffered (written in M(t-1), read in M(t)).
     v16f o[ND];
 #pragma unroll
     for (int d = 0; d < ND; ++d) o[d] = v16f{};
-    float lsum = 0.0f;      // this lane's share of the softmax denominator
-    float cofs = 0.0f;      // kShift - running max (log2 units)
-    v16f s[2];              // S^T of the tile of the next V half-step
-    v8bf pb[2][2];          // P of the tile of the next M half-step
+    float lsum0 = 0.0f, lsum1 = 0.0f;   // this lane's share of the softmax denominator
+    float cofs = 0.0f;                  // kShift - running max (log2 units)
+    v16f s[2];                          // S^T of the tile of the next V half-step
+    v8bf pb[2][2];                      // P of the tile of the next M half-step
 
-    auto half_v = [&](int t) {
-        const int r0 = t - t0;
-        const float *fa = reinterpret_cast<const float *>(smem + (r0 % 3) * L::BUF + L::F_OFF);
+    auto half_v = [&](int t, const uint8_t *buf, const uint8_t *buf1, uint8_t *vt_next) {
+        const float *fa = reinterpret_cast<const float *>(buf + L::F_OFF);
         // scores (log2 units, shifted by cofs); register r of block kb is key
         // 32kb + 16g + r of the tile
         float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 f = *reinterpret_cast<const f32x4 *>(fa + fk_index(32 * kb + 16 * g + 4 * q));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float v = s[kb][4 * q + r] * f[r] + cofs;
+                    s[kb][4 * q + r] = v;
+                    mx = fmaxf(mx, v);
+                }
+            }
         const int lim = a.n_valid - t * kKT;              // valid keys of this tile
-        auto scores = [&](bool masked) {
+        if (lim < kKT) {                                  // last tile of the window
+            mx = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x4 f = *reinterpret_cast<const f32x4 *>(fa + 32 * kb + 16 * g + 4 * q);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        float v = s[kb][4 * q + r] * f[r] + cofs;
-                        if (masked) v = (32 * kb + 16 * g + 4 * q + r < lim) ? v : -INFINITY;
-                        s[kb][4 * q + r] = v;
-                        mx = fmaxf(mx, v);
-                    }
+                for (int r = 0; r < 16; ++r) {
+                    const float v = 32 * kb + 16 * g + r < lim ? s[kb][r] : -INFINITY;
+                    s[kb][r] = v;
+                    mx = fmaxf(mx, v);
                 }
-        };
-        if (lim >= kKT) scores(false);
-        else scores(true);
+        }
         {
             // max with the other half of the wave (lanes l and l ^ 32 hold the
             // same query): swap the halves across two copies
@@ -425,7 +519,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
             } else if (over) {
                 shift = mx - kShift;
                 const float alpha = __builtin_amdgcn_exp2f(-shift);
-                lsum *= alpha;
+                lsum0 *= alpha;
+                lsum1 *= alpha;
 #pragma unroll
                 for (int d = 0; d < ND; ++d) o[d] *= alpha;
             }
@@ -445,38 +540,21 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
                 for (int e = 0; e < 4; ++e) {
                     w[e] = pack_bf16(__builtin_amdgcn_exp2f(s[kb][8 * ks + 2 * e]),
                                      __builtin_amdgcn_exp2f(s[kb][8 * ks + 2 * e + 1]));
-                    lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, (uint32_t)w[e]), one2,
-                                                           lsum, false);
+                    float &acc = (e & 1) ? lsum1 : lsum0;
+                    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, (uint32_t)w[e]), one2, acc,
+                                                          false);
                 }
                 // keep the weights computed in this half-step (not sunk
                 // into the matrix half-step that consumes them)
                 asm volatile("" : "+v"(w));
                 pb[kb][ks] = __builtin_bit_cast(v8bf, w);
             }
+        if (t + 1 < t1) convert_v(buf1, vt_next);      // V^T of tile t+1
     };
 
-    // Q operands of QK^T stay in VGPRs for the whole loop: lane (query, g)
-    // holds d in [64h + 32g, +32) of its query, hi and lo terms.
-    v8i qop[NH][2];
-#pragma unroll
-    for (int h = 0; h < NH; ++h)
-#pragma unroll
-        for (int hl = 0; hl < 2; ++hl) {
-            const u32x4 u0 = *reinterpret_cast<const u32x4 *>(qbase + ((4 * h + 2 * hl) * 64 + lane) * 16);
-            const u32x4 u1 = *reinterpret_cast<const u32x4 *>(qbase + ((4 * h + 2 * hl + 1) * 64 + lane) * 16);
-            qop[h][hl] = v8i{(int)u0[0], (int)u0[1], (int)u0[2], (int)u0[3],
-                             (int)u1[0], (int)u1[1], (int)u1[2], (int)u1[3]};
-        }
-
     // M half-step.  PV and PREP select the parts (both in the steady state).
-    // Operands are read one MFMA group ahead: the PV products go in four
-    // groups (kb, ks) of ND MFMAs, then QK^T of tile t+1 in NH groups of four.
-    auto half_m = [&](int t, auto PV, auto PREP_) {
+    auto half_m = [&](int t, const uint8_t *buf1, const uint8_t *vt, auto PV, auto PREP_) {
         const bool PREP_on = decltype(PREP_)::value && t + 1 < t1;
-        using PREP = decltype(PREP_);
-        const int r0 = t - t0;
-        const uint8_t *vt = vt_base + (r0 % 2) * L::VT_BYTES;
-        const uint8_t *buf1 = smem + ((r0 + 1) % 3) * L::BUF;
         auto read_v = [&](int grp, u32x4 (&va)[ND]) {
             const int kb = grp / 2, ks = grp % 2;
 #pragma unroll
@@ -525,70 +603,79 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
                 for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb) s[kb] = mfma(ka[h][kb], qop[h][hl], s[kb]);
-            convert_v(buf1, vt_base + ((r0 + 1) % 2) * L::VT_BYTES);
-            // slice-0 operands first, slice-1 reads behind the slice-0 MFMAs,
-            // the dequantisation (LDS reads, VALU, LDS writes) behind the rest
+            // slice-0 operands first, slice-1 reads behind the slice-0 MFMAs
             __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-#pragma unroll
-            for (int i = 0; i < 4 * NH - 4; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4 * NH - 4, 0);
         }
     };
     using yes = std::true_type;
     using no = std::false_type;
 
-    {
-        const float f0 = wave < 2 ? load_factor(a, my_scales, head, t0) : 0.0f;
-        const float f1 = wave < 2 && t0 + 1 < t1 ? load_factor(a, my_scales, head, t0 + 1) : 0.0f;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        store_factor<D>(smem, f0, qfac);
-        if (t0 + 1 < t1) store_factor<D>(smem + L::BUF, f1, qfac);
-    }
-    __syncthreads();
+    // Every wave lands its own part of a tile (waits for it, finishes its
+    // factors) two tiles ahead, at the end of its V(u): tile u+2, whose V rows
+    // the next V half-step dequantises.  The newest tile a wave has issued
+    // before V(u) ends is max(P-1, min(u+P-1, n-1)).
+    auto land = [&](int u, int m) {                    // tile t0+m
+        if (m < n) {
+            wait_tiles<D>(max(P - 1, min(u + P - 1, n - 1)) - m);
+            finish_factors<D>(a, tiles + (m % kNBuf) * L::BUF, t0 + m, wave, qfac);
+        }
+    };
+    land(-1, 0);
+    land(-1, 1);
+    lds_barrier();
+    half_m(t0 - 1, tiles, vt_base, no{}, yes{});       // S^T of tile t0
+    convert_v(tiles, vt_base);                         // V^T of tile t0
+    lds_barrier();
 
     // Both groups run the same loop; the trailing group enters it one
     // interval late (an extra barrier first), the lead group leaves it with an
-    // extra barrier, so both pass the same 2n+1 barriers.  The lead group
-    // streams the tiles: tile t0+u+2 is issued in interval 2u+1 and landed
-    // (waited for, factors stored) at the end of interval 2u+2.
-    float nf = 0.0f;
-    const int n = t1 - t0;
-    half_m(t0 - 1, no{}, yes{});
-    if (!lead) __syncthreads();
+    // extra barrier, so both pass the same 2n+1 barriers.
+    //   V(u): scores and weights of tile u, V^T of tile u+1 (buffer (u+1)%3)
+    //   M(u): O^T += V^T(u) . P^T(u), S^T of tile u+1
+    // V^T(u+1) is written in intervals 2u, 2u+1 and read in 2u+3, 2u+4; its
+    // buffer last held V^T(u-2), read in 2u-3, 2u-2.
+    if (!lead) lds_barrier();
+    int bcur = 0;                                      // tile buffer of tile t0+u
+    int vcur = 0;                                      // V^T buffer of tile t0+u
     for (int u = 0; u < n; ++u) {
-        half_v(t0 + u);
-        if (lead && u >= 1 && t0 + u + 1 < t1) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            store_factor<D>(smem + ((u + 1) % 3) * L::BUF, nf, qfac);
+        const int bnext = bcur + 1 == kNBuf ? 0 : bcur + 1;
+        const int vnext = vcur + 1 == 3 ? 0 : vcur + 1;
+        uint8_t *buf = tiles + bcur * L::BUF;
+        uint8_t *buf1 = tiles + bnext * L::BUF;
+        half_v(t0 + u, buf, buf1, vt_base + vnext * L::VT_BYTES);
+        land(u, u + 2);
+        lds_barrier();
+        if (u + P < n) {                               // stream tile t0+u+P
+            int bl = bcur + P;
+            bl = bl >= kNBuf ? bl - kNBuf : bl;
+            issue_tile<D>(a, kh, vh, scales_h, t0 + u + P, tiles + bl * L::BUF, wave);
         }
-        __syncthreads();
-        if (lead && t0 + u + 2 < t1) {
-            issue_tile<D>(a, head, t0 + u + 2, smem + ((u + 2) % 3) * L::BUF, wave);
-            if (wave < 2) nf = load_factor(a, my_scales, head, t0 + u + 2);
-        }
-        half_m(t0 + u, yes{}, yes{});
-        __syncthreads();
+        __builtin_amdgcn_s_setprio(1);                 // the MFMA half-step issues first
+        half_m(t0 + u, buf1, vt_base + vcur * L::VT_BYTES, yes{}, yes{});
+        __builtin_amdgcn_s_setprio(0);
+        lds_barrier();
+        bcur = bnext;
+        vcur = vnext;
     }
-    if (lead) __syncthreads();
+    if (lead) lds_barrier();
 
     // ---- epilogue ------------------------------------------------------------
-    // Normalised rows o = O / l go through this wave's LDS area (the Q
-    // operands are no longer needed), rows of 2*D bytes whose 8-byte units are
+    // Normalised rows o = O / l go through this wave's LDS area (inside the
+    // tile buffers, all consumed), rows of 2*D bytes whose 8-byte units are
     // XOR-swizzled by an even function of the row, then out to HBM in whole
     // 16-byte chunks:
     // bf16 outputs when there is one split, fp16 partials plus (max, sum) else.
+    const float lsum = lsum0 + lsum1;
     const float ltot = lsum + __shfl_xor(lsum, 32);
     const float f = ltot > 0.0f ? 1.0f / ltot : 0.0f;
     const bool to_out = a.n_splits == 1;
-    uint8_t *ob = qbase;
+    uint8_t *ob = tiles + wave * L::OUT_WAVE;
 #pragma unroll
     for (int d = 0; d < ND; ++d)
 #pragma unroll
@@ -685,18 +772,25 @@ size_t attn_workspace_bytes(int n_heads, int head_dim, int n_q, int n_splits) {
     return o_bytes + rows * 2 * sizeof(float);
 }
 
+template <int D, bool BF16>
+static void launch_attn_d(const AttnArgs &a, int grid, int64_t rows, hipStream_t s) {
+    hipLaunchKernelGGL((attn_kernel<D, BF16>), dim3(grid), dim3(kThreads), Lds<D>::TOTAL, s, a);
+    constexpr int RPB = 256 / (D / 8);               // rows per combine workgroup
+    if (a.n_splits > 1)
+        hipLaunchKernelGGL(combine_kernel<D>, dim3((rows + RPB - 1) / RPB), dim3(256), 0, s, a);
+}
+
 hipError_t launch_attention(const AttnArgs &a, int head_dim, hipStream_t s) {
     const int n_qb = (a.n_q + kQB - 1) / kQB;
     const int grid = n_qb * a.n_heads * a.n_splits;
     const int64_t rows = (int64_t)a.n_q * a.n_heads;
+    const bool bf16 = a.dtype == KVR_BF16;
     if (head_dim == 128) {
-        hipLaunchKernelGGL(attn_kernel<128>, dim3(grid), dim3(kThreads), Lds<128>::TOTAL, s, a);
-        if (a.n_splits > 1)
-            hipLaunchKernelGGL(combine_kernel<128>, dim3((rows + 15) / 16), dim3(256), 0, s, a);
+        if (bf16) launch_attn_d<128, true>(a, grid, rows, s);
+        else launch_attn_d<128, false>(a, grid, rows, s);
     } else {
-        hipLaunchKernelGGL(attn_kernel<64>, dim3(grid), dim3(kThreads), Lds<64>::TOTAL, s, a);
-        if (a.n_splits > 1)
-            hipLaunchKernelGGL(combine_kernel<64>, dim3((rows + 31) / 32), dim3(256), 0, s, a);
+        if (bf16) launch_attn_d<64, true>(a, grid, rows, s);
+        else launch_attn_d<64, false>(a, grid, rows, s);
     }
     return hipGetLastError();
 }

@@ -57,7 +57,8 @@ struct AttnArgs {
     const uint8_t *k_codes, *v_codes; // this layer: [H][W][D]
     const float *k_scales, *v_scales; // this layer: [H][W]
     const void *q;                    // [n_q][H][D]
-    ThetaTable theta;                 // rotary frequencies (fp64)
+    ThetaTable rev;                   // theta_i / (2 pi): rotary frequencies in revolutions (fp64)
+    double rev_step;                  // base^(-32/D) = theta_{i+16} / theta_i
     int64_t q_pos0;                   // rotary position of query 0
     uint16_t *out;                    // [n_q][H][D] bf16
     uint16_t *part_o;                 // [splits][n_q][H][D] fp16, normalised rows

@@ -288,7 +288,9 @@ int32_t attn_fp8_window(const kvr_cache *cache, int32_t layer, int32_t slot_star
     a.k_scales = cache->k_scales + lay;
     a.v_scales = cache->v_scales + lay;
     a.q = q;
-    a.theta = make_theta(D, rope_base);
+    a.rev = make_theta(D, rope_base);
+    for (int i = 0; i < D / 2; ++i) a.rev.t[i] *= 0.15915494309189535;   // 1 / (2 pi)
+    a.rev_step = pow(rope_base, -32.0 / (double)D);
     a.q_pos0 = q_pos_start;
     a.out = out;
     a.n_heads = cache->n_heads;
