@@ -230,7 +230,7 @@ def run_naive(args, K, inputs, shp, rope, chunks, qpool, outs, ws, torch, dev, p
     def upkeep(layer, k, v):
         a = wins[layer]
         s = ping[0]
-        K.naive_upkeep(a[2 * s], a[2 * s + 1], k[layer], v[layer], ring.n_valid, ring.pos_next, rope.base,
+        K.naive_upkeep(a[2 * s], a[2 * s + 1], k[layer], v[layer], ring.n_valid, ring.pos_next, rope,
                        a[2 - 2 * s], a[3 - 2 * s], lin.k_codes[layer], lin.v_codes[layer],
                        lin.k_scales[layer], lin.v_scales[layer])
 

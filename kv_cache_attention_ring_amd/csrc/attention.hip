@@ -727,16 +727,20 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
     const int64_t qh = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
     if (qh >= rows) return;
     const int e = 8 * (threadIdx.x % LPR);
+    const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml);
     float m = -INFINITY;
-    for (int s = 0; s < a.n_splits; ++s) m = fmaxf(m, a.part_ml[2 * (s * rows + qh)]);
+#pragma unroll 8
+    for (int s = 0; s < a.n_splits; ++s) m = fmaxf(m, ml[s * rows + qh].x);
     float l = 0.0f;
     float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    // unrolled so that the loads of several splits are in flight together
+#pragma unroll 8
     for (int s = 0; s < a.n_splits; ++s) {
         const int64_t row = s * rows + qh;
-        const float ls = a.part_ml[2 * row + 1];
-        const float wgt = ls > 0.0f ? ls * __builtin_amdgcn_exp2f(a.part_ml[2 * row] - m) : 0.0f;
-        l += wgt;
+        const float2 mls = ml[row];
         const u32x4 v = *reinterpret_cast<const u32x4 *>(a.part_o + row * D + e);
+        const float wgt = mls.y > 0.0f ? mls.y * __builtin_amdgcn_exp2f(mls.x - m) : 0.0f;
+        l += wgt;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const uint32_t word = v[k];                  // (bit_cast of a vector element
