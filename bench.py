@@ -29,6 +29,25 @@ HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 
 
+def counted_traffic():
+    """HBM bytes per attention call from the committed counter summary, or None
+    when the attention source has changed since the counters were taken."""
+    import hashlib
+    import re
+    prof = os.path.join(ROOT, "profiles", "attn_traffic_counters.md")
+    src = os.path.join(ROOT, "kv_cache_attention_ring_amd", "csrc", "attention.hip")
+    try:
+        text = open(prof).read()
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m = re.search(r"attention\.hip sha256: ([0-9a-f]{64})", text)
+    t = re.search(r"attn_call_traffic_bytes: (\d+)", text)
+    if not m or not t or m.group(1) != digest:
+        return None
+    return int(t.group(1))
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -43,11 +62,32 @@ def parse():
     ap.add_argument("--splits", type=int, default=0, help="attention key splits (0 = default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-naive", action="store_true")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB and exit "
+                         "(reference kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def copy_only(mib):
+    """A plain copy kernel of known size: its FETCH_SIZE / WRITE_SIZE readings
+    calibrate the counters used for the attention kernel's HBM traffic."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.random_(0, 255)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
 
 
 def main():
     args = parse()
+    if args.copy_mb:
+        copy_only(args.copy_mb)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; --gpus must be 1 "
                                    "(the path shards over heads, see the design notes)"}))
@@ -198,7 +238,7 @@ def main():
             "peak": FP8_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": counted_traffic(),
         },
         "breakdown": {
             "write_60_layers_us": round(write_ms * 1e3, 2),
