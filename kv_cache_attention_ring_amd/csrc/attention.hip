@@ -664,6 +664,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
         vcur = vnext;
     }
     if (lead) lds_barrier();
+    // a split shorter than P tiles may still be reloading its last tile into
+    // spare buffers: let every load land before the buffers stage the output
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
 
     // ---- epilogue ------------------------------------------------------------
     // Normalised rows o = O / l go through this wave's LDS area (inside the

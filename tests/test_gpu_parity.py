@@ -11,7 +11,8 @@ element with the bars in tests/_parity.py.  Cases:
     single split, determinism, the naive path, the rebase;
   * the 60-layer batched write of a full step (sampled layers);
   * edge cases: ring not yet full, one valid key, one query, ragged query
-    counts, fp32 inputs at D 128, all-zero rows.
+    counts, fp32 inputs at D 128, all-zero rows, scores that grow along the
+    window past the lazy-rescale threshold.
 """
 import numpy as np
 import pytest
@@ -238,6 +239,32 @@ def test_edge_cases_small():
     out0 = K.attn_fp8_window(run.cache, 0, 0, 16, torch.zeros_like(qd), 0, run.rope.base)
     torch.cuda.synchronize()
     assert_attention(_f32(out0), oracle.attention(run.orc, 0, 16, np.zeros_like(q), 0), "q=0")
+
+
+def test_lazy_rescale_when_scores_grow():
+    """Scores of the first 128 keys sit ~18 log2 units below the later ones,
+    so the running max of every query moves by more than the lazy-rescale
+    threshold inside a split (the accumulators are rescaled mid-window)."""
+    shp = inputs.Shape("test", 1, 2, 128, 512, 128)
+    run = SmallRun(shp, dtype=torch.float32)
+    H, D, N = shp.n_heads, shp.head_dim, shp.n_new
+    rng = np.random.default_rng(2024)
+    t = rng.standard_normal((H, D)).astype(np.float32)
+    t *= 12.0 / np.linalg.norm(t, axis=1, keepdims=True)          # |t| = 12 per head
+    for c in range(4):
+        pos = run.ring.pos_next + np.arange(N)
+        k_rot = (-t[None] if c == 0 else 0.0 * t[None]) + rng.standard_normal((N, H, D)).astype(np.float32) * (
+            0.3 if c == 0 else 1.0)
+        k = oracle.rope_rows(k_rot, -pos[:, None])                # stored rotated: k_rot
+        v = rng.standard_normal((N, H, D)).astype(np.float32)
+        run.step(np.ascontiguousarray(k), v)
+    q_pos = run.ring.pos_next - N + np.arange(N)
+    q = oracle.rope_rows(t[None] + 0.3 * rng.standard_normal((N, H, D)).astype(np.float32), -q_pos[:, None])
+    q = np.ascontiguousarray(q)
+    for n_splits in (1, 2):
+        _say(f"rescale n_splits={n_splits}")
+        got, ref = run.attention(q, n_splits=n_splits, naive_too=False)
+        assert_attention(got, ref, f"growing scores, {n_splits} splits")
 
 
 def test_fp32_inputs_head_dim_128():
