@@ -80,7 +80,15 @@ def copy_only(mib):
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 13, "copy_ms": round(ms, 4),
+                      "copy_GBps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def main():

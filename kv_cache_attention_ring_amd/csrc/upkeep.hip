@@ -10,7 +10,8 @@
 //
 // Every row of head_dim elements is handled by 8 consecutive lanes, each lane
 // owning head_dim/8 contiguous elements (16-byte loads and stores); the row
-// absmax is a 3-step butterfly across those 8 lanes.  The arithmetic order
+// absmax is a 3-step butterfly across those 8 lanes.  Decoding a stored row
+// is the exact E4M3 value times the fp32 row scale (one fp32 product).  The arithmetic order
 // of one element is fixed (rotation: x0*c - x1*s, x0*s + x1*c, each product
 // and sum rounded to fp32; quantisation: y * (448 / absmax) rounded to fp32,
 // then E4M3 round-to-nearest-even via v_cvt_pk_fp8_f32), and this file is
@@ -30,7 +31,6 @@ namespace {
 constexpr int kRowLanes = 8;          // lanes per row
 constexpr int kBlock = 256;           // threads per workgroup
 constexpr int kRowsPerIter = kBlock / kRowLanes;
-constexpr int kTokBlock = 16;         // new tokens per write workgroup
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
@@ -125,28 +125,6 @@ __device__ __forceinline__ void quantize_store(const float (&y)[EPT], uint8_t *c
     if (lane0) *scale_dst = scale;
 }
 
-// Dequantise EPT codes with the row scale (fp32 product, exact decode).
-template <int EPT>
-__device__ __forceinline__ void dequant_chunk(const uint8_t *src, float scale, float (&x)[EPT]) {
-    uint32_t w[EPT / 4];
-    if constexpr (EPT == 16) {
-        uint4 u = *reinterpret_cast<const uint4 *>(src);
-        w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
-    } else {
-        uint2 u = *reinterpret_cast<const uint2 *>(src);
-        w[0] = u.x; w[1] = u.y;
-    }
-#pragma unroll
-    for (int k = 0; k < EPT / 4; ++k) {
-        auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
-        auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
-        x[4 * k] = lo[0] * scale;
-        x[4 * k + 1] = lo[1] * scale;
-        x[4 * k + 2] = hi[0] * scale;
-        x[4 * k + 3] = hi[1] * scale;
-    }
-}
-
 // ---------------------------------------------------------------------------
 // Rotary table: cs[p][i] = (cos, sin)(p * theta_i), fp64 angle and trig.
 // ---------------------------------------------------------------------------
@@ -163,50 +141,62 @@ __global__ void __launch_bounds__(kBlock) rope_table_kernel(float2 *cs, int64_t 
     cs[idx] = make_float2((float)c, (float)s);
 }
 
+// The three row kernels below take a 2-D grid: blockIdx.y picks a (layer,
+// head) or (kv, head) row sequence, blockIdx.x a run of kUnroll * 32 rows of
+// it.  Each 8-lane row group handles kUnroll rows 32 apart and issues all of
+// their loads before any arithmetic, so a wave keeps kUnroll rows of data in
+// flight (the kernels are bound by HBM bandwidth, which needs many bytes in
+// flight per CU).
+constexpr int kUnroll = 4;
+constexpr int kRunRows = kUnroll * kRowsPerIter;
+
 // ---------------------------------------------------------------------------
-// Write-time RoPE + FP8 [AI-cache].  grid = (ceil(n_new / 16), n_layers).
-// Rows of a workgroup: (kv, head, token) with the token fastest, so lanes of a
-// wave touch consecutive slots (contiguous scale stores).
+// Write-time RoPE + FP8 [AI-cache].  grid = (ceil(n_new / kRunRows),
+// n_layers * 2 * n_heads); y = (layer, kv, head), rows = new tokens, so the
+// lanes of a wave touch consecutive slots (contiguous scale stores).
 // ---------------------------------------------------------------------------
 template <int D, bool BF16>
 __global__ void __launch_bounds__(kBlock) write_kernel(WriteArgs a) {
     constexpr int EPT = D / kRowLanes;
-    __shared__ float s_cs[kTokBlock * D];          // (cos, sin) per token and pair
-
-    const int j0 = blockIdx.x * kTokBlock;
-    const int layer = a.layer0 + blockIdx.y;
-    const int ntok = min(kTokBlock, a.n_new - j0);
-    for (int t = threadIdx.x; t < ntok * D; t += kBlock) s_cs[t] = a.cs[(int64_t)j0 * D + t];
-    __syncthreads();
-
     const int lane8 = threadIdx.x % kRowLanes;
-    const int rows = 2 * a.n_heads * kTokBlock;
-    const int64_t lay_in = (int64_t)blockIdx.y * a.layer_stride;
-    const int64_t lay_cache = (int64_t)layer * a.n_heads * a.window;
-    for (int r = threadIdx.x / kRowLanes; r < rows; r += kRowsPerIter) {
-        const int tok = r % kTokBlock;
-        const int h = (r / kTokBlock) % a.n_heads;
-        const int kv = r / (kTokBlock * a.n_heads);
-        if (tok >= ntok) continue;
-        const int j = j0 + tok;
-        const void *src = kv ? a.v_new : a.k_new;
-        RawChunk<EPT, BF16> raw;
-        raw.load(src, lay_in + ((int64_t)j * a.n_heads + h) * D + lane8 * EPT);
+    const int h = blockIdx.y % a.n_heads;
+    const int kv = (blockIdx.y / a.n_heads) % 2;
+    const int lrel = blockIdx.y / (2 * a.n_heads);
+    const int j0 = blockIdx.x * kRunRows + threadIdx.x / kRowLanes;
+    const void *src = kv ? a.v_new : a.k_new;
+    const int64_t lay_in = (int64_t)lrel * a.layer_stride;
+    RawChunk<EPT, BF16> raw[kUnroll];
+    float4 csv[kUnroll][EPT / 4];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const int j = min(j0 + u * kRowsPerIter, a.n_new - 1);
+        raw[u].load(src, lay_in + ((int64_t)j * a.n_heads + h) * D + lane8 * EPT);
+        if (kv == 0) {
+            const float4 *t = reinterpret_cast<const float4 *>(a.cs + (int64_t)j * D + lane8 * EPT);
+#pragma unroll
+            for (int v = 0; v < EPT / 4; ++v) csv[u][v] = t[v];
+        }
+    }
+    const int64_t lay_cache = (int64_t)(a.layer0 + lrel) * a.n_heads * a.window;
+    uint8_t *codes = kv ? a.v_codes : a.k_codes;
+    float *scales = kv ? a.v_scales : a.k_scales;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const int j = j0 + u * kRowsPerIter;
+        if (j >= a.n_new) break;
         float x[EPT];
-        raw.to_f32(x);
-        if (kv == 0) rotate_pairs<EPT>(x, &s_cs[tok * D + lane8 * EPT]);
+        raw[u].to_f32(x);
+        if (kv == 0) rotate_pairs<EPT>(x, reinterpret_cast<const float *>(csv[u]));
         int slot = a.head + j;
         if (slot >= a.window) slot -= a.window;
         const int64_t row = lay_cache + (int64_t)h * a.window + slot;
-        uint8_t *codes = kv ? a.v_codes : a.k_codes;
-        float *scales = kv ? a.v_scales : a.k_scales;
         quantize_store<EPT>(x, codes + row * D + lane8 * EPT, scales + row, lane8 == 0);
     }
 }
 
 // ---------------------------------------------------------------------------
 // Delta rebase [AI-cache]: every valid K row dequantised, rotated by -delta,
-// re-quantised.  Grid-stride over rows in memory order.
+// re-quantised.  grid = (ceil(n_valid / kRunRows), n_layers * n_heads).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(kBlock) rebase_kernel(RebaseArgs a, CosSinTable rot) {
@@ -215,76 +205,86 @@ __global__ void __launch_bounds__(kBlock) rebase_kernel(RebaseArgs a, CosSinTabl
     float cs[EPT];
 #pragma unroll
     for (int e = 0; e < EPT; ++e) cs[e] = rot.cs[lane8 * EPT + e];
-
-    const int64_t per_lh = a.n_valid;
-    const int64_t total = (int64_t)a.n_layers * a.n_heads * per_lh;
-    const int64_t stride = (int64_t)gridDim.x * kRowsPerIter;
-    for (int64_t r = (int64_t)blockIdx.x * kRowsPerIter + threadIdx.x / kRowLanes; r < total;
-         r += stride) {
-        const int64_t lh = r / per_lh;
-        const int i = (int)(r - lh * per_lh);
+    const int64_t lh = (int64_t)a.layer0 * a.n_heads + blockIdx.y;
+    const int i0 = blockIdx.x * kRunRows + threadIdx.x / kRowLanes;
+    int64_t rows[kUnroll];
+    uint32_t w[kUnroll][EPT / 4];
+    float sc[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const int i = min(i0 + u * kRowsPerIter, a.n_valid - 1);
         int slot = a.start + i;
         if (slot >= a.window) slot -= a.window;
-        const int64_t row = ((int64_t)a.layer0 * a.n_heads + lh) * a.window + slot;
+        rows[u] = lh * a.window + slot;
+        const uint8_t *src = a.k_codes + rows[u] * D + lane8 * EPT;
+        if constexpr (EPT == 16) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(src);
+            w[u][0] = v.x; w[u][1] = v.y; w[u][2] = v.z; w[u][3] = v.w;
+        } else {
+            const uint2 v = *reinterpret_cast<const uint2 *>(src);
+            w[u][0] = v.x; w[u][1] = v.y;
+        }
+        sc[u] = a.k_scales[rows[u]];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        if (i0 + u * kRowsPerIter >= a.n_valid) break;
         float x[EPT];
-        dequant_chunk<EPT>(a.k_codes + row * D + lane8 * EPT, a.k_scales[row], x);
+#pragma unroll
+        for (int k = 0; k < EPT / 4; ++k) {
+            auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[u][k], false);
+            auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[u][k], true);
+            x[4 * k] = lo[0] * sc[u];
+            x[4 * k + 1] = lo[1] * sc[u];
+            x[4 * k + 2] = hi[0] * sc[u];
+            x[4 * k + 3] = hi[1] * sc[u];
+        }
         rotate_pairs<EPT>(x, cs);
-        quantize_store<EPT>(x, a.k_codes + row * D + lane8 * EPT, a.k_scales + row, lane8 == 0);
+        quantize_store<EPT>(x, a.k_codes + rows[u] * D + lane8 * EPT, a.k_scales + rows[u], lane8 == 0);
     }
 }
 
 // ---------------------------------------------------------------------------
 // Naive per-call upkeep [WC]: rebuild the shifted linear window and
-// re-rotate / re-quantise all of it.  Rows (kv, head, i), i fastest.
+// re-rotate / re-quantise all of it.  grid = (ceil(n_after / kRunRows),
+// 2 * n_heads); y = (kv, head), rows = window positions.
 // ---------------------------------------------------------------------------
 template <int D, bool BF16>
 __global__ void __launch_bounds__(kBlock) naive_kernel(NaiveArgs a) {
     constexpr int EPT = D / kRowLanes;
     const int lane8 = threadIdx.x % kRowLanes;
-    const int64_t per_h = a.n_after;
-    const int64_t total = 2 * (int64_t)a.n_heads * per_h;
-    const int64_t stride = (int64_t)gridDim.x * kRowsPerIter;
-    for (int64_t r = (int64_t)blockIdx.x * kRowsPerIter + threadIdx.x / kRowLanes; r < total;
-         r += stride) {
-        const int64_t kvh = r / per_h;  // (kv, head) pair
-        const int i = (int)(r - kvh * per_h);
-        const int kv = (int)(kvh / a.n_heads);
-        const int h = (int)(kvh - (int64_t)kv * a.n_heads);
-        const void *src;
-        int64_t src_off;
-        if (i < a.kept) {
-            src = kv ? a.v_src : a.k_src;
-            src_off = ((int64_t)h * a.window + i + a.drop) * D + lane8 * EPT;
-        } else {
-            src = kv ? a.v_new : a.k_new;
-            src_off = ((int64_t)(i - a.kept) * a.n_heads + h) * D + lane8 * EPT;
-        }
-        const int64_t row = (int64_t)h * a.window + i;
-        RawChunk<EPT, BF16> raw;
-        raw.load(src, src_off);
-        raw.store(kv ? a.v_dst : a.k_dst, row * D + lane8 * EPT);
-        float x[EPT];
-        raw.to_f32(x);
+    const int h = blockIdx.y % a.n_heads;
+    const int kv = blockIdx.y / a.n_heads;
+    const int i0 = blockIdx.x * kRunRows + threadIdx.x / kRowLanes;
+    RawChunk<EPT, BF16> raw[kUnroll];
+    float4 csv[kUnroll][EPT / 4];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const int i = min(i0 + u * kRowsPerIter, a.n_after - 1);
+        if (i < a.kept)
+            raw[u].load(kv ? a.v_src : a.k_src, ((int64_t)h * a.window + i + a.drop) * D + lane8 * EPT);
+        else
+            raw[u].load(kv ? a.v_new : a.k_new, ((int64_t)(i - a.kept) * a.n_heads + h) * D + lane8 * EPT);
         if (kv == 0) {
-            float cs[EPT];
             const float4 *t = reinterpret_cast<const float4 *>(a.cs + (int64_t)i * D + lane8 * EPT);
 #pragma unroll
-            for (int v = 0; v < EPT / 4; ++v) {
-                float4 f = t[v];
-                cs[4 * v] = f.x; cs[4 * v + 1] = f.y; cs[4 * v + 2] = f.z; cs[4 * v + 3] = f.w;
-            }
-            rotate_pairs<EPT>(x, cs);
+            for (int v = 0; v < EPT / 4; ++v) csv[u][v] = t[v];
         }
-        uint8_t *codes = kv ? a.v_codes : a.k_codes;
-        float *scales = kv ? a.v_scales : a.k_scales;
+    }
+    uint8_t *codes = kv ? a.v_codes : a.k_codes;
+    float *scales = kv ? a.v_scales : a.k_scales;
+    void *dst = kv ? a.v_dst : a.k_dst;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+        const int i = i0 + u * kRowsPerIter;
+        if (i >= a.n_after) break;
+        const int64_t row = (int64_t)h * a.window + i;
+        raw[u].store(dst, row * D + lane8 * EPT);
+        float x[EPT];
+        raw[u].to_f32(x);
+        if (kv == 0) rotate_pairs<EPT>(x, reinterpret_cast<const float *>(csv[u]));
         quantize_store<EPT>(x, codes + row * D + lane8 * EPT, scales + row, lane8 == 0);
     }
-}
-
-int grid_for_rows(int64_t rows) {
-    int64_t g = (rows + kRowsPerIter - 1) / kRowsPerIter;
-    const int64_t cap = 256 * 16;      // 16 workgroups per CU on 256 CUs
-    return (int)(g < cap ? (g > 0 ? g : 1) : cap);
 }
 
 }  // namespace
@@ -300,7 +300,7 @@ hipError_t launch_rope_table(float *cs, int64_t pos0, int32_t n_pos, int32_t hea
 }
 
 hipError_t launch_write(const WriteArgs &a, int head_dim, hipStream_t s) {
-    dim3 grid((a.n_new + kTokBlock - 1) / kTokBlock, a.n_layers);
+    dim3 grid((a.n_new + kRunRows - 1) / kRunRows, a.n_layers * 2 * a.n_heads);
     const bool bf = a.dtype == KVR_BF16;
     if (head_dim == 128 && bf)
         hipLaunchKernelGGL((write_kernel<128, true>), grid, dim3(kBlock), 0, s, a);
@@ -315,25 +315,25 @@ hipError_t launch_write(const WriteArgs &a, int head_dim, hipStream_t s) {
 
 hipError_t launch_rebase(const RebaseArgs &a, const CosSinTable &rot, int head_dim,
                          hipStream_t s) {
-    const int grid = grid_for_rows((int64_t)a.n_layers * a.n_heads * a.n_valid);
+    dim3 grid((a.n_valid + kRunRows - 1) / kRunRows, a.n_layers * a.n_heads);
     if (head_dim == 128)
-        hipLaunchKernelGGL(rebase_kernel<128>, dim3(grid), dim3(kBlock), 0, s, a, rot);
+        hipLaunchKernelGGL(rebase_kernel<128>, grid, dim3(kBlock), 0, s, a, rot);
     else
-        hipLaunchKernelGGL(rebase_kernel<64>, dim3(grid), dim3(kBlock), 0, s, a, rot);
+        hipLaunchKernelGGL(rebase_kernel<64>, grid, dim3(kBlock), 0, s, a, rot);
     return hipGetLastError();
 }
 
 hipError_t launch_naive(const NaiveArgs &a, int head_dim, hipStream_t s) {
-    const int grid = grid_for_rows(2 * (int64_t)a.n_heads * a.n_after);
+    dim3 grid((a.n_after + kRunRows - 1) / kRunRows, 2 * a.n_heads);
     const bool bf = a.dtype == KVR_BF16;
     if (head_dim == 128 && bf)
-        hipLaunchKernelGGL((naive_kernel<128, true>), dim3(grid), dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL((naive_kernel<128, true>), grid, dim3(kBlock), 0, s, a);
     else if (head_dim == 128)
-        hipLaunchKernelGGL((naive_kernel<128, false>), dim3(grid), dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL((naive_kernel<128, false>), grid, dim3(kBlock), 0, s, a);
     else if (bf)
-        hipLaunchKernelGGL((naive_kernel<64, true>), dim3(grid), dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL((naive_kernel<64, true>), grid, dim3(kBlock), 0, s, a);
     else
-        hipLaunchKernelGGL((naive_kernel<64, false>), dim3(grid), dim3(kBlock), 0, s, a);
+        hipLaunchKernelGGL((naive_kernel<64, false>), grid, dim3(kBlock), 0, s, a);
     return hipGetLastError();
 }
 
