@@ -732,25 +732,46 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
     if (qh >= rows) return;
     const int e = 8 * (threadIdx.x % LPR);
     const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml);
-    float m = -INFINITY;
-#pragma unroll 8
-    for (int s = 0; s < a.n_splits; ++s) m = fmaxf(m, ml[s * rows + qh].x);
     float l = 0.0f;
     float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    // unrolled so that the loads of several splits are in flight together
-#pragma unroll 8
-    for (int s = 0; s < a.n_splits; ++s) {
-        const int64_t row = s * rows + qh;
-        const float2 mls = ml[row];
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(a.part_o + row * D + e);
-        const float wgt = mls.y > 0.0f ? mls.y * __builtin_amdgcn_exp2f(mls.x - m) : 0.0f;
-        l += wgt;
+    // up to kCombineBatch splits are loaded in one go (max, sum and the row part
+    // together), then merged in split order; more splits go batch by batch
+    // with the running max carried over
+    constexpr int kCombineBatch = 8;
+    float m = -INFINITY;
+    for (int s0 = 0; s0 < a.n_splits; s0 += kCombineBatch) {
+        const int nb = min(kCombineBatch, a.n_splits - s0);
+        float2 mls[kCombineBatch];
+        u32x4 v[kCombineBatch];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint32_t word = v[k];                  // (bit_cast of a vector element
-            const h2 x = __builtin_bit_cast(h2, word);   //  reference is not reliable)
-            acc[2 * k] += wgt * (float)x[0];
-            acc[2 * k + 1] += wgt * (float)x[1];
+        for (int i = 0; i < kCombineBatch; ++i) {
+            const int64_t row = (int64_t)(s0 + min(i, nb - 1)) * rows + qh;
+            mls[i] = ml[row];
+            v[i] = *reinterpret_cast<const u32x4 *>(a.part_o + row * D + e);
+        }
+        float mb = m;
+#pragma unroll
+        for (int i = 0; i < kCombineBatch; ++i)
+            if (i < nb) mb = fmaxf(mb, mls[i].x);
+        if (mb > m) {                                  // rescale what is merged so far
+            const float r = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mb);
+            l *= r;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] *= r;
+            m = mb;
+        }
+#pragma unroll
+        for (int i = 0; i < kCombineBatch; ++i) {
+            if (i >= nb) break;
+            const float wgt = mls[i].y > 0.0f ? mls[i].y * __builtin_amdgcn_exp2f(mls[i].x - m) : 0.0f;
+            l += wgt;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t word = v[i][k];           // (bit_cast of a vector element
+                const h2 x = __builtin_bit_cast(h2, word);   //  reference is not reliable)
+                acc[2 * k] += wgt * (float)x[0];
+                acc[2 * k + 1] += wgt * (float)x[1];
+            }
         }
     }
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
