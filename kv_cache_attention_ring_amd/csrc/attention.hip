@@ -14,8 +14,9 @@
 // (q_i rotated at position q_pos0 + i: fp64 angle reduced to revolutions, then
 // the hardware sine and cosine; the result goes into E4M3 hi/lo terms, so the
 // rotation only needs fp32 accuracy)
-// with k^_j = e4m3(code) * sk_j and v^_j = e4m3(code) * sv_j (one fp32 scale per
-// cached row).  Keys are visited in logical window order (slot_start + j) mod W.
+// with k^_j = e4m3(code) * sk_j and v^_j = e4m3(code) * sv_j (one power-of-two
+// scale per cached row).  Keys are visited in logical window order
+// (slot_start + j) mod W.
 //
 // Work decomposition.  A workgroup owns one head, a block of 256 queries and a
 // contiguous range of 64-key tiles (a "split"); each of its 8 waves (two per
@@ -40,9 +41,12 @@
 //
 // Precision: E4M3 has 3 mantissa bits, so Q goes in as two E4M3 terms (hi +
 // lo, lo = e4m3(x - hi)), about 8 significant bits and two MFMAs per 64-wide
-// slice.  The per-key K scale and the Q block scale fold into one fp32 factor
-// per key (a_j).  The weights and V^T are bf16 (8 significant bits), so the
-// second product needs no split.  Softmax runs in the log2 domain with a
+// slice.  Row scales are powers of two, so they enter the first product as
+// the matrix core's E8M0 block scales: the K row scale of each A row (its
+// exponent byte is the fp32 scale's bits 23..30) and a per-query Q scale of
+// each B column; the accumulator then holds q_i . k^_j itself.  The weights
+// and V^T are bf16 (8 significant bits; a code times a power of two is exact
+// in bf16), so the second product needs no split.  Softmax runs in the log2 domain with a
 // lazily updated running max (rescale only when a score passes it by more
 // than 16, so weights stay below 2^16 and the fp32 sums cannot overflow).  Splits of one (head, query block) are merged by a second kernel
 // in split order, so a call is deterministic and a linear window gives the
@@ -84,8 +88,8 @@ struct Lds {
     static constexpr int CH = D / 16;            // 16-byte chunks per row
     // dequantised V^T of one tile: [d][64 keys] bf16, 128-byte rows, triple buffered
     static constexpr int VT_BYTES = D * kKT * 2;
-    // one FP8 tile buffer: K rows, V rows, then the per-key factors, 64 floats
-    // per wave of which the first 16 are used: wave w < 4 holds a_j of keys
+    // one FP8 tile buffer: K rows, V rows, then the row scales, 64 floats per
+    // wave of which the first 16 are used: wave w < 4 holds sk_j of keys
     // 16w .. 16w+15, wave w >= 4 sv_j of keys 16(w-4) .. +15
     static constexpr int K_BYTES = kKT * D;
     static constexpr int V_BYTES = kKT * D;
@@ -117,8 +121,18 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf2));
 }
 
-__device__ __forceinline__ v16f mfma(v8i a, v8i b, v16f c) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+// E4M3 x E4M3 with E8M0 scales: sa (byte 0) scales the A row of this lane,
+// sb (byte 0) the B column, over this lane's 32-wide half of the contraction.
+__device__ __forceinline__ v16f mfma(v8i a, v8i b, v16f c, int sa, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// Exponent k of the smallest power of two with 448 * 2^k >= a (a >= 0),
+// clamped below at -127; from the fp32 fields, 448 = 1.75 * 2^8.
+__device__ __forceinline__ int scale_exponent(float a) {
+    const uint32_t b = __float_as_uint(a);
+    const int k = (int)(b >> 23) - ((b & 0x7FFFFFu) <= 0x600000u ? 135 : 134);
+    return k < -127 ? -127 : k;
 }
 
 __device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d) {
@@ -182,12 +196,6 @@ __device__ __forceinline__ void qwait(u32x4 (&q)[W]) {
 // clobber keeps the compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
-
 __device__ __forceinline__ int slot_of(const AttnArgs &a, int idx) {
     idx = idx < a.n_valid ? idx : a.n_valid - 1;       // keys past the window: any valid row
     const int s = a.slot_start + idx;
@@ -237,23 +245,10 @@ __device__ __forceinline__ void issue_tile(const AttnArgs &a, const uint8_t *kh,
                                      (LDS_AS void *)(buf + L::F_OFF + 256 * wave), 4, 0, 0);
 }
 
-// factor slot of key k (0..63): K a_j or V sv_j
+// scale slot of key k (0..63): K sk_j or V sv_j.  Keys past n_valid hold the
+// scale of a valid row; their weights are exactly zero.
 __device__ __forceinline__ int fk_index(int k) { return 64 * (k >> 4) + (k & 15); }
 __device__ __forceinline__ int fv_index(int k) { return 64 * (4 + (k >> 4)) + (k & 15); }
-
-// After its part of a tile has landed, each wave finishes its 16 factors in
-// place: K scales times the query-block factor, zero for keys past n_valid.
-template <int D>
-__device__ __forceinline__ void finish_factors(const AttnArgs &a, uint8_t *buf, int tile, int wave,
-                                               float qfac) {
-    const int lane = threadIdx.x % 64;
-    if (lane < 16) {
-        float *f = reinterpret_cast<float *>(buf + Lds<D>::F_OFF) + 64 * wave + lane;
-        const int key = 16 * (wave % 4) + lane;
-        const float v = *f;
-        *f = tile * kKT + key < a.n_valid ? (wave < 4 ? v * qfac : v) : 0.0f;
-    }
-}
 
 // Wait until at most `later` of this wave's tiles issued after the awaited
 // one are still in flight (the count must be an immediate).
@@ -276,7 +271,6 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     constexpr int P = kNBuf - 1;        // tiles in flight ahead of the one consumed
     static_assert(P - 1 <= 3, "wait_tiles covers up to three later tiles");
     extern __shared__ __align__(16) uint8_t smem[];
-    __shared__ float red[kNW];
 
     // ---- (head, split, query block); a (head, split) key range stays on one
     //      XCD (workgroups are dealt round-robin over the 8 XCDs) --------------
@@ -373,17 +367,16 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
                 qv[32 * h + 2 * i + 1] = x0 * ss + x1 * cc;
             }
     }
+    // per-query power-of-two scale 2^qk (lanes l and l ^ 32 hold the two
+    // halves of one query); the scaled query has absmax in (224, 448]
     float am = 0.0f;
 #pragma unroll
     for (int e = 0; e < QV; ++e) am = fmaxf(am, fabsf(qv[e]));
-    am = wave_max(am);
-    if (lane == 0) red[wave] = am;
-    lds_barrier();
-    float qmax = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kNW; ++w) qmax = fmaxf(qmax, red[w]);
-    const float qscale = qmax > 0.0f ? 448.0f / qmax : 1.0f;
-    const float qfac = (qmax > 0.0f ? qmax / 448.0f : 1.0f) * a.softmax_scale * kLog2e;
+    am = fmaxf(am, __shfl_xor(am, 32));
+    const int qk = scale_exponent(am);
+    const int qsc = qk + 127;                                   // E8M0 byte
+    const float qscale = __uint_as_float((uint32_t)(127 - qk) << 23);   // 2^-qk, a normal
+    const float c2 = a.softmax_scale * kLog2e;                  // scores in log2 units
 
     // Q hi/lo E4M3 operands: byte k of qop[h][hl] is element k of the lane's slice h
     v8i qop[NH][2];
@@ -400,8 +393,15 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
 
     // Lane-constant LDS offsets.  K A-operand: A-row i (= col) of block kb is
     // key 32kb + kk with kk = 16((i>>2)&1) + 4(i>>3) + (i&3); this lane reads
-    // the d chunks 4h + 2g and 4h + 2g + 1 (h = 64-wide slice).
+    // the d chunks 4h + 2g and 4h + 2g + 1 (h = 64-wide slice) and the row
+    // scale of that key.
     const int kk = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);
+    const int ks_off[2] = {L::F_OFF + 4 * fk_index(kk), L::F_OFF + 4 * fk_index(32 + kk)};
+    int ksc[2];                                                 // K E8M0 bytes, next S^T tile
+    auto read_kscales = [&](const uint8_t *buf) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) ksc[kb] = (int)(*reinterpret_cast<const uint32_t *>(buf + ks_off[kb]) >> 23);
+    };
     int koff[2][NH][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -463,7 +463,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     // busy while the other uses the VALU.
     // Buffers: tile t0+k sits in tile buffer k mod kNBuf.  The lead group
     // issues tile u+P (relative to t0) in interval 2u+1 and lands tile u+1
-    // (waits for it, finishes its factors) at the end of interval 2u, just
+    // (waits for its part of it) at the end of interval 2u, just
     // before its first use; the last reader of a tile is the trailing group's
     // V half-step, one interval before the buffer is reloaded.  V^T is double
     // buffered (written in M(t-1), read in M(t)).
@@ -475,22 +475,17 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     v16f s[2];                          // S^T of the tile of the next V half-step
     v8bf pb[2][2];                      // P of the tile of the next M half-step
 
-    auto half_v = [&](int t, const uint8_t *buf, const uint8_t *buf1, uint8_t *vt_next) {
-        const float *fa = reinterpret_cast<const float *>(buf + L::F_OFF);
+    auto half_v = [&](int t, const uint8_t *buf1, uint8_t *vt_next) {
         // scores (log2 units, shifted by cofs); register r of block kb is key
         // 32kb + 16g + r of the tile
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x4 f = *reinterpret_cast<const f32x4 *>(fa + fk_index(32 * kb + 16 * g + 4 * q));
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float v = s[kb][4 * q + r] * f[r] + cofs;
-                    s[kb][4 * q + r] = v;
-                    mx = fmaxf(mx, v);
-                }
+            for (int r = 0; r < 16; ++r) {
+                const float v = s[kb][r] * c2 + cofs;
+                s[kb][r] = v;
+                mx = fmaxf(mx, v);
             }
         const int lim = a.n_valid - t * kKT;              // valid keys of this tile
         if (lim < kKT) {                                  // last tile of the window
@@ -550,6 +545,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
                 pb[kb][ks] = __builtin_bit_cast(v8bf, w);
             }
         if (t + 1 < t1) convert_v(buf1, vt_next);      // V^T of tile t+1
+        read_kscales(buf1);                            // for S^T of tile t+1
     };
 
     // M half-step.  PV and PREP select the parts (both in the steady state).
@@ -602,7 +598,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
 #pragma unroll
                 for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb) s[kb] = mfma(ka[h][kb], qop[h][hl], s[kb]);
+                    for (int kb = 0; kb < 2; ++kb) s[kb] = mfma(ka[h][kb], qop[h][hl], s[kb], ksc[kb], qsc);
             // slice-0 operands first, slice-1 reads behind the slice-0 MFMAs
             __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
@@ -616,19 +612,17 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     using yes = std::true_type;
     using no = std::false_type;
 
-    // Every wave lands its own part of a tile (waits for it, finishes its
-    // factors) two tiles ahead, at the end of its V(u): tile u+2, whose V rows
-    // the next V half-step dequantises.  The newest tile a wave has issued
-    // before V(u) ends is max(P-1, min(u+P-1, n-1)).
+    // Every wave lands its own part of a tile (waits for it) two tiles ahead,
+    // at the end of its V(u): tile u+2, whose V rows the next V half-step
+    // dequantises; the barrier that follows publishes it.  The newest tile a
+    // wave has issued before V(u) ends is max(P-1, min(u+P-1, n-1)).
     auto land = [&](int u, int m) {                    // tile t0+m
-        if (m < n) {
-            wait_tiles<D>(max(P - 1, min(u + P - 1, n - 1)) - m);
-            finish_factors<D>(a, tiles + (m % kNBuf) * L::BUF, t0 + m, wave, qfac);
-        }
+        if (m < n) wait_tiles<D>(max(P - 1, min(u + P - 1, n - 1)) - m);
     };
     land(-1, 0);
     land(-1, 1);
     lds_barrier();
+    read_kscales(tiles);
     half_m(t0 - 1, tiles, vt_base, no{}, yes{});       // S^T of tile t0
     convert_v(tiles, vt_base);                         // V^T of tile t0
     lds_barrier();
@@ -646,9 +640,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     for (int u = 0; u < n; ++u) {
         const int bnext = bcur + 1 == kNBuf ? 0 : bcur + 1;
         const int vnext = vcur + 1 == 3 ? 0 : vcur + 1;
-        uint8_t *buf = tiles + bcur * L::BUF;
         uint8_t *buf1 = tiles + bnext * L::BUF;
-        half_v(t0 + u, buf, buf1, vt_base + vnext * L::VT_BYTES);
+        half_v(t0 + u, buf1, vt_base + vnext * L::VT_BYTES);
         land(u, u + 2);
         lds_barrier();
         if (u + P < n) {                               // stream tile t0+u+P

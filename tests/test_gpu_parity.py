@@ -63,8 +63,40 @@ def test_rope_table_matches_oracle():
         assert same >= 0.9999 and ulps.max() <= 1, (same, ulps.max())
 
 
+def test_scale_exponent_boundaries_through_write():
+    """Row absmax exactly at 448 * 2^j, one float above and below, from the
+    subnormal range to 2^100: codes and power-of-two scales bit-exact."""
+    _say("scale exponent boundaries")
+    D = 64
+    heads = []
+    for j in range(-150, 101):
+        b = np.float32(448.0 * 2.0 ** j)
+        if b == 0 or not np.isfinite(b):
+            continue
+        heads += [b, np.nextafter(b, np.float32(np.inf)), np.nextafter(b, np.float32(0))]
+    heads = np.array([h for h in heads if h > 0], np.float32)
+    n = heads.size
+    rng = np.random.default_rng(17)
+    v = (rng.uniform(-1, 1, (n, D)) * heads[:, None]).astype(np.float32)
+    v[:, 0] = np.where(rng.random(n) < 0.5, heads, -heads)
+    v = np.where(np.abs(v) <= np.abs(v[:, :1]), v, v[:, :1]).astype(np.float32)
+    H, W = 1, n
+    cache = K.KVCache(1, H, D, W)
+    rope = K.RopeTable(0, n, D)
+    k = torch.zeros((n, H, D), dtype=torch.float32, device="cuda")
+    vt = torch.from_numpy(v).view(n, H, D).cuda()
+    K.kv_write_rope_quant(cache, K.kvr_ring_init(), 0, k, vt, rope)
+    torch.cuda.synchronize()
+    want_c, want_s = oracle.quant_rows(v)
+    got_s = _np(cache.v_scales)[0, 0]
+    assert np.array_equal(got_s.view(np.uint32), want_s.view(np.uint32)), \
+        np.argwhere(got_s.view(np.uint32) != want_s.view(np.uint32))[:5]
+    got_c = _np(cache.v_codes)[0, 0]
+    assert np.array_equal(got_c, want_c), np.argwhere(got_c != want_c)[:5]
+
+
 def test_e4m3_conversion_sweep_through_write():
-    """V rows whose absmax is 448 are encoded without scaling (448/448 = 1)."""
+    """V rows whose absmax is 448 are encoded without scaling (448 = 448 * 2^0)."""
     _say("e4m3 sweep")
     codes = np.arange(0x7F, dtype=np.uint8)
     tv = np.sort(oracle.e4m3_decode(codes)).astype(np.float32)
