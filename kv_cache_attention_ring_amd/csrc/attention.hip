@@ -272,19 +272,22 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     static_assert(P - 1 <= 3, "wait_tiles covers up to three later tiles");
     extern __shared__ __align__(16) uint8_t smem[];
 
-    // ---- (head, split, query block); a (head, split) key range stays on one
-    //      XCD (workgroups are dealt round-robin over the 8 XCDs) --------------
+    // ---- (head, split, query block) ------------------------------------------
+    // Workgroups are dealt round-robin over the 8 XCDs (block b runs on XCD
+    // b % 8).  Renumber them so that the blocks of one XCD take consecutive
+    // slots of the (unit, query block) order: the query blocks of a (head,
+    // split) key range then share an XCD and its L2, and the range is read
+    // from HBM once rather than once per query block (at most 7 ranges
+    // straddle two XCDs).
     const int n_qb = (a.n_q + kQB - 1) / kQB;
-    const int units = a.n_heads * a.n_splits;
     int unit, qb;
-    const int b = blockIdx.x;
-    if (units % 8 == 0) {
+    {
+        const int b = blockIdx.x, G = gridDim.x;
         const int xcd = b % 8, k = b / 8;
-        unit = (k / n_qb) * 8 + xcd;
-        qb = k % n_qb;
-    } else {
-        unit = b / n_qb;
-        qb = b % n_qb;
+        const int per = G / 8, extra = G % 8;             // XCDs below `extra` hold per + 1
+        const int slot = xcd * per + min(xcd, extra) + k;
+        unit = slot / n_qb;
+        qb = slot % n_qb;
     }
     const int head = unit / a.n_splits;
     const int split = unit % a.n_splits;
