@@ -34,9 +34,7 @@
  *   - Cache layout (one K and one V buffer pair per cache):
  *       codes  uint8  [n_layers][n_heads][window][head_dim]   OCP E4M3 bytes
  *       scales float  [n_layers][n_heads][window]             dequant factor
- *     A stored element decodes to e4m3(code) * scale.  scale is a power of
- *     two, 2^k with k the smallest integer such that 448 * 2^k >= row absmax
- *     (k clamped to [-127, 127]), so it doubles as an E8M0 matrix-core scale.
+ *     A stored element decodes to e4m3(code) * scale, scale = row absmax / 448.
  *   - head_dim is 64 or 128; window and n_new are >= 1 and < 2^24.
  */
 #ifndef KVRING_H
@@ -116,9 +114,8 @@ int32_t kv_rope_table_fill(float *cs, int64_t pos0, int32_t n_pos, int32_t head_
  * [AI-cache] [NC-cache] [WC].  For layers layer0 .. layer0+n_layers-1 and new
  * tokens j < n_new: K row (j, h) is rotated at position before->pos_next + j
  * (pairs (x[2i], x[2i+1]) by angle p * theta_i, fp32, no FMA), then K and V
- * rows are quantised (a = row absmax; scale = 2^k, k the smallest integer with
- * 448 * 2^k >= a, clamped to [-127, 127]; code = E4M3 RNE of y * 2^-k, exact
- * scaling; a == 0 gives scale 0 and zero codes) and stored at slot
+ * rows are quantised (a = row absmax; scale = a / 448; code = E4M3 RNE of
+ * y * (448 / a); a == 0 gives scale 0 and zero codes) and stored at slot
  * (before->head + j) mod window.  The ring itself is not modified: call
  * kvr_ring_after_write afterwards.
  *   k_new, v_new : device, per layer [n_new][n_heads][head_dim] of `dtype`,

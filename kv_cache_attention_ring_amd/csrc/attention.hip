@@ -14,9 +14,8 @@
 // (q_i rotated at position q_pos0 + i: fp64 angle reduced to revolutions, then
 // the hardware sine and cosine; the result goes into E4M3 hi/lo terms, so the
 // rotation only needs fp32 accuracy)
-// with k^_j = e4m3(code) * sk_j and v^_j = e4m3(code) * sv_j (one power-of-two
-// scale per cached row).  Keys are visited in logical window order
-// (slot_start + j) mod W.
+// with k^_j = e4m3(code) * sk_j and v^_j = e4m3(code) * sv_j (one fp32 scale per
+// cached row).  Keys are visited in logical window order (slot_start + j) mod W.
 //
 // Work decomposition.  A workgroup owns one head, a block of 256 queries and a
 // contiguous range of 64-key tiles (a "split"); each of its 8 waves (two per
@@ -41,12 +40,11 @@
 //
 // Precision: E4M3 has 3 mantissa bits, so Q goes in as two E4M3 terms (hi +
 // lo, lo = e4m3(x - hi)), about 8 significant bits and two MFMAs per 64-wide
-// slice.  Row scales are powers of two, so they enter the first product as
-// the matrix core's E8M0 block scales: the K row scale of each A row (its
-// exponent byte is the fp32 scale's bits 23..30) and a per-query Q scale of
-// each B column; the accumulator then holds q_i . k^_j itself.  The weights
-// and V^T are bf16 (8 significant bits; a code times a power of two is exact
-// in bf16), so the second product needs no split.  Softmax runs in the log2 domain with a
+// slice.  Each query has its own power-of-two scale, applied by the matrix
+// core as the E8M0 scale of its B column, and softmax_scale * log2(e) is
+// folded into Q before it is split, so the accumulator holds the score in log2
+// units up to the K row scale: one FMA per score applies sk_j.  The weights
+// and V^T are bf16 (8 significant bits), so the second product needs no split.  Softmax runs in the log2 domain with a
 // lazily updated running max (rescale only when a score passes it by more
 // than 16, so weights stay below 2^16 and the fp32 sums cannot overflow).  Splits of one (head, query block) are merged by a second kernel
 // in split order, so a call is deterministic and a linear window gives the
@@ -90,7 +88,8 @@ struct Lds {
     static constexpr int VT_BYTES = D * kKT * 2;
     // one FP8 tile buffer: K rows, V rows, then the row scales, 64 floats per
     // wave of which the first 16 are used: wave w < 4 holds sk_j of keys
-    // 16w .. 16w+15, wave w >= 4 sv_j of keys 16(w-4) .. +15
+    // 16w .. 16w+15, wave w >= 4 sv_j of keys 16(w-4) .. +15 (keys past n_valid
+    // hold the scale of a valid row; their weights are exactly zero)
     static constexpr int K_BYTES = kKT * D;
     static constexpr int V_BYTES = kKT * D;
     static constexpr int F_OFF = K_BYTES + V_BYTES;
@@ -121,10 +120,11 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf2));
 }
 
-// E4M3 x E4M3 with E8M0 scales: sa (byte 0) scales the A row of this lane,
-// sb (byte 0) the B column, over this lane's 32-wide half of the contraction.
-__device__ __forceinline__ v16f mfma(v8i a, v8i b, v16f c, int sa, int sb) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+// E4M3 x E4M3 with E8M0 scales: 2^(sb-127) (byte 0 of sb) scales the B column
+// of this lane over its 32-wide half of the contraction; the A rows are
+// unscaled (127 = 2^0).
+__device__ __forceinline__ v16f mfma(v8i a, v8i b, v16f c, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, sb);
 }
 
 // Exponent k of the smallest power of two with 448 * 2^k >= a (a >= 0),
@@ -245,8 +245,7 @@ __device__ __forceinline__ void issue_tile(const AttnArgs &a, const uint8_t *kh,
                                      (LDS_AS void *)(buf + L::F_OFF + 256 * wave), 4, 0, 0);
 }
 
-// scale slot of key k (0..63): K sk_j or V sv_j.  Keys past n_valid hold the
-// scale of a valid row; their weights are exactly zero.
+// scale slot of key k (0..63): K sk_j or V sv_j
 __device__ __forceinline__ int fk_index(int k) { return 64 * (k >> 4) + (k & 15); }
 __device__ __forceinline__ int fv_index(int k) { return 64 * (4 + (k >> 4)) + (k & 15); }
 
@@ -370,16 +369,20 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
                 qv[32 * h + 2 * i + 1] = x0 * ss + x1 * cc;
             }
     }
+    // scores in log2 units: fold softmax_scale * log2(e) into q; then a
     // per-query power-of-two scale 2^qk (lanes l and l ^ 32 hold the two
-    // halves of one query); the scaled query has absmax in (224, 448]
+    // halves of one query), so the scaled query has absmax in (224, 448]
+    const float c2 = a.softmax_scale * kLog2e;
     float am = 0.0f;
 #pragma unroll
-    for (int e = 0; e < QV; ++e) am = fmaxf(am, fabsf(qv[e]));
+    for (int e = 0; e < QV; ++e) {
+        qv[e] *= c2;
+        am = fmaxf(am, fabsf(qv[e]));
+    }
     am = fmaxf(am, __shfl_xor(am, 32));
     const int qk = scale_exponent(am);
     const int qsc = qk + 127;                                   // E8M0 byte
     const float qscale = __uint_as_float((uint32_t)(127 - qk) << 23);   // 2^-qk, a normal
-    const float c2 = a.softmax_scale * kLog2e;                  // scores in log2 units
 
     // Q hi/lo E4M3 operands: byte k of qop[h][hl] is element k of the lane's slice h
     v8i qop[NH][2];
@@ -396,15 +399,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
 
     // Lane-constant LDS offsets.  K A-operand: A-row i (= col) of block kb is
     // key 32kb + kk with kk = 16((i>>2)&1) + 4(i>>3) + (i&3); this lane reads
-    // the d chunks 4h + 2g and 4h + 2g + 1 (h = 64-wide slice) and the row
-    // scale of that key.
+    // the d chunks 4h + 2g and 4h + 2g + 1 (h = 64-wide slice).
     const int kk = 16 * ((col >> 2) & 1) + 4 * (col >> 3) + (col & 3);
-    const int ks_off[2] = {L::F_OFF + 4 * fk_index(kk), L::F_OFF + 4 * fk_index(32 + kk)};
-    int ksc[2];                                                 // K E8M0 bytes, next S^T tile
-    auto read_kscales = [&](const uint8_t *buf) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) ksc[kb] = (int)(*reinterpret_cast<const uint32_t *>(buf + ks_off[kb]) >> 23);
-    };
     int koff[2][NH][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -478,17 +474,22 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     v16f s[2];                          // S^T of the tile of the next V half-step
     v8bf pb[2][2];                      // P of the tile of the next M half-step
 
-    auto half_v = [&](int t, const uint8_t *buf1, uint8_t *vt_next) {
-        // scores (log2 units, shifted by cofs); register r of block kb is key
-        // 32kb + 16g + r of the tile
+    auto half_v = [&](int t, const uint8_t *buf, const uint8_t *buf1, uint8_t *vt_next) {
+        const float *fk = reinterpret_cast<const float *>(buf + L::F_OFF);
+        // scores (log2 units, shifted by cofs): the accumulator times the K row
+        // scale; register r of block kb is key 32kb + 16g + r of the tile
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float v = s[kb][r] * c2 + cofs;
-                s[kb][r] = v;
-                mx = fmaxf(mx, v);
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 f = *reinterpret_cast<const f32x4 *>(fk + fk_index(32 * kb + 16 * g + 4 * q));
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float v = s[kb][4 * q + r] * f[r] + cofs;
+                    s[kb][4 * q + r] = v;
+                    mx = fmaxf(mx, v);
+                }
             }
         const int lim = a.n_valid - t * kKT;              // valid keys of this tile
         if (lim < kKT) {                                  // last tile of the window
@@ -548,7 +549,6 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
                 pb[kb][ks] = __builtin_bit_cast(v8bf, w);
             }
         if (t + 1 < t1) convert_v(buf1, vt_next);      // V^T of tile t+1
-        read_kscales(buf1);                            // for S^T of tile t+1
     };
 
     // M half-step.  PV and PREP select the parts (both in the steady state).
@@ -601,7 +601,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
 #pragma unroll
                 for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb) s[kb] = mfma(ka[h][kb], qop[h][hl], s[kb], ksc[kb], qsc);
+                    for (int kb = 0; kb < 2; ++kb) s[kb] = mfma(ka[h][kb], qop[h][hl], s[kb], qsc);
             // slice-0 operands first, slice-1 reads behind the slice-0 MFMAs
             __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
@@ -625,7 +625,6 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     land(-1, 0);
     land(-1, 1);
     lds_barrier();
-    read_kscales(tiles);
     half_m(t0 - 1, tiles, vt_base, no{}, yes{});       // S^T of tile t0
     convert_v(tiles, vt_base);                         // V^T of tile t0
     lds_barrier();
@@ -643,8 +642,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     for (int u = 0; u < n; ++u) {
         const int bnext = bcur + 1 == kNBuf ? 0 : bcur + 1;
         const int vnext = vcur + 1 == 3 ? 0 : vcur + 1;
+        uint8_t *buf = tiles + bcur * L::BUF;
         uint8_t *buf1 = tiles + bnext * L::BUF;
-        half_v(t0 + u, buf1, vt_base + vnext * L::VT_BYTES);
+        half_v(t0 + u, buf, buf1, vt_base + vnext * L::VT_BYTES);
         land(u, u + 2);
         lds_barrier();
         if (u + P < n) {                               // stream tile t0+u+P

@@ -13,9 +13,8 @@
 // absmax is a 3-step butterfly across those 8 lanes.  Decoding a stored row
 // is the exact E4M3 value times the fp32 row scale (one fp32 product).  The arithmetic order
 // of one element is fixed (rotation: x0*c - x1*s, x0*s + x1*c, each product
-// and sum rounded to fp32; quantisation: y * 2^-k with 2^k the power-of-two
-// row scale (an exact scaling), then E4M3 round-to-nearest-even via
-// v_cvt_pk_fp8_f32), and this file is
+// and sum rounded to fp32; quantisation: y * (448 / absmax) rounded to fp32,
+// then E4M3 round-to-nearest-even via v_cvt_pk_fp8_f32), and this file is
 // built with -ffp-contract=off so no FMA merges those roundings.  The write,
 // rebase and naive kernels share these device helpers, so the ring cache and
 // the naive linear window are bit-identical.
@@ -89,22 +88,8 @@ __device__ __forceinline__ void rotate_pairs(float (&x)[EPT], const float *cs) {
     }
 }
 
-// Exponent k of the power-of-two row scale: the smallest k with
-// 448 * 2^k >= a, for a > 0, clamped below at -127.  With a = (1 + m) 2^(E-127)
-// (E the biased exponent, m the 23-bit fraction), 448 = 1.75 * 2^8 gives
-// k = E - 135 when 1 + m <= 1.75 and E - 134 otherwise; subnormal a (E = 0)
-// falls under the clamp.
-__device__ __forceinline__ int scale_exponent(float a) {
-    const uint32_t b = __float_as_uint(a);
-    const int e = (int)(b >> 23);
-    const int k = e - ((b & 0x7FFFFFu) <= 0x600000u ? 135 : 134);
-    return k < -127 ? -127 : k;
-}
-
-// Row quantisation: absmax a over the 8 lanes of the row, scale = 2^k
-// (scale_exponent), codes = E4M3_RNE(y * 2^-k); 2^-k is a normal fp32 for
-// every k here, so the scaling is exact.  Writes EPT codes and (lane 0) the
-// scale.
+// Row quantisation: absmax over the 8 lanes of the row, scale = a / 448,
+// codes = E4M3_RNE(y * (448 / a)).  Writes EPT codes and (lane 0) the scale.
 template <int EPT>
 __device__ __forceinline__ void quantize_store(const float (&y)[EPT], uint8_t *codes_dst,
                                                float *scale_dst, bool lane0) {
@@ -121,9 +106,8 @@ __device__ __forceinline__ void quantize_store(const float (&y)[EPT], uint8_t *c
 #pragma unroll
         for (int k = 0; k < EPT / 4; ++k) w[k] = 0u;
     } else {
-        const int k = scale_exponent(a);
-        scale = k >= -126 ? __uint_as_float((uint32_t)(k + 127) << 23) : __uint_as_float(0x00400000u);
-        const float inv = __uint_as_float((uint32_t)(127 - k) << 23);
+        scale = a / 448.0f;
+        const float inv = 448.0f / a;
 #pragma unroll
         for (int k = 0; k < EPT / 4; ++k) {
             const float t0 = y[4 * k] * inv, t1 = y[4 * k + 1] * inv;

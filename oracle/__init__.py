@@ -68,8 +68,6 @@ def lib():
                                     ctypes.c_double]
         L.orc_rope_cs_n.argtypes = [_c_i64p, ctypes.c_int64, ctypes.c_int, ctypes.c_double, _c_f32p]
         L.orc_quant_rows.argtypes = [_c_f32p, ctypes.c_int64, ctypes.c_int, _c_u8p, _c_f32p]
-        L.orc_scale_exp.restype = ctypes.c_int
-        L.orc_scale_exp.argtypes = [ctypes.c_float]
         L.orc_dequant_rows.argtypes = [_c_u8p, _c_f32p, ctypes.c_int64, ctypes.c_int, _c_f32p]
         L.orc_slot_of_token.restype = ctypes.c_int32
         L.orc_slot_of_token.argtypes = [ctypes.c_int64, ctypes.c_int32]
@@ -132,11 +130,6 @@ def rope_cs(pos, D: int, base: float = 10000.0) -> np.ndarray:
     out = np.empty((p.size, D // 2, 2), np.float32)
     lib().orc_rope_cs_n(_p(p, _c_i64p), p.size, D, float(base), _p(out, _c_f32p))
     return out
-
-
-def scale_exp(a: float) -> int:
-    """Exponent k of the row scale 2^k for a row absmax a > 0."""
-    return int(lib().orc_scale_exp(float(a)))
 
 
 def quant_rows(y):

@@ -23,11 +23,8 @@
  *                format E4M3 (bias 7, no infinities, S.1111.111 = NaN).
  *
  * Readings where the pages are silent (all recorded in the design notes):
- *   - FP8 is OCP E4M3 with one scale per (token, head) row.  The scale is a
- *     power of two (an E8M0 value, the block-scale format of the OCP MX
- *     specification): 2^k with k the smallest integer such that 448 * 2^k is
- *     at least the row absmax; codes are RNE(y * 2^-k) (an exact scaling),
- *     so the largest element lands in (224, 448].
+ *   - FP8 is OCP E4M3 with one fp32 scale per (token, head) row; the scale is
+ *     the row absmax / 448 and codes are RNE(y * (448 / absmax)), saturating.
  *   - RoPE is the 1-D rotary encoding on interleaved pairs (x[2i], x[2i+1]),
  *     theta_i = base^(-2i/D), angle = p * theta_i formed in fp64, cos/sin in
  *     fp64 and rounded to fp32, rotation in fp32 without FMA.
@@ -86,25 +83,9 @@ uint8_t orc_e4m3_encode(float v)
 
 /* ------------------------------------------------------------------------ */
 /* Row quantisation (per token, per head)            [AI-cache] [NC-cache]  */
-/* Pins: the scale is the smallest power of two with 448 * scale >= absmax */
-/* (brute force over exponents); the absmax element encodes into           */
-/* (224, 448]; the dequantisation error is within half an E4M3 ulp; zero   */
-/* rows give scale 0 and zero codes.                                       */
+/* Pins: absmax element encodes to +-448 exactly; dequantisation error is  */
+/* within half an E4M3 ulp; zero rows give scale 0 and zero codes.         */
 /* ------------------------------------------------------------------------ */
-
-/* Exponent k of the row scale 2^k: the smallest k with 448 * 2^k >= a (a > 0).
- * With a = f * 2^e, f in [0.5, 1): 448 * 2^k = 0.875 * 2^(k+9), so k = e - 9
- * when f <= 0.875 and e - 8 otherwise.  Clamped to the E8M0 range [-127, 127]. */
-int orc_scale_exp(float a)
-{
-    int e;
-    double f = frexp((double)a, &e);
-    int k = (f <= 0.875) ? e - 9 : e - 8;
-    if (k < -127) k = -127;
-    if (k > 127) k = 127;
-    return k;
-}
-
 void orc_quant_row(const float *y, int D, uint8_t *codes, float *scale)
 {
     float a = 0.0f;
@@ -117,10 +98,10 @@ void orc_quant_row(const float *y, int D, uint8_t *codes, float *scale)
         memset(codes, 0, (size_t)D);
         return;
     }
-    int k = orc_scale_exp(a);
-    *scale = ldexpf(1.0f, k);
+    *scale = a / 448.0f;
+    float inv = 448.0f / a;
     for (int d = 0; d < D; ++d) {
-        float t = ldexpf(y[d], -k);        /* exact: a power-of-two scaling */
+        float t = y[d] * inv;
         codes[d] = orc_e4m3_encode(t);
     }
 }
@@ -208,7 +189,7 @@ void orc_write(uint8_t *k_codes, uint8_t *v_codes, float *k_scales, float *v_sca
 /* Delta rebase of the stored window on a position reset         [AI-cache] */
 /* Every valid K row (logical index 0..n_valid-1 at slot (start+i) mod W) is
  * dequantised, rotated by -delta (so a key stored at position p now encodes
- * p - delta) and re-quantised with a fresh row scale.  V is untouched.
+ * p - delta) and re-quantised with a fresh absmax scale.  V is untouched.
  * Pin: R(-D)R(p) == R(p-D); rebase(+D) then rebase(-D) returns the row
  * within quantisation error; attention is unchanged when queries move too. */
 /* ------------------------------------------------------------------------ */

@@ -6,10 +6,9 @@ the rotation-group identity R(-delta) R(p) = R(p - delta) in fp32 to 1e-5 over
 the positions a 42-step reset period reaches; p = 0 is the identity; pair norms
 are kept; q.k depends on position differences only.
 
-Quantisation pins: the row scale is the smallest power of two whose 448-fold
-reaches the row absmax (brute force over exponents, exact in double); the
-absmax element encodes into [224, 448]; the dequantisation error is within
-half an E4M3 ulp of the scaled value; zero rows give scale 0 and zero codes.
+Quantisation pins: the absmax element of every non-zero row encodes to +-448;
+the dequantisation error is within half an E4M3 ulp; zero rows give scale 0
+and zero codes.
 """
 import numpy as np
 import pytest
@@ -88,27 +87,6 @@ def _half_ulp(t):
     return np.where(a < 2.0 ** -6, 2.0 ** -10, 2.0 ** (e - 4))
 
 
-def _brute_scale_exp(a):
-    """Smallest k with 448 * 2^k >= a (a > 0), by search (exact in double)."""
-    k = -140
-    while 448.0 * 2.0 ** k < a:
-        k += 1
-    return k
-
-
-def test_scale_exponent_brute_force():
-    rng = np.random.default_rng(9)
-    vals = list((rng.standard_normal(2000) * 10.0 ** rng.uniform(-6, 6, 2000)).astype(np.float32))
-    for j in range(-20, 20):                       # exact boundaries and their neighbours
-        b = np.float32(448.0 * 2.0 ** j)
-        vals += [b, np.nextafter(b, np.float32(np.inf)), np.nextafter(b, np.float32(0))]
-    for a in vals:
-        a = abs(float(np.float32(a)))
-        if a == 0.0:
-            continue
-        assert oracle.scale_exp(a) == _brute_scale_exp(a), a
-
-
 def test_quant_rows_invariants():
     rng = np.random.default_rng(5)
     y = (rng.standard_normal((3000, 128)) * rng.uniform(1e-3, 50, (3000, 1))).astype(np.float32)
@@ -118,22 +96,17 @@ def test_quant_rows_invariants():
     assert scales[7] == 0.0 and not codes[7].any()
     a = np.abs(y).max(axis=1)
     nz = a > 0
-    # scales are exact powers of two, the smallest whose 448-fold reaches the absmax
-    m, e = np.frexp(scales[nz].astype(np.float64))
-    assert np.all(m == 0.5)
-    assert np.all(448.0 * scales[nz].astype(np.float64) >= a[nz])
-    assert np.all(224.0 * scales[nz].astype(np.float64) < a[nz])
-    # the absmax element lands in [224, 448]
     am = np.abs(y).argmax(axis=1)
-    top = np.abs(oracle.e4m3_decode(codes[np.arange(len(y)), am]))
-    assert np.all((top[nz] > 224.0 - 16.0) & (top[nz] <= 448.0))
+    top = codes[np.arange(len(y)), am]
+    assert np.all((top[nz] & 0x7F) == 0x7E)
+    assert np.all(np.abs(scales[nz] - a[nz] / 448.0) <= 1e-7 * a[nz] / 448.0)
     # error of each code against the scaled value is at most half an ulp
-    t = y[nz].astype(np.float64) / scales[nz, None].astype(np.float64)
+    t = y[nz].astype(np.float64) * (448.0 / a[nz, None])
     dec = oracle.e4m3_decode(codes[nz])
-    assert np.all(np.abs(dec - t) <= _half_ulp(t) * (1 + 1e-6) + 1e-12)
+    assert np.all(np.abs(dec - t) <= _half_ulp(t) * (1 + 1e-6) + 1e-5)
     # dequantised rows reproduce the input within half an ulp of the scaled value
     x = oracle.dequant_rows(codes, scales)
-    assert np.all(np.abs(x[nz] - y[nz]) <= (_half_ulp(t) + 1e-12) * scales[nz, None] * 1.0001)
+    assert np.all(np.abs(x[nz] - y[nz]) <= (_half_ulp(t) + 1e-5) * scales[nz, None] * 1.0001)
 
 
 def test_quant_sign_of_zero_and_tiny():
@@ -141,5 +114,4 @@ def test_quant_sign_of_zero_and_tiny():
     y[0, 0] = 1.0
     y[0, 1] = -1e-9          # rounds to a negative zero code
     codes, s = oracle.quant_rows(y)
-    assert s[0] == 2.0 ** -8                  # 448 * 2^-9 < 1 <= 448 * 2^-8
-    assert codes[0, 0] == 0x78 and codes[0, 1] == 0x80 and codes[0, 2] == 0x00   # 256 = 2^8
+    assert codes[0, 0] == 0x7E and codes[0, 1] == 0x80 and codes[0, 2] == 0x00
