@@ -48,6 +48,12 @@ def counted_traffic():
     return int(t.group(1))
 
 
+def pct(sorted_vals, p):
+    """p-th percentile (nearest rank) of an ascending list."""
+    k = max(0, min(len(sorted_vals) - 1, int(round(p / 100.0 * len(sorted_vals) + 0.5)) - 1))
+    return sorted_vals[k]
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -153,17 +159,20 @@ def main():
     torch.cuda.synchronize()
 
     # ---- timed steps ---------------------------------------------------------
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event per step boundary (recording an event does not synchronise)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t_wall = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
+    evs[0].record()
+    for i in range(args.steps):
         step(sidx)
         sidx += 1
-    ev1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t_wall) * 1e3
-    ms_step = ev0.elapsed_time(ev1) / args.steps
-    log(f"{args.steps} steps: {ms_step:.4f} ms/step (wall {wall_ms / args.steps:.4f})")
+    ms_step = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    log(f"{args.steps} steps: {ms_step:.4f} ms/step (wall {wall_ms / args.steps:.4f}); median "
+        f"{pct(per_step, 50):.4f}, p90 {pct(per_step, 90):.4f}, max {per_step[-1]:.4f}")
 
     # ---- per-kernel times, measured with events on the launch stream -----------
     n_meas = 2
@@ -187,6 +196,7 @@ def main():
         a_ms += [e[j].elapsed_time(e[j + 1]) for j in range(2, len(e), 2)]
     write_ms = sum(w_ms) / len(w_ms)
     attn_ms = sum(a_ms) / len(a_ms)
+    a_sorted = sorted(a_ms)
     attn_flops = 4.0 * N * W * H * D
     attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
     write_bytes = L * (2 * N * H * D * 2 + 2 * N * H * D + 2 * N * H * 4)
@@ -248,11 +258,16 @@ def main():
             "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
             "traffic": counted_traffic(),
         },
+        "step_ms": {"mean": round(ms_step, 5), "median": round(pct(per_step, 50), 5),
+                    "p90": round(pct(per_step, 90), 5), "max": round(per_step[-1], 5)},
         "breakdown": {
             "write_60_layers_us": round(write_ms * 1e3, 2),
             "write_GBps": round(write_gbs, 1),
             "write_frac_hbm": round(write_gbs / HBM_PEAK_GBS, 4),
             "attention_call_us": round(attn_ms * 1e3, 3),
+            "attention_call_us_median": round(pct(a_sorted, 50) * 1e3, 3),
+            "attention_call_us_p90": round(pct(a_sorted, 90) * 1e3, 3),
+            "upkeep_share_of_step": round(write_ms / ms_step, 4),
             "attention_ms_per_step": round(attn_ms * P * L, 4),
             "rebase_ms": round(reb_ms, 4),
             "rebase_GBps": round(reb_gbs, 1),

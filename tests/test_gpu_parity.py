@@ -185,7 +185,7 @@ class SmallRun:
                 assert np.array_equal(np.ascontiguousarray(r).view(np.uint8),
                                       np.ascontiguousarray(l).view(np.uint8)), f"{what}: ring != naive"
 
-    def attention(self, q, n_splits=0, naive_too=True):
+    def attention(self, q, n_splits=0, naive_too=True, ws=None):
         """q fp32 numpy [n_q][H][D]; returns (gpu bf16 as fp32, oracle fp64)."""
         W = self.s.window
         qd = torch.from_numpy(q).to(self.dtype).cuda()
@@ -193,7 +193,7 @@ class SmallRun:
         qpos = self.ring.pos_next - n_q
         start = K.kvr_ring_logical_start(self.ring, W)
         out = K.attn_fp8_window(self.cache, 0, start, self.ring.n_valid, qd, qpos, self.rope.base,
-                                n_splits=n_splits)
+                                n_splits=n_splits, ws=ws)
         if naive_too:
             lin_cache = K.KVCache(1, self.s.n_heads, self.s.head_dim, W)
             lin_cache.k_codes[0].copy_(self.lc)
@@ -201,7 +201,7 @@ class SmallRun:
             lin_cache.k_scales[0].copy_(self.lks)
             lin_cache.v_scales[0].copy_(self.lvs)
             out_lin = K.attn_fp8_window(lin_cache, 0, 0, self.ring.n_valid, qd, qpos, self.rope.base,
-                                        n_splits=n_splits)
+                                        n_splits=n_splits, ws=ws)
             torch.cuda.synchronize()
             assert torch.equal(out, out_lin), "ring and naive attention differ"
         torch.cuda.synchronize()
@@ -308,6 +308,25 @@ def test_fp32_inputs_head_dim_128():
         run.check_cache(f"fp32 D128 step {step}")
         got, ref = run.attention(inputs.np_queries(shp, step, 0), n_splits=(step % 3) + 1)
         assert_attention(got, ref, f"fp32 D128 step {step}")
+
+
+def test_split_merge_shares_one_workspace():
+    """One workspace serves a run of calls with different split and query
+    counts (3, 2 and 1 query blocks; up to 17 requested splits): every output
+    matches the oracle, and the linear window bit for bit."""
+    shp = inputs.Shape("test", 1, 3, 128, 1100, 600)
+    run = SmallRun(shp, dtype=torch.bfloat16)
+    for step in range(2):
+        k, v = inputs.np_chunk(shp, step)
+        run.step(k, v)
+    calls = [(600, 2), (600, 17), (257, 5), (600, 3), (1, 9), (600, 7), (513, 4)]
+    cap = max(K.attn_fp8_window_workspace_bytes(run.cache, n_q, run.ring.n_valid, sp) for n_q, sp in calls)
+    ws = torch.empty(cap, dtype=torch.uint8, device="cuda")
+    for i, (n_q, splits) in enumerate(calls):
+        _say(f"shared workspace call {i}: n_q {n_q}, splits {splits}")
+        q = inputs.np_queries(shp, 1, i)[:n_q]
+        got, ref = run.attention(q, n_splits=splits, ws=ws)
+        assert_attention(got, ref, f"shared workspace call {i}")
 
 
 def test_bf16_ragged_queries_head_dim_64():
