@@ -71,7 +71,47 @@ def parse():
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB and exit "
                          "(reference kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--attn-calls", type=int, default=0,
+                    help="only time this many attention calls on one production-shape layer "
+                         "(12 heads x 128, window 5788, 757 queries) and exit (for counter runs)")
     return ap.parse_args()
+
+
+def attn_only(calls, splits):
+    """One layer cache written with 8 chunks (full, wrapped ring), then `calls`
+    timed attention calls after 3 warm-up calls: the attention kernel alone,
+    for profiler counter runs."""
+    import torch
+    from kv_cache_attention_ring_amd import inputs
+    from kv_cache_attention_ring_amd import kvring as K
+    shp = inputs.PAGE_LAYER
+    H, D, W, N = shp.n_heads, shp.head_dim, shp.window, shp.n_new
+    cache = K.KVCache(1, H, D, W)
+    rope = K.RopeTable(0, 12 * N, D)
+    ring = K.kvr_ring_init()
+    for s in range(8):
+        k, v = inputs.torch_chunk(shp, s, 0, "cuda")
+        K.kv_write_rope_quant(cache, ring, 0, k[0], v[0], rope)
+        K.kvr_ring_after_write(ring, W, N)
+    qs = [inputs.torch_queries(shp, 8, p, 0, "cuda") for p in range(4)]
+    out = torch.empty_like(qs[0])
+    need = K.attn_fp8_window_workspace_bytes(cache, N, W, splits)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    start = K.kvr_ring_logical_start(ring, W)
+    call = lambda i: K.attn_fp8_window(cache, 0, start, W, qs[i % 4], ring.pos_next - N, rope.base,
+                                       out=out, n_splits=splits, ws=ws)
+    for i in range(3):
+        call(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(calls):
+        call(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / calls * 1e3
+    print(json.dumps({"attention_calls": calls, "splits": splits or "default", "attention_call_us": round(us, 3),
+                      "TFLOPs": round(4.0 * N * W * H * D / (us * 1e-6) / 1e12, 1)}), flush=True)
 
 
 def copy_only(mib):
@@ -101,6 +141,9 @@ def main():
     args = parse()
     if args.copy_mb:
         copy_only(args.copy_mb)
+        return
+    if args.attn_calls:
+        attn_only(args.attn_calls, args.splits)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; --gpus must be 1 "
