@@ -429,18 +429,21 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
         cv_kg[i] = kg;
     }
     static_assert(NBLK % (4 * kNW) == 0, "whole dequantisation rounds");
-    auto convert_v = [&](const uint8_t *buf, uint8_t *vt) {
+    auto convert_read = [&](const uint8_t *buf, v2i (&ut)[NCV], f32x4 (&sv)[NCV][2]) {
         const float *fv = reinterpret_cast<const float *>(buf + L::F_OFF);
-        v2i ut[NCV];
 #pragma unroll
         for (int i = 0; i < NCV; ++i) ut[i] = lds_read_tr8(buf + cv_src[i]);
 #pragma unroll
-        for (int i = 0; i < NCV; ++i) lds_wait(ut[i]);
+        for (int i = 0; i < NCV; ++i) {
+            sv[i][0] = *reinterpret_cast<const f32x4 *>(fv + fv_index(8 * cv_kg[i]));
+            sv[i][1] = *reinterpret_cast<const f32x4 *>(fv + fv_index(8 * cv_kg[i] + 4));
+        }
+    };
+    auto convert_write = [&](const v2i (&ut)[NCV], const f32x4 (&sv)[NCV][2], uint8_t *vt) {
 #pragma unroll
         for (int i = 0; i < NCV; ++i) {
             const v2i u = ut[i];
-            const f32x4 s0 = *reinterpret_cast<const f32x4 *>(fv + fv_index(8 * cv_kg[i]));
-            const f32x4 s1 = *reinterpret_cast<const f32x4 *>(fv + fv_index(8 * cv_kg[i] + 4));
+            const f32x4 s0 = sv[i][0], s1 = sv[i][1];
             const auto x0 = __builtin_amdgcn_cvt_pk_f32_fp8(u[0], false);
             const auto x1 = __builtin_amdgcn_cvt_pk_f32_fp8(u[0], true);
             const auto x2 = __builtin_amdgcn_cvt_pk_f32_fp8(u[1], false);
@@ -476,6 +479,20 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
 
     auto half_v = [&](int t, const uint8_t *buf, const uint8_t *buf1, uint8_t *vt_next) {
         const float *fk = reinterpret_cast<const float *>(buf + L::F_OFF);
+        // every LDS read of the half-step first (K scales of tile t; FP8 V and
+        // V scales of tile t+1), one wait for all of them
+        f32x4 fkr[2][4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                fkr[kb][q] = *reinterpret_cast<const f32x4 *>(fk + fk_index(32 * kb + 16 * g + 4 * q));
+        v2i ut[NCV];
+        f32x4 sv[NCV][2];
+        convert_read(buf1, ut, sv);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < NCV; ++i) asm volatile("" : "+v"(ut[i]));
         // scores (log2 units, shifted by cofs): the accumulator times the K row
         // scale; register r of block kb is key 32kb + 16g + r of the tile
         float mx = -INFINITY;
@@ -483,7 +500,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const f32x4 f = *reinterpret_cast<const f32x4 *>(fk + fk_index(32 * kb + 16 * g + 4 * q));
+                const f32x4 f = fkr[kb][q];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float v = s[kb][4 * q + r] * f[r] + cofs;
@@ -545,10 +562,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
                 }
                 // keep the weights computed in this half-step (not sunk
                 // into the matrix half-step that consumes them)
-                asm volatile("" : "+v"(w));
                 pb[kb][ks] = __builtin_bit_cast(v8bf, w);
+                asm volatile("" : "+v"(pb[kb][ks]));
             }
-        if (t + 1 < t1) convert_v(buf1, vt_next);      // V^T of tile t+1
+        if (t + 1 < t1) convert_write(ut, sv, vt_next); // V^T of tile t+1
     };
 
     // M half-step.  PV and PREP select the parts (both in the steady state).
@@ -626,7 +643,15 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     land(-1, 1);
     lds_barrier();
     half_m(t0 - 1, tiles, vt_base, no{}, yes{});       // S^T of tile t0
-    convert_v(tiles, vt_base);                         // V^T of tile t0
+    {                                                  // V^T of tile t0
+        v2i ut[NCV];
+        f32x4 sv[NCV][2];
+        convert_read(tiles, ut, sv);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < NCV; ++i) asm volatile("" : "+v"(ut[i]));
+        convert_write(ut, sv, vt_base);
+    }
     lds_barrier();
 
     // Both groups run the same loop; the trailing group enters it one
