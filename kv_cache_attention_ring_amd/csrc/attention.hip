@@ -570,7 +570,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
 
     // M half-step.  PV and PREP select the parts (both in the steady state).
     auto half_m = [&](int t, const uint8_t *buf1, const uint8_t *vt, auto PV, auto PREP_) {
-        const bool PREP_on = decltype(PREP_)::value && t + 1 < t1;
+        constexpr bool PREP = decltype(PREP_)::value;
+        const bool PREP_on = PREP && t + 1 < t1;
         auto read_v = [&](int grp, u32x4 (&va)[ND]) {
             const int kb = grp / 2, ks = grp % 2;
 #pragma unroll
@@ -587,30 +588,42 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
                              (int)u1[0], (int)u1[1], (int)u1[2], (int)u1[3]};
             }
         };
+        v8i ka[NH][2];                                 // K operands of tile t+1
         if constexpr (decltype(PV)::value) {
-            // O^T += V^T . P^T; A-operand lane (d, g) holds keys 32kb + 16g + 8ks + 0..7
+            // O^T += V^T . P^T; A-operand lane (d, g) holds keys 32kb + 16g + 8ks + 0..7.
+            // The K operands of tile t+1 are read behind the V^T reads (reading
+            // the next buffer is harmless when there is no tile t+1).
             u32x4 va[4][ND];
 #pragma unroll
             for (int grp = 0; grp < 4; ++grp) read_v(grp, va[grp]);
+            if constexpr (PREP) {
+#pragma unroll
+                for (int h = 0; h < NH; ++h) read_k(h, ka[h]);
+            }
 #pragma unroll
             for (int grp = 0; grp < 4; ++grp)
 #pragma unroll
                 for (int d = 0; d < ND; ++d)
                     o[d] = mfma_bf16(__builtin_bit_cast(v8bf, va[grp][d]), pb[grp / 2][grp % 2], o[d]);
-            // reads run one MFMA group ahead
+            // reads run one MFMA group ahead; the K reads behind the last groups
+            constexpr int KPER = PREP ? (4 * NH + ND - 1) / ND : 0;   // K reads per last-group MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, ND, 0);
 #pragma unroll
             for (int i = 0; i < 3 * ND; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, ND, 0);
+#pragma unroll
+            for (int i = 0; i < ND; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if constexpr (KPER > 0) __builtin_amdgcn_sched_group_barrier(0x100, KPER, 0);
+            }
+        } else if constexpr (PREP) {
+#pragma unroll
+            for (int h = 0; h < NH; ++h) read_k(h, ka[h]);
         }
         if (PREP_on) {
             // S^T of tile t+1 = K . Q^T (Q hi and lo terms), both 32-key blocks
-            v8i ka[NH][2];
-#pragma unroll
-            for (int h = 0; h < NH; ++h) read_k(h, ka[h]);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) s[kb] = v16f{};
 #pragma unroll
@@ -619,14 +632,6 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
                 for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb) s[kb] = mfma(ka[h][kb], qop[h][hl], s[kb], qsc);
-            // slice-0 operands first, slice-1 reads behind the slice-0 MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4 * NH - 4, 0);
         }
     };
     using yes = std::true_type;
