@@ -20,10 +20,12 @@
 // Work decomposition.  A workgroup owns one head, a block of 256 queries and a
 // contiguous range of 64-key tiles (a "split"); each of its 8 waves (two per
 // SIMD) owns 32 queries.  Key tiles go global -> LDS with direct loads
-// (global_load_lds, 16 bytes a lane, no VGPR staging), triple buffered, one
-// barrier per tile.
-//   S^T[key][query] = K . Q^T   on v_mfma_f32_32x32x64_f8f6f4: A = FP8 K rows
-//                               from LDS, B = Q as two E4M3 terms (hi + lo)
+// (global_load_lds, 16 bytes a lane, no VGPR staging) into five buffers, four
+// tiles in flight.  The two waves of a SIMD alternate between a VALU
+// half-step and a matrix half-step (see the main loop); two LDS-only
+// barriers per tile.
+//   S^T[key][query] = K . Q^T   on v_mfma_scale_f32_32x32x64_f8f6f4: A = FP8 K
+//                               rows from LDS, B = Q as two E4M3 terms (hi + lo)
 //   O^T[d][query]  += V^T . P^T on v_mfma_f32_32x32x16_bf16: A = V^T in bf16,
 //                               B = the softmax weights in bf16
 // Each V tile is dequantised once per workgroup (E4M3 code times its row
@@ -44,11 +46,12 @@
 // core as the E8M0 scale of its B column, and softmax_scale * log2(e) is
 // folded into Q before it is split, so the accumulator holds the score in log2
 // units up to the K row scale: one FMA per score applies sk_j.  The weights
-// and V^T are bf16 (8 significant bits), so the second product needs no split.  Softmax runs in the log2 domain with a
-// lazily updated running max (rescale only when a score passes it by more
-// than 16, so weights stay below 2^16 and the fp32 sums cannot overflow).  Splits of one (head, query block) are merged by a second kernel
-// in split order, so a call is deterministic and a linear window gives the
-// same bits as the ring.
+// and V^T are bf16 (8 significant bits), so the second product needs no
+// split.  Softmax runs in the log2 domain with a lazily updated running max
+// (rescale only when a score passes it by more than 16, so weights stay below
+// 2^16 and the fp32 sums cannot overflow).  Splits of one (head, query block)
+// are merged by a second kernel in split order, so a call is deterministic and
+// a linear window gives the same bits as the ring.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -456,19 +459,21 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
 
     // ---- main loop: two wave groups in ping-pong --------------------------------
     // Per tile t a wave runs two half-steps:
-    //   V(t): scores, running max, weights p = 2^x and their sum -> bf16 B operands
-    //   M(t): O^T += V^T(t) . P^T(t); S^T(t+1) = K(t+1) . Q^T; dequantise V(t+1)
+    //   V(t): scores, running max, weights p = 2^x and their sum -> bf16 B
+    //         operands; its share of the dequantisation of V(t+1) into V^T
+    //   M(t): O^T += V^T(t) . P^T(t); S^T(t+1) = K(t+1) . Q^T
     // in the order M(t0-1) V(t0) M(t0) V(t0+1) ... M(t1-1), where M(t0-1) only
     // holds the tile-t0 parts.  Half-steps are separated by workgroup barriers,
     // and waves 4..7 run one half-step behind waves 0..3, so the two waves
     // sharing a SIMD are in different half-steps: one keeps the matrix core
     // busy while the other uses the VALU.
-    // Buffers: tile t0+k sits in tile buffer k mod kNBuf.  The lead group
-    // issues tile u+P (relative to t0) in interval 2u+1 and lands tile u+1
-    // (waits for its part of it) at the end of interval 2u, just
-    // before its first use; the last reader of a tile is the trailing group's
-    // V half-step, one interval before the buffer is reloaded.  V^T is double
-    // buffered (written in M(t-1), read in M(t)).
+    // Buffers: tile t0+k sits in tile buffer k mod kNBuf.  Each wave issues its
+    // part of tile u+P (relative to t0) after the barrier that ends its V(u),
+    // and lands (waits for) its part of tile u+2 at the end of V(u); the
+    // barrier that follows publishes it before its first use, in V(u+1) and
+    // M(u+1).  The last reader of a tile is the trailing group's V half-step,
+    // at least one interval before the buffer is reloaded.  V^T is triple
+    // buffered (below).
     v16f o[ND];
 #pragma unroll
     for (int d = 0; d < ND; ++d) o[d] = v16f{};
