@@ -29,9 +29,10 @@ HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 
 
-def counted_traffic():
-    """HBM bytes per attention call from the committed counter summary, or None
-    when the attention source has changed since the counters were taken."""
+def counted_traffic(key="attn_kernel_traffic_bytes"):
+    """HBM bytes per launch from the committed counter summary (the attention
+    kernel's by default, or `attn_call_traffic_bytes` for the whole call), or
+    None when the attention source has changed since the counters were taken."""
     import hashlib
     import re
     prof = os.path.join(ROOT, "profiles", "attn_traffic_counters.md")
@@ -42,7 +43,7 @@ def counted_traffic():
     except OSError:
         return None
     m = re.search(r"attention\.hip sha256: ([0-9a-f]{64})", text)
-    t = re.search(r"attn_call_traffic_bytes: (\d+)", text)
+    t = re.search(key + r": (\d+)", text)
     if not m or not t or m.group(1) != digest:
         return None
     return int(t.group(1))
@@ -218,6 +219,31 @@ def main():
         f"{pct(per_step, 50):.4f}, p90 {pct(per_step, 90):.4f}, max {per_step[-1]:.4f}")
 
     # ---- per-kernel times, measured with events on the launch stream -----------
+    # (1) every launch of one kind back to back between two events: the average
+    #     launch duration of the attention kernel alone (the call's first launch,
+    #     attn_fp8_window_partial), of the split merge alone, and of whole calls;
+    # (2) one event pair around each whole call, for the per-call percentiles.
+    def batch_ms(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start = K.kvr_ring_logical_start(ring, W)
+        e0.record()
+        for p in range(P):
+            for layer in range(L):
+                fn(layer, p, start)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (P * L)
+
+    def partial(layer, p, start):
+        K.attn_fp8_window_partial(cache, layer, start, ring.n_valid, qpool[p * L + layer], ring.pos_next - N,
+                                  rope.base, out=outs[layer], n_splits=args.splits, ws=ws)
+
+    def merge(layer, p, start):
+        K.attn_fp8_window_merge(cache, N, ring.n_valid, outs[layer], n_splits=args.splits, ws=ws)
+
+    kern_ms = sum(batch_ms(partial) for _ in range(2)) / 2
+    merge_ms = sum(batch_ms(merge) for _ in range(2)) / 2
+    call_batch_ms = sum(batch_ms(attend) for _ in range(2)) / 2
     n_meas = 2
     w_ms, a_ms = [], []
     for _ in range(n_meas):
@@ -238,14 +264,16 @@ def main():
         w_ms.append(e[0].elapsed_time(e[1]))
         a_ms += [e[j].elapsed_time(e[j + 1]) for j in range(2, len(e), 2)]
     write_ms = sum(w_ms) / len(w_ms)
-    attn_ms = sum(a_ms) / len(a_ms)
+    attn_ms = call_batch_ms
     a_sorted = sorted(a_ms)
     attn_flops = 4.0 * N * W * H * D
     attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
+    kern_tflops = attn_flops / (kern_ms * 1e-3) / 1e12
     write_bytes = L * (2 * N * H * D * 2 + 2 * N * H * D + 2 * N * H * 4)
     write_gbs = write_bytes / (write_ms * 1e-3) / 1e9
     log(f"write (60 layers) {write_ms * 1e3:.1f} us = {write_gbs:.0f} GB/s; attention call "
-        f"{attn_ms * 1e3:.2f} us = {attn_tflops:.1f} TFLOP/s")
+        f"{attn_ms * 1e3:.2f} us = {attn_tflops:.1f} TFLOP/s (kernel {kern_ms * 1e3:.2f} us = "
+        f"{kern_tflops:.1f} TFLOP/s, merge {merge_ms * 1e3:.2f} us)")
 
     # ---- rebase (position reset) -------------------------------------------------
     delta = inputs.rebase_delta()
@@ -293,12 +321,12 @@ def main():
             "attention_splits": args.splits or "default",
         },
         "roofline": {
-            "kernel": "attn_fp8_window (attention + split combine), per call",
+            "kernel": "attn_kernel<128, bf16 Q> (attn_fp8_window_partial), per launch",
             "bound": "mfma",
-            "achieved": round(attn_tflops, 2),
+            "achieved": round(kern_tflops, 2),
             "peak": FP8_PEAK_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4),
+            "frac": round(kern_tflops / FP8_PEAK_TFLOPS, 4),
             "traffic": counted_traffic(),
         },
         "step_ms": {"mean": round(ms_step, 5), "median": round(pct(per_step, 50), 5),
@@ -308,8 +336,12 @@ def main():
             "write_GBps": round(write_gbs, 1),
             "write_frac_hbm": round(write_gbs / HBM_PEAK_GBS, 4),
             "attention_call_us": round(attn_ms * 1e3, 3),
-            "attention_call_us_median": round(pct(a_sorted, 50) * 1e3, 3),
-            "attention_call_us_p90": round(pct(a_sorted, 90) * 1e3, 3),
+            "attention_call_TFLOPs": round(attn_tflops, 2),
+            "attention_kernel_us": round(kern_ms * 1e3, 3),
+            "attention_merge_us": round(merge_ms * 1e3, 3),
+            "attention_call_traffic_bytes": counted_traffic("attn_call_traffic_bytes"),
+            "attention_call_us_median_single": round(pct(a_sorted, 50) * 1e3, 3),
+            "attention_call_us_p90_single": round(pct(a_sorted, 90) * 1e3, 3),
             "upkeep_share_of_step": round(write_ms / ms_step, 4),
             "attention_ms_per_step": round(attn_ms * P * L, 4),
             "rebase_ms": round(reb_ms, 4),

@@ -169,6 +169,19 @@ int32_t attn_fp8_window(const kvr_cache *cache, int32_t layer, int32_t slot_star
                         int64_t q_pos_start, float softmax_scale, double rope_base,
                         uint16_t *out, int32_t n_splits, void *ws, size_t ws_bytes,
                         void *stream);
+/* The two launches of attn_fp8_window, callable one by one (same arguments,
+ * same validation and errors): _partial runs the attention kernel, which
+ * writes `out` itself when the effective split count is 1 and the split
+ * partials to `ws` otherwise; _merge then combines the partials into `out`
+ * (it launches nothing for one split).  attn_fp8_window == _partial followed
+ * by _merge on the same stream, bit for bit.  [AI-cache] [AI-latency] */
+int32_t attn_fp8_window_partial(const kvr_cache *cache, int32_t layer, int32_t slot_start,
+                                int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
+                                int64_t q_pos_start, float softmax_scale, double rope_base,
+                                uint16_t *out, int32_t n_splits, void *ws, size_t ws_bytes,
+                                void *stream);
+int32_t attn_fp8_window_merge(const kvr_cache *cache, int32_t n_q, int32_t n_valid, int32_t n_splits,
+                              uint16_t *out, void *ws, size_t ws_bytes, void *stream);
 
 /* ---- (a5) naive per-call upkeep (the original implementation) ------------
  * [WC] [AI-cache] [NC-cache].  Shift the linear, un-rotated window: the new

@@ -832,26 +832,31 @@ size_t attn_workspace_bytes(int n_heads, int head_dim, int n_q, int n_splits) {
     return o_bytes + rows * 2 * sizeof(float);
 }
 
-template <int D, bool BF16>
-static void launch_attn_d(const AttnArgs &a, int grid, int64_t rows, hipStream_t s) {
-    hipLaunchKernelGGL((attn_kernel<D, BF16>), dim3(grid), dim3(kThreads), Lds<D>::TOTAL, s, a);
+template <int D>
+static void launch_merge_d(const AttnArgs &a, hipStream_t s) {
     constexpr int RPB = 256 / (D / 8);               // rows per combine workgroup
-    if (a.n_splits > 1)
-        hipLaunchKernelGGL(combine_kernel<D>, dim3((rows + RPB - 1) / RPB), dim3(256), 0, s, a);
+    const int64_t rows = (int64_t)a.n_q * a.n_heads;
+    hipLaunchKernelGGL(combine_kernel<D>, dim3((rows + RPB - 1) / RPB), dim3(256), 0, s, a);
 }
 
-hipError_t launch_attention(const AttnArgs &a, int head_dim, hipStream_t s) {
+hipError_t launch_attention_main(const AttnArgs &a, int head_dim, hipStream_t s) {
     const int n_qb = (a.n_q + kQB - 1) / kQB;
-    const int grid = n_qb * a.n_heads * a.n_splits;
-    const int64_t rows = (int64_t)a.n_q * a.n_heads;
+    const dim3 grid(n_qb * a.n_heads * a.n_splits), block(kThreads);
     const bool bf16 = a.dtype == KVR_BF16;
     if (head_dim == 128) {
-        if (bf16) launch_attn_d<128, true>(a, grid, rows, s);
-        else launch_attn_d<128, false>(a, grid, rows, s);
+        if (bf16) hipLaunchKernelGGL((attn_kernel<128, true>), grid, block, Lds<128>::TOTAL, s, a);
+        else hipLaunchKernelGGL((attn_kernel<128, false>), grid, block, Lds<128>::TOTAL, s, a);
     } else {
-        if (bf16) launch_attn_d<64, true>(a, grid, rows, s);
-        else launch_attn_d<64, false>(a, grid, rows, s);
+        if (bf16) hipLaunchKernelGGL((attn_kernel<64, true>), grid, block, Lds<64>::TOTAL, s, a);
+        else hipLaunchKernelGGL((attn_kernel<64, false>), grid, block, Lds<64>::TOTAL, s, a);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_attention_merge(const AttnArgs &a, int head_dim, hipStream_t s) {
+    if (a.n_splits <= 1) return hipSuccess;
+    if (head_dim == 128) launch_merge_d<128>(a, s);
+    else launch_merge_d<64>(a, s);
     return hipGetLastError();
 }
 

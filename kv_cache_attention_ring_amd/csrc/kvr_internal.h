@@ -69,6 +69,9 @@ struct AttnArgs {
 };
 int attn_default_splits(int n_heads, int n_q, int n_valid);
 size_t attn_workspace_bytes(int n_heads, int head_dim, int n_q, int n_splits);
-hipError_t launch_attention(const AttnArgs &a, int head_dim, hipStream_t s);
+// the attention kernel (output rows when n_splits == 1, split partials else)
+hipError_t launch_attention_main(const AttnArgs &a, int head_dim, hipStream_t s);
+// the merge of the split partials into the output rows (nothing for one split)
+hipError_t launch_attention_merge(const AttnArgs &a, int head_dim, hipStream_t s);
 
 }  // namespace kvr

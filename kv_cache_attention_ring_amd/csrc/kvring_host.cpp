@@ -252,11 +252,31 @@ size_t attn_fp8_window_workspace_bytes(const kvr_cache *cache, int32_t n_q, int3
     return kvr::attn_workspace_bytes(cache->n_heads, cache->head_dim, n_q, n_splits);
 }
 
-int32_t attn_fp8_window(const kvr_cache *cache, int32_t layer, int32_t slot_start,
-                        int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
-                        int64_t q_pos_start, float softmax_scale, double rope_base,
-                        uint16_t *out, int32_t n_splits, void *ws, size_t ws_bytes,
-                        void *stream) {
+namespace {
+
+// Workspace of a call with n_splits > 1: fp16 partial rows, then (max, sum).
+int32_t check_workspace(size_t need, const void *ws, size_t ws_bytes) {
+    if (need == 0) return KVR_OK;
+    if (!ws) return fail(KVR_EINVAL, "workspace of %zu bytes required", need);
+    if (ws_bytes < need) return fail(KVR_EINVAL, "workspace %zu < %zu bytes", ws_bytes, need);
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+        return fail(KVR_EALIGN, "workspace must be 256-byte aligned");
+    return KVR_OK;
+}
+
+void set_partials(kvr::AttnArgs &a, void *ws, int32_t n_heads, int32_t D, int32_t n_q, int32_t n_splits) {
+    if (n_splits <= 1) return;
+    const size_t rows = (size_t)n_splits * n_q * n_heads;
+    const size_t o_bytes = (rows * D * sizeof(uint16_t) + 255) / 256 * 256;
+    a.part_o = static_cast<uint16_t *>(ws);
+    a.part_ml = reinterpret_cast<float *>(static_cast<char *>(ws) + o_bytes);
+}
+
+// Validation and kernel arguments shared by attn_fp8_window and its two parts.
+int32_t attn_setup(kvr::AttnArgs &a, const kvr_cache *cache, int32_t layer, int32_t slot_start,
+                   int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
+                   int64_t q_pos_start, float softmax_scale, double rope_base, uint16_t *out,
+                   int32_t n_splits, void *ws, size_t ws_bytes) {
     if (int32_t e = check_cache(cache)) return e;
     const int32_t W = cache->window, D = cache->head_dim;
     if (int32_t e = check_dtype(dtype)) return e;
@@ -274,14 +294,9 @@ int32_t attn_fp8_window(const kvr_cache *cache, int32_t layer, int32_t slot_star
     if (n_splits < 0) return fail(KVR_EINVAL, "n_splits %d < 0", n_splits);
     int32_t tps;
     n_splits = effective_splits(cache->n_heads, n_q, n_valid, n_splits, &tps);
-    const size_t need = kvr::attn_workspace_bytes(cache->n_heads, D, n_q, n_splits);
-    if (need > 0) {
-        if (!ws) return fail(KVR_EINVAL, "workspace of %zu bytes required", need);
-        if (ws_bytes < need) return fail(KVR_EINVAL, "workspace %zu < %zu bytes", ws_bytes, need);
-        if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
-            return fail(KVR_EALIGN, "workspace must be 256-byte aligned");
-    }
-    kvr::AttnArgs a{};
+    if (int32_t e = check_workspace(kvr::attn_workspace_bytes(cache->n_heads, D, n_q, n_splits), ws, ws_bytes))
+        return e;
+    a = kvr::AttnArgs{};
     const int64_t lay = (int64_t)layer * cache->n_heads * W;
     a.k_codes = cache->k_codes + lay * D;
     a.v_codes = cache->v_codes + lay * D;
@@ -302,13 +317,73 @@ int32_t attn_fp8_window(const kvr_cache *cache, int32_t layer, int32_t slot_star
     a.n_splits = n_splits;
     a.tiles_per_split = tps;
     a.softmax_scale = softmax_scale;
-    if (n_splits > 1) {
-        const size_t rows = (size_t)n_splits * n_q * cache->n_heads;
-        const size_t o_bytes = (rows * D * sizeof(uint16_t) + 255) / 256 * 256;
-        a.part_o = static_cast<uint16_t *>(ws);
-        a.part_ml = reinterpret_cast<float *>(static_cast<char *>(ws) + o_bytes);
-    }
-    return launch_status(kvr::launch_attention(a, D, static_cast<hipStream_t>(stream)), "attention");
+    set_partials(a, ws, cache->n_heads, D, n_q, n_splits);
+    return KVR_OK;
+}
+
+// Validation and kernel arguments of the merge alone: the partials' layout
+// follows from the cache shape, n_q and the effective split count.
+int32_t merge_setup(kvr::AttnArgs &a, const kvr_cache *cache, int32_t n_q, int32_t n_valid,
+                    int32_t n_splits, uint16_t *out, void *ws, size_t ws_bytes) {
+    if (int32_t e = check_cache(cache)) return e;
+    const int32_t W = cache->window, D = cache->head_dim;
+    if (n_valid < 1 || n_valid > W) return fail(KVR_EINVAL, "n_valid %d not in [1,%d]", n_valid, W);
+    if (n_q < 1 || n_q >= kMaxExtent) return fail(KVR_EINVAL, "n_q %d out of range", n_q);
+    if (!out) return fail(KVR_EINVAL, "out is NULL");
+    if (!aligned16(out)) return fail(KVR_EALIGN, "out not 16-byte aligned");
+    if (n_splits < 0) return fail(KVR_EINVAL, "n_splits %d < 0", n_splits);
+    int32_t tps;
+    n_splits = effective_splits(cache->n_heads, n_q, n_valid, n_splits, &tps);
+    a = kvr::AttnArgs{};
+    a.out = out;
+    a.n_heads = cache->n_heads;
+    a.window = W;
+    a.n_valid = n_valid;
+    a.n_q = n_q;
+    a.n_splits = n_splits;
+    a.tiles_per_split = tps;
+    if (int32_t e = check_workspace(kvr::attn_workspace_bytes(cache->n_heads, D, n_q, n_splits), ws, ws_bytes))
+        return e;
+    set_partials(a, ws, cache->n_heads, D, n_q, n_splits);
+    return KVR_OK;
+}
+
+}  // namespace
+
+int32_t attn_fp8_window(const kvr_cache *cache, int32_t layer, int32_t slot_start,
+                        int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
+                        int64_t q_pos_start, float softmax_scale, double rope_base,
+                        uint16_t *out, int32_t n_splits, void *ws, size_t ws_bytes,
+                        void *stream) {
+    kvr::AttnArgs a;
+    if (int32_t e = attn_setup(a, cache, layer, slot_start, n_valid, q, dtype, n_q, q_pos_start,
+                               softmax_scale, rope_base, out, n_splits, ws, ws_bytes))
+        return e;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (int32_t e = launch_status(kvr::launch_attention_main(a, cache->head_dim, s), "attention"))
+        return e;
+    return launch_status(kvr::launch_attention_merge(a, cache->head_dim, s), "attention merge");
+}
+
+int32_t attn_fp8_window_partial(const kvr_cache *cache, int32_t layer, int32_t slot_start,
+                                int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
+                                int64_t q_pos_start, float softmax_scale, double rope_base,
+                                uint16_t *out, int32_t n_splits, void *ws, size_t ws_bytes,
+                                void *stream) {
+    kvr::AttnArgs a;
+    if (int32_t e = attn_setup(a, cache, layer, slot_start, n_valid, q, dtype, n_q, q_pos_start,
+                               softmax_scale, rope_base, out, n_splits, ws, ws_bytes))
+        return e;
+    return launch_status(kvr::launch_attention_main(a, cache->head_dim, static_cast<hipStream_t>(stream)),
+                         "attention");
+}
+
+int32_t attn_fp8_window_merge(const kvr_cache *cache, int32_t n_q, int32_t n_valid, int32_t n_splits,
+                              uint16_t *out, void *ws, size_t ws_bytes, void *stream) {
+    kvr::AttnArgs a;
+    if (int32_t e = merge_setup(a, cache, n_q, n_valid, n_splits, out, ws, ws_bytes)) return e;
+    return launch_status(kvr::launch_attention_merge(a, cache->head_dim, static_cast<hipStream_t>(stream)),
+                         "attention merge");
 }
 
 // ---- (a5) naive per-call upkeep -------------------------------------------

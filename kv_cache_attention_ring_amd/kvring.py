@@ -68,6 +68,9 @@ _SIGS = {
     "attn_fp8_window_workspace_bytes": (_SZ, [ctypes.POINTER(kvr_cache), _I32, _I32, _I32]),
     "attn_fp8_window": (_I32, [ctypes.POINTER(kvr_cache), _I32, _I32, _I32, _P, _I32, _I32, _I64,
                                _F32, _F64, _P, _I32, _P, _SZ, _P]),
+    "attn_fp8_window_partial": (_I32, [ctypes.POINTER(kvr_cache), _I32, _I32, _I32, _P, _I32, _I32, _I64,
+                                       _F32, _F64, _P, _I32, _P, _SZ, _P]),
+    "attn_fp8_window_merge": (_I32, [ctypes.POINTER(kvr_cache), _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "naive_upkeep": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32,
                             ctypes.POINTER(kvr_rope_table), _P, _P, _P, _P, _P, _P, _P]),
     "kvr_last_error": (ctypes.c_char_p, []),
@@ -224,11 +227,8 @@ def attn_fp8_window_workspace_bytes(cache: KVCache, n_q: int, n_valid: int, n_sp
     return int(lib().attn_fp8_window_workspace_bytes(ctypes.byref(c), n_q, n_valid, n_splits))
 
 
-def attn_fp8_window(cache: KVCache, layer: int, slot_start: int, n_valid: int, q: torch.Tensor,
-                    q_pos_start: int, rope_base: float = 10000.0, out: torch.Tensor | None = None,
-                    n_splits: int = 0, ws: torch.Tensor | None = None,
-                    softmax_scale: float | None = None, stream=None) -> torch.Tensor:
-    """q: [n_q][H][D] bf16/fp32 -> out: [n_q][H][D] bf16."""
+def _attn_args(cache: KVCache, layer: int, slot_start: int, n_valid: int, q: torch.Tensor,
+               q_pos_start: int, rope_base: float, out, n_splits: int, ws, softmax_scale, stream):
     n_q = q.shape[0]
     if q.dim() != 3 or q.shape[1:] != (cache.n_heads, cache.head_dim):
         raise KVRError(KVR_EINVAL, f"q shape {tuple(q.shape)} does not match the cache")
@@ -244,10 +244,43 @@ def attn_fp8_window(cache: KVCache, layer: int, slot_start: int, n_valid: int, q
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(cache.head_dim)
     c = cache.desc()
-    _check(lib().attn_fp8_window(ctypes.byref(c), layer, slot_start, n_valid, _dev(q, "q"),
-                                 _dtype_code(q), n_q, int(q_pos_start), float(softmax_scale),
-                                 float(rope_base), _dev(out, "out"), int(n_splits), ws_ptr, ws_len,
-                                 _stream(stream)))
+    args = (ctypes.byref(c), layer, slot_start, n_valid, _dev(q, "q"), _dtype_code(q), n_q,
+            int(q_pos_start), float(softmax_scale), float(rope_base), _dev(out, "out"), int(n_splits),
+            ws_ptr, ws_len, _stream(stream))
+    return args, out, ws, c
+
+
+def attn_fp8_window(cache: KVCache, layer: int, slot_start: int, n_valid: int, q: torch.Tensor,
+                    q_pos_start: int, rope_base: float = 10000.0, out: torch.Tensor | None = None,
+                    n_splits: int = 0, ws: torch.Tensor | None = None,
+                    softmax_scale: float | None = None, stream=None) -> torch.Tensor:
+    """q: [n_q][H][D] bf16/fp32 -> out: [n_q][H][D] bf16."""
+    args, out, _, _c = _attn_args(cache, layer, slot_start, n_valid, q, q_pos_start, rope_base, out,
+                                  n_splits, ws, softmax_scale, stream)
+    _check(lib().attn_fp8_window(*args))
+    return out
+
+
+def attn_fp8_window_partial(cache: KVCache, layer: int, slot_start: int, n_valid: int, q: torch.Tensor,
+                            q_pos_start: int, rope_base: float = 10000.0, out: torch.Tensor | None = None,
+                            n_splits: int = 0, ws: torch.Tensor | None = None,
+                            softmax_scale: float | None = None, stream=None):
+    """The attention kernel alone: out for one split, partials in ws otherwise.
+    Returns (out, ws) for attn_fp8_window_merge."""
+    args, out, ws, _c = _attn_args(cache, layer, slot_start, n_valid, q, q_pos_start, rope_base, out,
+                                   n_splits, ws, softmax_scale, stream)
+    _check(lib().attn_fp8_window_partial(*args))
+    return out, ws
+
+
+def attn_fp8_window_merge(cache: KVCache, n_q: int, n_valid: int, out: torch.Tensor,
+                          n_splits: int = 0, ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Merge the split partials in ws into out (nothing to do for one split)."""
+    c = cache.desc()
+    ws_ptr = _dev(ws, "ws") if ws is not None else None
+    ws_len = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(lib().attn_fp8_window_merge(ctypes.byref(c), n_q, n_valid, int(n_splits), _dev(out, "out"),
+                                       ws_ptr, ws_len, _stream(stream)))
     return out
 
 

@@ -165,6 +165,35 @@ def test_attention_validation():
     assert _attn(_cache(D=256), 5788) == K.KVR_EUNSUPPORTED
 
 
+@no_gpu
+def test_attention_parts_validation():
+    """The two halves of the call validate like the call itself."""
+    c = _cache()
+    lib = K.lib()
+    part = lambda **kw: lib.attn_fp8_window_partial(
+        ctypes.byref(c), 0, kw.get("start", 0), kw.get("n_valid", 5788), FAKE + 0x7000000, K.KVR_BF16, 757, 0,
+        0.088, 10000.0, kw.get("out", FAKE + 0x8000000), kw.get("splits", 1), kw.get("ws", None),
+        kw.get("ws_bytes", 0), None)
+    assert part(n_valid=0) == K.KVR_EINVAL
+    assert part(start=5788) == K.KVR_EINVAL
+    assert part(splits=4) == K.KVR_EINVAL                       # workspace required
+    assert part(out=FAKE + 0x8000002) == K.KVR_EALIGN
+    merge = lambda **kw: lib.attn_fp8_window_merge(
+        ctypes.byref(c), kw.get("n_q", 757), kw.get("n_valid", 5788), kw.get("splits", 4),
+        kw.get("out", FAKE + 0x8000000), kw.get("ws", None), kw.get("ws_bytes", 0), None)
+    need = lib.attn_fp8_window_workspace_bytes(ctypes.byref(c), 757, 5788, 4)
+    assert merge() == K.KVR_EINVAL                              # workspace required
+    assert merge(ws=FAKE + 0x9000000, ws_bytes=need - 1) == K.KVR_EINVAL
+    assert merge(ws=FAKE + 0x9000010, ws_bytes=need) == K.KVR_EALIGN
+    assert merge(out=FAKE + 0x8000004, ws=FAKE + 0x9000000, ws_bytes=need) == K.KVR_EALIGN
+    assert merge(n_valid=0) == K.KVR_EINVAL
+    assert merge(n_q=0) == K.KVR_EINVAL
+    assert merge(splits=-1) == K.KVR_EINVAL
+    assert lib.attn_fp8_window_merge(None, 757, 5788, 4, FAKE, None, 0, None) == K.KVR_EINVAL
+    # one split: nothing to merge, no workspace needed
+    assert merge(splits=1) == K.KVR_OK
+
+
 def _ws_bytes(rows, D):
     # fp16 normalised partial rows (padded to 256 bytes) + fp32 (max, sum) per row
     return (rows * D * 2 + 255) // 256 * 256 + rows * 2 * 4

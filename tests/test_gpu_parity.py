@@ -329,6 +329,28 @@ def test_split_merge_shares_one_workspace():
         assert_attention(got, ref, f"shared workspace call {i}")
 
 
+def test_partial_then_merge_equals_the_call():
+    """attn_fp8_window_partial followed by attn_fp8_window_merge gives the
+    same bits as attn_fp8_window, for one split, several and the default."""
+    shp = inputs.Shape("test", 1, 3, 128, 1100, 600)
+    run = SmallRun(shp, dtype=torch.bfloat16)
+    for step in range(2):
+        k, v = inputs.np_chunk(shp, step)
+        run.step(k, v)
+    W = shp.window
+    start = K.kvr_ring_logical_start(run.ring, W)
+    for i, (n_q, splits) in enumerate([(600, 1), (600, 3), (513, 0), (1, 5)]):
+        _say(f"partial + merge {i}: n_q {n_q}, splits {splits}")
+        q = torch.from_numpy(inputs.np_queries(shp, 1, i)[:n_q]).to(torch.bfloat16).cuda()
+        qpos = run.ring.pos_next - n_q
+        whole = K.attn_fp8_window(run.cache, 0, start, run.ring.n_valid, q, qpos, run.rope.base, n_splits=splits)
+        out, ws = K.attn_fp8_window_partial(run.cache, 0, start, run.ring.n_valid, q, qpos, run.rope.base,
+                                            n_splits=splits)
+        K.attn_fp8_window_merge(run.cache, n_q, run.ring.n_valid, out, n_splits=splits, ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(whole, out), i
+
+
 def test_bf16_ragged_queries_head_dim_64():
     shp = inputs.Shape("test", 1, 4, 64, 1000, 161)
     run = SmallRun(shp, dtype=torch.bfloat16)
