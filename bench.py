@@ -65,6 +65,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=42)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--naive-steps", type=int, default=3)
+    ap.add_argument("--every-pass-steps", type=int, default=5,
+                    help="steps timed with the chunk written again on every denoise pass (0 = skip)")
     ap.add_argument("--rebase-iters", type=int, default=20)
     ap.add_argument("--splits", type=int, default=0, help="attention key splits (0 = default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -159,7 +161,7 @@ def main():
     shp = inputs.PAGE_STEP
     L, H, D, W, N, P = shp.n_layers, shp.n_heads, shp.head_dim, shp.window, shp.n_new, shp.passes
     pre = 8
-    total_steps = pre + args.warmup + args.steps + 2
+    total_steps = pre + args.warmup + args.steps + 2 + (args.every_pass_steps + 1 if args.every_pass_steps > 0 else 0)
     pos_lo = -inputs.DELTA_MAX - 8 * N
     rope = K.RopeTable(pos_lo, total_steps * N - pos_lo, D, device=dev)
     cache = K.KVCache(L, H, D, W, device=dev)
@@ -217,6 +219,36 @@ def main():
     per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     log(f"{args.steps} steps: {ms_step:.4f} ms/step (wall {wall_ms / args.steps:.4f}); median "
         f"{pct(per_step, 50):.4f}, p90 {pct(per_step, 90):.4f}, max {per_step[-1]:.4f}")
+
+    # ---- the chunk written on every denoise pass ------------------------------
+    # each pass brings new K/V rows for the step's chunk: they are written to
+    # the same slots at the same positions (ring state of the step's start)
+    # before that pass's 60 calls; the ring advances once per step
+    every_pass = None
+    if args.every_pass_steps > 0:
+        def step_every_pass(step_idx):
+            before = ring.copy()
+            K.kvr_ring_after_write(ring, W, N)
+            start = K.kvr_ring_logical_start(ring, W)
+            for p in range(P):
+                k, v = chunks[(step_idx + p) % pool]
+                K.kv_write_rope_quant(cache, before, 0, k, v, rope)
+                for layer in range(L):
+                    attend(layer, p, start)
+        step_every_pass(sidx)
+        sidx += 1
+        torch.cuda.synchronize()
+        q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        q0.record()
+        for _ in range(args.every_pass_steps):
+            step_every_pass(sidx)
+            sidx += 1
+        q1.record()
+        torch.cuda.synchronize()
+        ep_ms = q0.elapsed_time(q1) / args.every_pass_steps
+        every_pass = {"ms_per_step": round(ep_ms, 5), "steps": args.every_pass_steps,
+                      "writes_per_step": P, "upkeep_bytes_per_step": P * L * (2 * N * H * D * 2 + 2 * N * H * D + 2 * N * H * 4)}
+        log(f"write on every pass: {ep_ms:.4f} ms/step ({P} writes of 60 layers per step)")
 
     # ---- per-kernel times, measured with events on the launch stream -----------
     # (1) every launch of one kind back to back between two events: the average
@@ -350,6 +382,7 @@ def main():
             "rebase_delta": delta,
         },
         "naive": naive,
+        "write_every_pass": every_pass,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

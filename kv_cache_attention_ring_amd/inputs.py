@@ -70,12 +70,13 @@ def torch_seed(workload: str, step: int = 0, layer: int = 0, pss: int = 0, tenso
 # ---------------------------------------------------------------------------
 # fp32 NumPy inputs (small shapes)
 # ---------------------------------------------------------------------------
-def np_chunk(shape: Shape, step: int, layer: int = 0, workload: str | None = None):
-    """New K, V rows of one chunk: fp32 [N][H][D] ~ N(0, 1)."""
+def np_chunk(shape: Shape, step: int, layer: int = 0, workload: str | None = None, pss: int = 0):
+    """New K, V rows of one chunk: fp32 [N][H][D] ~ N(0, 1).  `pss` > 0 draws
+    the rows of a later denoise pass of the same step (pass 0 is the default)."""
     w = workload or shape.name
     sz = (shape.n_new, shape.n_heads, shape.head_dim)
-    k = np_rng(w, step, layer, 0, "k").standard_normal(sz, dtype=np.float32)
-    v = np_rng(w, step, layer, 0, "v").standard_normal(sz, dtype=np.float32)
+    k = np_rng(w, step, layer, pss, "k").standard_normal(sz, dtype=np.float32)
+    v = np_rng(w, step, layer, pss, "v").standard_normal(sz, dtype=np.float32)
     return k, v
 
 
@@ -98,8 +99,9 @@ def head_scales(shape: Shape, layer: int, workload: str | None = None):
 
 
 def torch_chunk(shape: Shape, step: int, layer: int, device, dtype=None, workload: str | None = None,
-                n_layers: int = 1):
-    """New K, V rows: [n_layers][N][H][D] in dtype (bf16 default), scaled per head."""
+                n_layers: int = 1, pss: int = 0):
+    """New K, V rows: [n_layers][N][H][D] in dtype (bf16 default), scaled per head.
+    `pss` > 0 draws the rows of a later denoise pass of the same step."""
     import torch
     dtype = dtype or torch.bfloat16
     w = workload or shape.name
@@ -110,7 +112,7 @@ def torch_chunk(shape: Shape, step: int, layer: int, device, dtype=None, workloa
         out = []
         for t, s in (("k", sk), ("v", sv)):
             g = torch.Generator(device=device)
-            g.manual_seed(torch_seed(w, step, li, 0, t))
+            g.manual_seed(torch_seed(w, step, li, pss, t))
             x = torch.randn(sz, generator=g, device=device, dtype=torch.float32)
             x = x * torch.as_tensor(s, device=device).view(1, -1, 1)
             out.append(x.to(dtype))

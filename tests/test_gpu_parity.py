@@ -162,6 +162,15 @@ class SmallRun:
         K.kvr_ring_after_write(self.ring, s.window, k.shape[0])
         self.total += k.shape[0]
 
+    def write_pass(self, k, v, before, total_before):
+        """Write a chunk again from the step-start ring state `before` (the
+        same slots and positions as that step's first write); the ring path
+        and the oracle only."""
+        kd = torch.from_numpy(k).to(self.dtype).cuda()
+        vd = torch.from_numpy(v).to(self.dtype).cuda()
+        K.kv_write_rope_quant(self.cache, before, 0, kd, vd, self.rope)
+        oracle.write(self.orc, total_before, before.pos_next, _f32(kd), _f32(vd))
+
     def rebase(self, delta):
         start = K.kvr_ring_logical_start(self.ring, self.s.window)
         K.kv_delta_rebase(self.cache, self.ring, 0, 1, delta)
@@ -308,6 +317,30 @@ def test_fp32_inputs_head_dim_128():
         run.check_cache(f"fp32 D128 step {step}")
         got, ref = run.attention(inputs.np_queries(shp, step, 0), n_splits=(step % 3) + 1)
         assert_attention(got, ref, f"fp32 D128 step {step}")
+
+
+def test_write_on_every_pass():
+    """Each denoise pass brings new K/V for the step's chunk: they are written
+    again, to the same slots at the same positions (the ring advances once per
+    step), before that pass's attention.  After every pass the cache equals
+    the oracle's and attention matches it; the window wraps mid-chunk."""
+    shp = inputs.Shape("test", 1, 3, 128, 300, 70)
+    run = SmallRun(shp, dtype=torch.bfloat16)
+    W, N = shp.window, shp.n_new
+    for step in range(6):
+        before = K.kvr_ring(run.ring.head, run.ring.n_valid, run.ring.pos_next)
+        total_before = run.total
+        after = K.kvr_ring(before.head, before.n_valid, before.pos_next)
+        K.kvr_ring_after_write(after, W, N)
+        for p in range(shp.passes):
+            _say(f"write every pass: step {step} pass {p}")
+            k, v = inputs.np_chunk(shp, step, pss=p)
+            run.write_pass(k, v, before, total_before)
+            run.ring = K.kvr_ring(after.head, after.n_valid, after.pos_next)
+            run.check_cache(f"step {step} pass {p}", naive_too=False)
+            got, ref = run.attention(inputs.np_queries(shp, step, p), naive_too=False)
+            assert_attention(got, ref, f"write every pass: step {step} pass {p}")
+        run.total = total_before + N
 
 
 def test_split_merge_shares_one_workspace():
