@@ -28,6 +28,9 @@
 namespace kvr {
 namespace {
 
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+
 constexpr int kRowLanes = 8;          // lanes per row
 constexpr int kBlock = 256;           // threads per workgroup
 constexpr int kRowsPerIter = kBlock / kRowLanes;
@@ -117,12 +120,14 @@ __device__ __forceinline__ void quantize_store(const float (&y)[EPT], uint8_t *c
             w[k] = (uint32_t)pk;
         }
     }
+    // codes and scales are written once and not read again by this launch:
+    // nontemporal stores
     if constexpr (EPT == 16) {
-        *reinterpret_cast<uint4 *>(codes_dst) = make_uint4(w[0], w[1], w[2], w[3]);
+        __builtin_nontemporal_store(u32x4v{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4v *>(codes_dst));
     } else {
-        *reinterpret_cast<uint2 *>(codes_dst) = make_uint2(w[0], w[1]);
+        __builtin_nontemporal_store(u32x2v{w[0], w[1]}, reinterpret_cast<u32x2v *>(codes_dst));
     }
-    if (lane0) *scale_dst = scale;
+    if (lane0) __builtin_nontemporal_store(scale, scale_dst);
 }
 
 // ---------------------------------------------------------------------------
