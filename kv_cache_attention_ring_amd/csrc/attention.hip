@@ -105,14 +105,33 @@ struct Lds {
     static_assert(TOTAL <= 160 * 1024, "LDS budget");
 };
 
-// Chunk swizzles: K rows are gathered 8 at a time in the pattern
-// {0..3, 16..19} + 4k, V rows are read 8 consecutive rows at a time.
-__device__ __forceinline__ int swz_k(int row) { return row + 4 * (row >> 4); }
-__device__ __forceinline__ int swz_v(int row) { return row; }
-// V^T rows (one per d, 8 chunks of 8 keys): chunk c of row d sits at
-// c ^ ((d >> 1) & 7), so 16 consecutive rows hit 16 distinct 16-byte bank
-// groups for both the transposing writes and the MFMA operand reads.
-__device__ __forceinline__ int vt_pos(int d, int c) { return d * (2 * kKT) + 16 * (c ^ ((d >> 1) & 7)); }
+// LDS bank groups.  A 16-byte-per-lane read is served 16 consecutive lanes at
+// a time over a 256-byte span (16 bank groups of 16 bytes), a 16-byte write 8
+// lanes at a time over 128 bytes, the 8-byte transposing read 32 lanes at a
+// time over 256 bytes (measured: SQ_LDS_BANK_CONFLICT of variants with one
+// access pattern removed).  Chunk c of a row is stored at chunk position
+// c ^ swizzle(row), with the swizzles chosen so that every access pattern below
+// hits distinct bank groups within a step:
+//   K rows (D bytes): one 16-lane step of the operand reads takes rows
+//     {0..3, 16..19, 4..7, 20..23} (or those plus 8) of a 32-key block and one
+//     chunk; with 128-byte rows the group is 8 * (row & 1) + position, so per
+//     row parity the swizzle must be a permutation of the remaining row bits
+//     (1, 2, 4); with 64-byte rows the group is 4 * (row & 3) + position (bits 2, 4).
+//   V rows: the transposing reads of a step cover 16 consecutive rows of one
+//     chunk: row >> 1 (128-byte rows), row >> 2 (64-byte rows).
+template <int D>
+__device__ __forceinline__ int swz_k(int row) {
+    return D == 128 ? (((row >> 1) & 3) | (((row >> 4) & 1) << 2)) : (((row >> 2) & 1) | (((row >> 4) & 1) << 1));
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int row) { return D == 128 ? row >> 1 : row >> 2; }
+// V^T rows (one per d, 128 bytes = 8 chunks of 8 keys): chunk c of row d sits at
+// c ^ f(d), f(d) = 4 d2 + 2 d1 + (d3 ^ d0) (bits of d), a permutation of 0..7
+// both over 8 consecutive rows (the conversion writes) and, per row parity,
+// over 16 consecutive rows (the MFMA operand reads).
+__device__ __forceinline__ int vt_pos(int d, int c) {
+    return d * (2 * kKT) + 16 * (c ^ ((((d >> 1) & 3) << 1) | (((d >> 3) ^ d) & 1)));
+}
 
 __device__ __forceinline__ v16f mfma_bf16(v8bf a, v8bf b, v16f c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -229,8 +248,8 @@ __device__ __forceinline__ void issue_tile(const AttnArgs &a, const uint8_t *kh,
         const int p = p0 + lane;
         const int row = p / CH, pos = p % CH;
         const uint32_t srow = (uint32_t)slot_of(a, tile * kKT + row) * D;
-        const uint32_t offk = srow + 16 * (pos ^ (swz_k(row) & (CH - 1)));
-        const uint32_t offv = srow + 16 * (pos ^ (swz_v(row) & (CH - 1)));
+        const uint32_t offk = srow + 16 * (pos ^ (swz_k<D>(row) & (CH - 1)));
+        const uint32_t offv = srow + 16 * (pos ^ (swz_v<D>(row) & (CH - 1)));
         __builtin_amdgcn_global_load_lds(kh + offk, (LDS_AS void *)(buf + 16 * p0), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(vh + offv, (LDS_AS void *)(buf + L::K_BYTES + 16 * p0), 16, 0, 0);
     } else {
@@ -239,7 +258,7 @@ __device__ __forceinline__ void issue_tile(const AttnArgs &a, const uint8_t *kh,
         const int p = p0 + lane;
         const int row = p / CH, pos = p % CH;
         const uint32_t off = (uint32_t)slot_of(a, tile * kKT + row) * D +
-                             16 * (pos ^ ((is_k ? swz_k(row) : swz_v(row)) & (CH - 1)));
+                             16 * (pos ^ ((is_k ? swz_k<D>(row) : swz_v<D>(row)) & (CH - 1)));
         __builtin_amdgcn_global_load_lds((is_k ? kh : vh) + off,
                                          (LDS_AS void *)(buf + (is_k ? 0 : L::K_BYTES) + 16 * p0), 16, 0, 0);
     }
@@ -412,7 +431,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
         for (int h = 0; h < NH; ++h)
 #pragma unroll
             for (int e = 0; e < 2; ++e)
-                koff[kb][h][e] = row * D + 16 * ((4 * h + 2 * g + e) ^ (swz_k(row) & (CH - 1)));
+                koff[kb][h][e] = row * D + 16 * ((4 * h + 2 * g + e) ^ (swz_k<D>(row) & (CH - 1)));
     }
     // V dequantisation: 8-key x 16-column blocks of the FP8 V tile, read with
     // the 8x16-byte transpose.  16-lane group G of wave w takes blocks
@@ -427,7 +446,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
         const int blk = 4 * wave + G + 4 * kNW * i;
         const int kg = blk % 8, dc = blk / 8;
         const int row = 8 * kg + j / 2;
-        cv_src[i] = L::K_BYTES + row * D + 16 * (dc ^ (swz_v(row) & (CH - 1))) + 8 * (j % 2);
+        cv_src[i] = L::K_BYTES + row * D + 16 * (dc ^ (swz_v<D>(row) & (CH - 1))) + 8 * (j % 2);
         cv_dst[i] = vt_pos(16 * dc + j, kg);
         cv_kg[i] = kg;
     }
