@@ -332,7 +332,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     // ---- Q straight into MFMA B-operand order ----------------------------------
     // Lane (query, g) holds d in [64h + 32g, +32) of its query for each slice h:
     // 64 contiguous bytes (bf16) per slice.  The raw words are loaded first
-    // (rows past n_q read row n_q-1 and are zeroed later), the tiles are
+    // (rows past n_q read row n_q-1; their results are never stored), the tiles are
     // issued behind them, and only then are the words unpacked, so the wait
     // for Q does not hold back the tile stream.
     constexpr int QV = NH * 32;                           // Q elements per lane
@@ -364,10 +364,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             if (BF16) {
-                qv[8 * w + 2 * e] = q_ok ? __uint_as_float(qraw[w][e] << 16) : 0.0f;
-                qv[8 * w + 2 * e + 1] = q_ok ? __uint_as_float(qraw[w][e] & 0xFFFF0000u) : 0.0f;
+                qv[8 * w + 2 * e] = __uint_as_float(qraw[w][e] << 16);
+                qv[8 * w + 2 * e + 1] = __uint_as_float(qraw[w][e] & 0xFFFF0000u);
             } else {
-                qv[4 * w + e] = q_ok ? __uint_as_float(qraw[w][e]) : 0.0f;
+                qv[4 * w + e] = __uint_as_float(qraw[w][e]);
             }
         }
 
@@ -391,20 +391,22 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
                 qv[32 * h + 2 * i + 1] = x0 * ss + x1 * cc;
             }
     }
-    // scores in log2 units: fold softmax_scale * log2(e) into q; then a
-    // per-query power-of-two scale 2^qk (lanes l and l ^ 32 hold the two
-    // halves of one query), so the scaled query has absmax in (224, 448]
+    // scores in log2 units: softmax_scale * log2(e) (c2) times a per-query
+    // power-of-two scale 2^-qk (lanes l and l ^ 32 hold the two halves of one
+    // query) multiplies q, so the scaled query has absmax in (224, 448]; the
+    // product by 2^-qk c2 equals that by c2 then by 2^-qk bit for bit (a power
+    // of two commutes with rounding), and rounding is monotone, so the absmax
+    // of c2 q is c2 times the absmax of q.  Lanes of queries past n_q hold row
+    // n_q - 1 (their results are never stored).
     const float c2 = a.softmax_scale * kLog2e;
     float am = 0.0f;
 #pragma unroll
-    for (int e = 0; e < QV; ++e) {
-        qv[e] *= c2;
-        am = fmaxf(am, fabsf(qv[e]));
-    }
+    for (int e = 0; e < QV; ++e) am = fmaxf(am, fabsf(qv[e]));
+    am *= c2;
     am = fmaxf(am, __shfl_xor(am, 32));
     const int qk = scale_exponent(am);
     const int qsc = qk + 127;                                   // E8M0 byte
-    const float qscale = __uint_as_float((uint32_t)(127 - qk) << 23);   // 2^-qk, a normal
+    const float qscale = __uint_as_float((uint32_t)(127 - qk) << 23) * c2;   // 2^-qk c2
 
     // Q hi/lo E4M3 operands: byte k of qop[h][hl] is element k of the lane's slice h
     v8i qop[NH][2];
@@ -503,35 +505,41 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
 
     auto half_v = [&](int t, const uint8_t *buf, const uint8_t *buf1, uint8_t *vt_next) {
         const float *fk = reinterpret_cast<const float *>(buf + L::F_OFF);
-        // every LDS read of the half-step first (K scales of tile t; FP8 V and
-        // V scales of tile t+1), one wait for all of them
+        // the K scales of tile t first, then the FP8 V rows and V scales of tile t+1
         f32x4 fkr[2][4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 fkr[kb][q] = *reinterpret_cast<const f32x4 *>(fk + fk_index(32 * kb + 16 * g + 4 * q));
+        asm volatile("" ::: "memory");
         v2i ut[NCV];
         f32x4 sv[NCV][2];
         convert_read(buf1, ut, sv);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        // the K scales were read first: wait for them only (LDS reads complete in order)
+        asm volatile("s_waitcnt lgkmcnt(%0)" :: "n"(3 * NCV) : "memory");
 #pragma unroll
-        for (int i = 0; i < NCV; ++i) asm volatile("" : "+v"(ut[i]));
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(fkr[kb][q]));
         // scores (log2 units, shifted by cofs): the accumulator times the K row
         // scale; register r of block kb is key 32kb + 16g + r of the tile
-        float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const f32x4 f = fkr[kb][q];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float v = s[kb][4 * q + r] * f[r] + cofs;
-                    s[kb][4 * q + r] = v;
-                    mx = fmaxf(mx, v);
-                }
+                for (int r = 0; r < 4; ++r) s[kb][4 * q + r] = s[kb][4 * q + r] * f[r] + cofs;
             }
+        // running max as a tree (depth 4 instead of a 16-long chain)
+        float m8[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            m8[i] = fmaxf(fmaxf(s[i / 4][4 * (i % 4)], s[i / 4][4 * (i % 4) + 1]),
+                          fmaxf(s[i / 4][4 * (i % 4) + 2], s[i / 4][4 * (i % 4) + 3]));
+        float mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
+                         fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
         const int lim = a.n_valid - t * kKT;              // valid keys of this tile
         if (lim < kKT) {                                  // last tile of the window
             mx = -INFINITY;
@@ -589,6 +597,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
                 pb[kb][ks] = __builtin_bit_cast(v8bf, w);
                 asm volatile("" : "+v"(pb[kb][ks]));
             }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < NCV; ++i) asm volatile("" : "+v"(ut[i]));
         if (t + 1 < t1) convert_write(ut, sv, vt_next); // V^T of tile t+1
     };
 
