@@ -146,54 +146,60 @@ __global__ void __launch_bounds__(kBlock) rope_table_kernel(float2 *cs, int64_t 
     cs[idx] = make_float2((float)c, (float)s);
 }
 
-// The three row kernels below take a 2-D grid: blockIdx.y picks a (layer,
-// head) or (kv, head) row sequence, blockIdx.x a run of kUnroll * 32 rows of
-// it.  Each 8-lane row group handles kUnroll rows 32 apart and issues all of
-// their loads before any arithmetic, so a wave keeps kUnroll rows of data in
-// flight (the kernels are bound by HBM bandwidth, which needs many bytes in
-// flight per CU).
+// The three row kernels below take a 2-D grid, and each 8-lane row group
+// handles kUnroll rows, issuing all of their loads before any arithmetic, so a
+// wave keeps kUnroll rows of data in flight (the kernels are bound by HBM
+// bandwidth, which needs many bytes in flight per CU).  Rebase and naive:
+// blockIdx.y picks a (layer, head) or (kv, head) row sequence, blockIdx.x a run
+// of kUnroll * 32 rows of it, a group's rows 32 apart.  Write: see below.
 constexpr int kUnroll = 4;
 constexpr int kRunRows = kUnroll * kRowsPerIter;
 
 // ---------------------------------------------------------------------------
-// Write-time RoPE + FP8 [AI-cache].  grid = (ceil(n_new / kRunRows),
-// n_layers * 2 * n_heads); y = (layer, kv, head), rows = new tokens, so the
-// lanes of a wave touch consecutive slots (contiguous scale stores).
+// Write-time RoPE + FP8 [AI-cache].  grid = (ceil(n_new / 32),
+// n_layers * 2 * ceil(n_heads / kUnroll)); y = (layer, kv, group of kUnroll
+// consecutive heads), x = a run of 32 new tokens.  A row group takes one token
+// and the kUnroll heads of its group: its source rows are contiguous in the
+// [n_new][n_heads][D] input and its slice of the (cos, sin) row of that
+// position is loaded once for all of them.
 // ---------------------------------------------------------------------------
 template <int D, bool BF16>
 __global__ void __launch_bounds__(kBlock) write_kernel(WriteArgs a) {
     constexpr int EPT = D / kRowLanes;
     const int lane8 = threadIdx.x % kRowLanes;
-    const int h = blockIdx.y % a.n_heads;
-    const int kv = (blockIdx.y / a.n_heads) % 2;
-    const int lrel = blockIdx.y / (2 * a.n_heads);
-    const int j0 = blockIdx.x * kRunRows + threadIdx.x / kRowLanes;
+    const int n_hg = (a.n_heads + kUnroll - 1) / kUnroll;      // head groups
+    const int hg = blockIdx.y % n_hg;
+    const int kv = (blockIdx.y / n_hg) % 2;
+    const int lrel = blockIdx.y / (2 * n_hg);
+    const int jr = blockIdx.x * kRowsPerIter + threadIdx.x / kRowLanes;
+    const int j = min(jr, a.n_new - 1);                         // position of the group's rows
     const void *src = kv ? a.v_new : a.k_new;
     const int64_t lay_in = (int64_t)lrel * a.layer_stride;
     RawChunk<EPT, BF16> raw[kUnroll];
-    float4 csv[kUnroll][EPT / 4];
+    float4 csv[EPT / 4];
+    if (kv == 0) {
+        const float4 *t = reinterpret_cast<const float4 *>(a.cs + (int64_t)j * D + lane8 * EPT);
+#pragma unroll
+        for (int v = 0; v < EPT / 4; ++v) csv[v] = t[v];
+    }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-        const int j = min(j0 + u * kRowsPerIter, a.n_new - 1);
+        const int h = min(kUnroll * hg + u, a.n_heads - 1);
         raw[u].load(src, lay_in + ((int64_t)j * a.n_heads + h) * D + lane8 * EPT);
-        if (kv == 0) {
-            const float4 *t = reinterpret_cast<const float4 *>(a.cs + (int64_t)j * D + lane8 * EPT);
-#pragma unroll
-            for (int v = 0; v < EPT / 4; ++v) csv[u][v] = t[v];
-        }
     }
+    if (jr >= a.n_new) return;
     const int64_t lay_cache = (int64_t)(a.layer0 + lrel) * a.n_heads * a.window;
     uint8_t *codes = kv ? a.v_codes : a.k_codes;
     float *scales = kv ? a.v_scales : a.k_scales;
+    int slot = a.head + j;
+    if (slot >= a.window) slot -= a.window;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-        const int j = j0 + u * kRowsPerIter;
-        if (j >= a.n_new) break;
+        const int h = kUnroll * hg + u;
+        if (h >= a.n_heads) break;
         float x[EPT];
         raw[u].to_f32(x);
-        if (kv == 0) rotate_pairs<EPT>(x, reinterpret_cast<const float *>(csv[u]));
-        int slot = a.head + j;
-        if (slot >= a.window) slot -= a.window;
+        if (kv == 0) rotate_pairs<EPT>(x, reinterpret_cast<const float *>(csv));
         const int64_t row = lay_cache + (int64_t)h * a.window + slot;
         quantize_store<EPT>(x, codes + row * D + lane8 * EPT, scales + row, lane8 == 0);
     }
@@ -305,7 +311,8 @@ hipError_t launch_rope_table(float *cs, int64_t pos0, int32_t n_pos, int32_t hea
 }
 
 hipError_t launch_write(const WriteArgs &a, int head_dim, hipStream_t s) {
-    dim3 grid((a.n_new + kRunRows - 1) / kRunRows, a.n_layers * 2 * a.n_heads);
+    dim3 grid((a.n_new + kRowsPerIter - 1) / kRowsPerIter,
+              a.n_layers * 2 * ((a.n_heads + kUnroll - 1) / kUnroll));
     const bool bf = a.dtype == KVR_BF16;
     if (head_dim == 128 && bf)
         hipLaunchKernelGGL((write_kernel<128, true>), grid, dim3(kBlock), 0, s, a);
