@@ -776,7 +776,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
         const u32x4 v = *reinterpret_cast<const u32x4 *>(ob + r * (2 * D) + 8 * ((2 * k) ^ ((2 * r) & (D / 4 - 2))));
         uint16_t *dst = to_out ? a.out + ((int64_t)qr * a.n_heads + head) * D
                                : a.part_o + (((int64_t)split * a.n_q + qr) * a.n_heads + head) * D;
-        *reinterpret_cast<u32x4 *>(dst + 8 * k) = v;
+        // written once, read by another kernel (or the caller): nontemporal
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst + 8 * k));
     }
 }
 
