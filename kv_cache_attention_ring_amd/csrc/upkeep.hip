@@ -229,13 +229,13 @@ __global__ void __launch_bounds__(kBlock) rebase_kernel(RebaseArgs a, CosSinTabl
         rows[u] = lh * a.window + slot;
         const uint8_t *src = a.k_codes + rows[u] * D + lane8 * EPT;
         if constexpr (EPT == 16) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(src);
-            w[u][0] = v.x; w[u][1] = v.y; w[u][2] = v.z; w[u][3] = v.w;
+            const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v *>(src));
+            w[u][0] = v[0]; w[u][1] = v[1]; w[u][2] = v[2]; w[u][3] = v[3];
         } else {
-            const uint2 v = *reinterpret_cast<const uint2 *>(src);
-            w[u][0] = v.x; w[u][1] = v.y;
+            const u32x2v v = __builtin_nontemporal_load(reinterpret_cast<const u32x2v *>(src));
+            w[u][0] = v[0]; w[u][1] = v[1];
         }
-        sc[u] = a.k_scales[rows[u]];
+        sc[u] = __builtin_nontemporal_load(a.k_scales + rows[u]);   // read once: nontemporal
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
