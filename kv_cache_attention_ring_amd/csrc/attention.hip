@@ -482,7 +482,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     // Per tile t a wave runs two half-steps:
     //   V(t): scores, running max, weights p = 2^x and their sum -> bf16 B
     //         operands; its share of the dequantisation of V(t+1) into V^T
-    //   M(t): O^T += V^T(t) . P^T(t); S^T(t+1) = K(t+1) . Q^T
+    //   M(t): O^T += V^T(t) . P^T(t); S^T(t+1) = K(t+1) . Q^T; the K scales of
+    //         tile t+1 for V(t+1) (they land during the barrier wait)
     // in the order M(t0-1) V(t0) M(t0) V(t0+1) ... M(t1-1), where M(t0-1) only
     // holds the tile-t0 parts.  Half-steps are separated by workgroup barriers,
     // and waves 4..7 run one half-step behind waves 0..3, so the two waves
@@ -503,25 +504,20 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     v16f s[2];                          // S^T of the tile of the next V half-step
     v8bf pb[2][2];                      // P of the tile of the next M half-step
 
-    auto half_v = [&](int t, const uint8_t *buf, const uint8_t *buf1, uint8_t *vt_next) {
-        const float *fk = reinterpret_cast<const float *>(buf + L::F_OFF);
-        // the K scales of tile t first, then the FP8 V rows and V scales of tile t+1
-        f32x4 fkr[2][4];
+    f32x4 fkr[2][4];                    // K scales of the tile of the next V half-step
+    auto read_fk = [&](const uint8_t *bk) {
+        const float *fk = reinterpret_cast<const float *>(bk + L::F_OFF);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 fkr[kb][q] = *reinterpret_cast<const f32x4 *>(fk + fk_index(32 * kb + 16 * g + 4 * q));
-        asm volatile("" ::: "memory");
+    };
+    auto half_v = [&](int t, const uint8_t *buf, const uint8_t *buf1, uint8_t *vt_next) {
+        (void)buf;
         v2i ut[NCV];
         f32x4 sv[NCV][2];
         convert_read(buf1, ut, sv);
-        // the K scales were read first: wait for them only (LDS reads complete in order)
-        asm volatile("s_waitcnt lgkmcnt(%0)" :: "n"(3 * NCV) : "memory");
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(fkr[kb][q]));
         // scores (log2 units, shifted by cofs): the accumulator times the K row
         // scale; register r of block kb is key 32kb + 16g + r of the tile
 #pragma unroll
@@ -667,8 +663,12 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
                 for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb) s[kb] = mfma(ka[h][kb], qop[h][hl], s[kb], qsc);
+            read_fk(buf1);                             // K scales of tile t+1
         }
     };
+    // (the barrier after a matrix half-step waits for every LDS read, the K
+    // scales included; the loop redefines them after it so the compiler, which
+    // does not see that wait, places none of its own before their use)
     using yes = std::true_type;
     using no = std::false_type;
 
@@ -721,6 +721,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
         half_m(t0 + u, buf1, vt_base + vcur * L::VT_BYTES, yes{}, yes{});
         __builtin_amdgcn_s_setprio(0);
         lds_barrier();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(fkr[kb][q]));
         bcur = bnext;
         vcur = vnext;
     }
