@@ -278,6 +278,9 @@ def main():
     call_batch_ms = sum(batch_ms(attend) for _ in range(2)) / 2
     n_meas = 2
     w_ms, a_ms = [], []
+    # ring state before the writes below (their positions lie inside the rotary table)
+    ring_w = K.kvr_ring(ring.head, ring.n_valid, ring.pos_next)
+    chunk_w = chunks[sidx % pool]
     for _ in range(n_meas):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(2 + 2 * P * L)]
         e[0].record()
@@ -300,14 +303,14 @@ def main():
     # without the ring bookkeeping stores the same rows in the same slots each time);
     # the single launch inside a step above also counts the host's submission gap
     # after the preceding synchronisation
-    k_w, v_w = chunks[sidx % pool]
-    K.kv_write_rope_quant(cache, ring, 0, k_w, v_w, rope)
+    k_w, v_w = chunk_w
+    K.kv_write_rope_quant(cache, ring_w, 0, k_w, v_w, rope)
     torch.cuda.synchronize()
     we0, we1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     n_w = 20
     we0.record()
     for _ in range(n_w):
-        K.kv_write_rope_quant(cache, ring, 0, k_w, v_w, rope)
+        K.kv_write_rope_quant(cache, ring_w, 0, k_w, v_w, rope)
     we1.record()
     torch.cuda.synchronize()
     write_ms = we0.elapsed_time(we1) / n_w
