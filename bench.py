@@ -300,16 +300,18 @@ def main():
         a_ms += [e[j].elapsed_time(e[j + 1]) for j in range(2, len(e), 2)]
     write_in_step_ms = sum(w_ms) / len(w_ms)
     # the write kernel's own rate: launches back to back between two events (a write
-    # without the ring bookkeeping stores the same rows in the same slots each time);
-    # the single launch inside a step above also counts the host's submission gap
+    # without the ring bookkeeping stores rows in the same slots each time); each
+    # launch takes the next chunk of the pool (8 x 280 MB of bf16 rows), so its
+    # source rows come from HBM rather than from the 256 MB last-level cache; the
+    # single launch inside a step above also counts the host's submission gap
     # after the preceding synchronisation
-    k_w, v_w = chunk_w
-    K.kv_write_rope_quant(cache, ring_w, 0, k_w, v_w, rope)
+    K.kv_write_rope_quant(cache, ring_w, 0, chunk_w[0], chunk_w[1], rope)
     torch.cuda.synchronize()
     we0, we1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n_w = 20
+    n_w = 2 * pool
     we0.record()
-    for _ in range(n_w):
+    for i in range(n_w):
+        k_w, v_w = chunks[(sidx + 1 + i) % pool]
         K.kv_write_rope_quant(cache, ring_w, 0, k_w, v_w, rope)
     we1.record()
     torch.cuda.synchronize()
