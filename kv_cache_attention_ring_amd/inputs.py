@@ -135,3 +135,33 @@ def torch_queries(shape: Shape, step: int, pss: int, layer: int, device, dtype=N
 def rebase_delta(workload: str = "rebase") -> int:
     """Shift of a position reset, uniform in [1, 42 * 757]."""
     return int(np_rng(workload, 0, 0, 0, "delta").integers(1, DELTA_MAX + 1))
+
+
+# ---------------------------------------------------------------------------
+# 3-D (t, y, x) token coordinates (video tokens)
+# ---------------------------------------------------------------------------
+#: latent frame width in tokens: a chunk's tokens are numbered row-major over a
+#: grid this many columns wide (757 is prime, so its last row is partial)
+FRAME_COLS = 28
+#: the frame-index shift of a position reset at most: one frame per chunk step
+DELTA_T_MAX = RESET_PERIOD
+
+
+def axis_pairs(head_dim: int):
+    """Pairs per axis (t, y, x): the row and column groups get floor(D/6) pairs
+    each and the frame group the rest (D = 128: 22, 21, 21; D = 64: 12, 10, 10)."""
+    half = head_dim // 2
+    s = half // 3
+    return (half - 2 * s, s, s)
+
+
+def chunk_coords(n_new: int, frame: int, cols: int = FRAME_COLS) -> np.ndarray:
+    """(t, y, x) of the n_new tokens of the chunk that carries frame `frame`:
+    int64 [n_new][3], t = frame, token j at row j // cols, column j % cols."""
+    j = np.arange(n_new, dtype=np.int64)
+    return np.stack([np.full(n_new, frame, np.int64), j // cols, j % cols], axis=1)
+
+
+def rebase_delta_t(workload: str = "rebase") -> int:
+    """Frame-index shift of a position reset, uniform in [1, 42]."""
+    return int(np_rng(workload, 0, 0, 0, "delta").integers(1, DELTA_T_MAX + 1))

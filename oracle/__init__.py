@@ -83,6 +83,19 @@ def lib():
                                          ctypes.c_int, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
                                          _c_f32p, ctypes.c_int, ctypes.c_int64, ctypes.c_double,
                                          ctypes.c_double, _c_i32p, ctypes.c_int, _c_f64p]
+        L.orc_rope3d_rows.argtypes = [_c_f32p, _c_f32p, ctypes.c_int64, ctypes.c_int, _c_i64p,
+                                      _c_i32p, ctypes.c_double]
+        L.orc_rope3d_cs_n.argtypes = [_c_i64p, ctypes.c_int64, ctypes.c_int, _c_i32p, ctypes.c_double,
+                                      _c_f32p]
+        L.orc_write3d.argtypes = [_c_u8p, _c_u8p, _c_f32p, _c_f32p, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_int64, _c_i64p, _c_i32p, _c_f32p, _c_f32p,
+                                  ctypes.c_int, ctypes.c_double]
+        L.orc_rebase3d.argtypes = [_c_u8p, _c_f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int32, ctypes.c_int32, _c_i64p, _c_i32p, ctypes.c_double]
+        L.orc_attention_rows3d.argtypes = [_c_u8p, _c_u8p, _c_f32p, _c_f32p, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
+                                           _c_f32p, _c_i64p, _c_i32p, ctypes.c_double,
+                                           ctypes.c_double, _c_i32p, ctypes.c_int, _c_f64p]
         _lib = L
     return _lib
 
@@ -234,6 +247,94 @@ def attention(cache: LayerCache, start: int, n_valid: int, q, q_pos: int,
                              H, D, cache.W, int(start), int(n_valid), _p(qq, _c_f32p), n_q,
                              int(q_pos), float(base), float(sm_scale), _p(qh, _c_i32p),
                              qh.shape[0], _p(out, _c_f64p))
+    if rows is None:
+        return out.reshape(n_q, H, D)
+    return out
+
+
+# --------------------------------------------------------------------------
+# 3-D (t, y, x) rotary encoding: pairs cut into per-axis groups
+# --------------------------------------------------------------------------
+def _npairs(npairs) -> np.ndarray:
+    n = np.ascontiguousarray(np.asarray(npairs, np.int32).reshape(3))
+    assert (n >= 0).all() and n[0] >= 1, "the temporal group needs at least one pair"
+    return n
+
+
+def _coords(coords, n: int) -> np.ndarray:
+    c = np.ascontiguousarray(np.broadcast_to(np.asarray(coords, np.int64), (n, 3)))
+    return c
+
+
+def rope3d_rows(x, coords, npairs, base: float = 10000.0) -> np.ndarray:
+    """Rotate rows x[..., D] at (t, y, x) coordinates coords[..., 3]."""
+    x = _f32(x)
+    D = x.shape[-1]
+    n = x.size // D
+    npr = _npairs(npairs)
+    assert int(npr.sum()) == D // 2
+    c = _coords(np.asarray(coords, np.int64).reshape(-1, 3) if np.ndim(coords) > 1 else coords, n)
+    y = np.empty_like(x)
+    lib().orc_rope3d_rows(_p(x, _c_f32p), _p(y, _c_f32p), n, D, _p(c, _c_i64p), _p(npr, _c_i32p),
+                          float(base))
+    return y
+
+
+def rope3d_cs(coords, D: int, npairs, base: float = 10000.0) -> np.ndarray:
+    """fp32 (cos, sin) per token and pair: array [n_tok][D/2][2]."""
+    c = np.ascontiguousarray(np.asarray(coords, np.int64).reshape(-1, 3))
+    npr = _npairs(npairs)
+    assert int(npr.sum()) == D // 2
+    out = np.empty((c.shape[0], D // 2, 2), np.float32)
+    lib().orc_rope3d_cs_n(_p(c, _c_i64p), c.shape[0], D, _p(npr, _c_i32p), float(base),
+                          _p(out, _c_f32p))
+    return out
+
+
+def write3d(cache: LayerCache, total_before: int, coords, npairs, k_new, v_new,
+            base: float = 10000.0) -> None:
+    """Write-time upkeep of one chunk whose tokens carry (t, y, x) coordinates."""
+    k = _f32(k_new)
+    v = _f32(v_new)
+    N = k.shape[0]
+    assert k.shape == (N, cache.H, cache.D) and v.shape == k.shape
+    c = np.ascontiguousarray(np.asarray(coords, np.int64).reshape(N, 3))
+    npr = _npairs(npairs)
+    lib().orc_write3d(_p(cache.k_codes, _c_u8p), _p(cache.v_codes, _c_u8p),
+                      _p(cache.k_scales, _c_f32p), _p(cache.v_scales, _c_f32p),
+                      cache.H, cache.D, cache.W, int(total_before), _p(c, _c_i64p),
+                      _p(npr, _c_i32p), _p(k, _c_f32p), _p(v, _c_f32p), N, float(base))
+
+
+def rebase3d(cache: LayerCache, start: int, n_valid: int, delta, npairs,
+             base: float = 10000.0) -> None:
+    """Rotate every valid K row by -delta (a (t, y, x) triple) and re-quantise."""
+    d = np.ascontiguousarray(np.asarray(delta, np.int64).reshape(3))
+    npr = _npairs(npairs)
+    lib().orc_rebase3d(_p(cache.k_codes, _c_u8p), _p(cache.k_scales, _c_f32p),
+                       cache.H, cache.D, cache.W, int(start), int(n_valid), _p(d, _c_i64p),
+                       _p(npr, _c_i32p), float(base))
+
+
+def attention3d(cache: LayerCache, start: int, n_valid: int, q, q_coords, npairs,
+                sm_scale: float | None = None, base: float = 10000.0, rows=None) -> np.ndarray:
+    """As attention(), with query i rotated at q_coords[i] = (t, y, x)."""
+    qq = _f32(q)
+    n_q, H, D = qq.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(D)
+    if rows is None:
+        qh = np.array([(i, h) for i in range(n_q) for h in range(H)], np.int32).reshape(-1, 2)
+    else:
+        qh = np.ascontiguousarray(np.asarray(rows, np.int32).reshape(-1, 2))
+    c = np.ascontiguousarray(np.asarray(q_coords, np.int64).reshape(n_q, 3))
+    npr = _npairs(npairs)
+    out = np.zeros((qh.shape[0], D), np.float64)
+    lib().orc_attention_rows3d(_p(cache.k_codes, _c_u8p), _p(cache.v_codes, _c_u8p),
+                               _p(cache.k_scales, _c_f32p), _p(cache.v_scales, _c_f32p),
+                               H, D, cache.W, int(start), int(n_valid), _p(qq, _c_f32p),
+                               _p(c, _c_i64p), _p(npr, _c_i32p), float(base), float(sm_scale),
+                               _p(qh, _c_i32p), qh.shape[0], _p(out, _c_f64p))
     if rows is None:
         return out.reshape(n_q, H, D)
     return out

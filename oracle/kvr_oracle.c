@@ -324,6 +324,169 @@ void orc_attention_rows(const uint8_t *k_codes, const uint8_t *v_codes,
 }
 
 /* ------------------------------------------------------------------------ */
+/* 3-D (t, y, x) rotary encoding for video tokens                           */
+/* The pages describe the model as a video diffusion transformer and say no */
+/* more about its rotary encoding.  Reading taken: the D/2 interleaved pairs */
+/* are cut into three contiguous groups of n_t, n_y, n_x pairs, one per axis */
+/* (frame index, row, column of the token); group a is the 1-D rotary rule  */
+/* of a 2 n_a-dimensional vector at that axis's coordinate, i.e. its pair k  */
+/* has theta = base^(-k / n_a).  A position reset moves the frame index     */
+/* only, so the rebase rotates each group by its own axis delta (temporal   */
+/* only: (delta, 0, 0)).                                                    */
+/* Pins: split (D/2, 0, 0) is the 1-D encoding bit for bit; every group is  */
+/* the 1-D encoding of its slice at its coordinate; groups of axes with a   */
+/* zero coordinate are left bit-identical; R(-d) R(c) = R(c - d) per axis;  */
+/* q.k depends only on coordinate offsets, axis by axis.                    */
+/* ------------------------------------------------------------------------ */
+void orc_rope3d_cs(const int64_t coord[3], int i, const int32_t npairs[3], double base,
+                   float *c, float *s)
+{
+    int a = 0, k = i;
+    while (a < 2 && k >= npairs[a]) { k -= npairs[a]; ++a; }
+    double theta = pow(base, -(double)k / (double)npairs[a]);
+    double ang = (double)coord[a] * theta;
+    *c = (float)cos(ang);
+    *s = (float)sin(ang);
+}
+
+/* y = R(coord) x on each pair (x[2i], x[2i+1]); y may alias x. */
+void orc_rope3d_row(const float *x, float *y, int D, const int64_t coord[3],
+                    const int32_t npairs[3], double base)
+{
+    for (int i = 0; i < D / 2; ++i) {
+        float c, s;
+        orc_rope3d_cs(coord, i, npairs, base, &c, &s);
+        float x0 = x[2 * i], x1 = x[2 * i + 1];
+        float a = x0 * c;
+        float b = x1 * s;
+        float e = x0 * s;
+        float f = x1 * c;
+        y[2 * i] = a - b;
+        y[2 * i + 1] = e + f;
+    }
+}
+
+/* Write-time upkeep with 3-D coordinates: as orc_write, with new token j
+ * rotated at coords[j] (int64 triples) instead of a 1-D position. */
+void orc_write3d(uint8_t *k_codes, uint8_t *v_codes, float *k_scales, float *v_scales,
+                 int H, int D, int W, int64_t total_before, const int64_t *coords,
+                 const int32_t npairs[3], const float *k_new, const float *v_new, int N,
+                 double base)
+{
+#pragma omp parallel
+    {
+        float *y = (float *)malloc(sizeof(float) * (size_t)D);
+#pragma omp for collapse(2) schedule(static)
+        for (int j = 0; j < N; ++j) {
+            for (int h = 0; h < H; ++h) {
+                int32_t slot = orc_slot_of_token(total_before + j, W);
+                const float *kr = k_new + ((size_t)j * H + h) * D;
+                const float *vr = v_new + ((size_t)j * H + h) * D;
+                size_t row = (size_t)h * W + slot;
+                orc_rope3d_row(kr, y, D, coords + 3 * (size_t)j, npairs, base);
+                orc_quant_row(y, D, k_codes + row * D, &k_scales[row]);
+                orc_quant_row(vr, D, v_codes + row * D, &v_scales[row]);
+            }
+        }
+        free(y);
+    }
+}
+
+/* Rebase with a delta per axis: every valid K row dequantised, rotated by
+ * R(-delta) (delta a triple; a reset of the frame index is (d, 0, 0)),
+ * re-quantised.  V untouched. */
+void orc_rebase3d(uint8_t *k_codes, float *k_scales, int H, int D, int W,
+                  int32_t start, int32_t n_valid, const int64_t delta[3],
+                  const int32_t npairs[3], double base)
+{
+    const int64_t neg[3] = {-delta[0], -delta[1], -delta[2]};
+#pragma omp parallel
+    {
+        float *x = (float *)malloc(sizeof(float) * (size_t)D);
+#pragma omp for collapse(2) schedule(static)
+        for (int h = 0; h < H; ++h) {
+            for (int i = 0; i < n_valid; ++i) {
+                int32_t slot = orc_slot_of_token((int64_t)start + i, W);
+                size_t row = (size_t)h * W + slot;
+                orc_dequant_row(k_codes + row * D, k_scales[row], D, x);
+                orc_rope3d_row(x, x, D, neg, npairs, base);
+                orc_quant_row(x, D, k_codes + row * D, &k_scales[row]);
+            }
+        }
+        free(x);
+    }
+}
+
+/* Window attention with queries rotated at 3-D coordinates q_coords[i]
+ * (int64 triples); otherwise exactly orc_attention_rows. */
+void orc_attention_rows3d(const uint8_t *k_codes, const uint8_t *v_codes,
+                          const float *k_scales, const float *v_scales,
+                          int H, int D, int W, int32_t start, int32_t n_valid,
+                          const float *q, const int64_t *q_coords, const int32_t npairs[3],
+                          double base, double sm_scale, const int32_t *qh, int n_list,
+                          double *out)
+{
+#pragma omp parallel
+    {
+        float *qr = (float *)malloc(sizeof(float) * (size_t)D);
+        float *kh = (float *)malloc(sizeof(float) * (size_t)D);
+        double *sc = (double *)malloc(sizeof(double) * (size_t)(n_valid > 0 ? n_valid : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int t = 0; t < n_list; ++t) {
+            int i = qh[2 * t], h = qh[2 * t + 1];
+            double *o = out + (size_t)t * D;
+            orc_rope3d_row(q + ((size_t)i * H + h) * D, qr, D, q_coords + 3 * (size_t)i, npairs, base);
+            double m = -INFINITY;
+            for (int j = 0; j < n_valid; ++j) {
+                size_t row = (size_t)h * W + orc_slot_of_token((int64_t)start + j, W);
+                orc_dequant_row(k_codes + row * D, k_scales[row], D, kh);
+                double s = 0.0;
+                for (int d = 0; d < D; ++d) s += (double)qr[d] * (double)kh[d];
+                s *= sm_scale;
+                sc[j] = s;
+                if (s > m) m = s;
+            }
+            double l = 0.0;
+            for (int j = 0; j < n_valid; ++j) {
+                sc[j] = exp(sc[j] - m);
+                l += sc[j];
+            }
+            for (int d = 0; d < D; ++d) o[d] = 0.0;
+            for (int j = 0; j < n_valid; ++j) {
+                size_t row = (size_t)h * W + orc_slot_of_token((int64_t)start + j, W);
+                double w = sc[j] / l;
+                const uint8_t *vc = v_codes + row * D;
+                float vsc = v_scales[row];
+                for (int d = 0; d < D; ++d) {
+                    float vh = (float)orc_e4m3_decode(vc[d]) * vsc;
+                    o[d] += w * (double)vh;
+                }
+            }
+        }
+        free(qr);
+        free(kh);
+        free(sc);
+    }
+}
+
+/* rows x [n][D] rotated at 3-D coordinates coords[n][3] into y [n][D] */
+void orc_rope3d_rows(const float *x, float *y, int64_t n, int D, const int64_t *coords,
+                     const int32_t npairs[3], double base)
+{
+    for (int64_t r = 0; r < n; ++r)
+        orc_rope3d_row(x + r * D, y + r * D, D, coords + 3 * r, npairs, base);
+}
+
+void orc_rope3d_cs_n(const int64_t *coords, int64_t n, int D, const int32_t npairs[3],
+                     double base, float *cs)
+{
+    for (int64_t r = 0; r < n; ++r)
+        for (int i = 0; i < D / 2; ++i)
+            orc_rope3d_cs(coords + 3 * r, i, npairs, base, &cs[(r * (D / 2) + i) * 2],
+                          &cs[(r * (D / 2) + i) * 2 + 1]);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Array helpers for the test harness (loops over the scalar definitions). */
 /* ------------------------------------------------------------------------ */
 void orc_e4m3_encode_n(const float *v, uint8_t *codes, int64_t n)
