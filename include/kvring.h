@@ -149,10 +149,10 @@ int32_t kv_delta_rebase(const kvr_cache *cache, const kvr_ring *ring, int32_t la
  * dequantised cache rows.  Keys are visited in
  * this logical order, so a linear window (slot_start = 0) holding the same
  * rows gives a bit-identical result.
- * On the GPU, Q is split into two E4M3 terms (hi + lo, one scale per call
- * block) and the softmax weights likewise (hi + lo, with the per-key V scale
- * folded in), so both products run on FP8 matrix cores with fp32
- * accumulation and an online softmax.
+ * On the GPU, Q goes into the FP8 matrix cores as two E4M3 terms (hi + lo)
+ * with one power-of-two scale per query row; the softmax weights and the
+ * dequantised V rows go into bf16 matrix products; accumulation is fp32 with
+ * an online softmax.
  *   q       : device [n_q][n_heads][head_dim] of `dtype`, 16-byte aligned.
  *   out     : device bf16 [n_q][n_heads][head_dim] (uint16 storage).
  *   n_splits: key-range splits per (head, query block); 0 picks one for the
@@ -204,6 +204,55 @@ int32_t naive_upkeep(const void *lin_k_src, const void *lin_v_src,
                      void *lin_k_dst, void *lin_v_dst,
                      uint8_t *k_codes, uint8_t *v_codes, float *k_scales, float *v_scales,
                      void *stream);
+
+/* ---- 3-D (frame, row, column) rotary encoding ------------------------------
+ * The pages describe a video diffusion transformer and do not spell out its
+ * rotary encoding; this is the 3-D reading.  A token carries integer
+ * coordinates (t, y, x): frame index, row and column.  The head_dim/2
+ * interleaved pairs are cut into axis_pairs[0] frame pairs, then axis_pairs[1]
+ * row pairs, then axis_pairs[2] column pairs (axis_pairs[0] >= 1, the sum
+ * = head_dim/2); pair k of axis a's group turns by coord[a] * theta with
+ * theta = base^(-k / axis_pairs[a]) -- the 1-D rule of that group's slice.
+ * axis_pairs = (head_dim/2, 0, 0) is exactly the 1-D encoding at t.
+ * A position reset moves the frame index only: kv_delta_rebase_axes with
+ * delta = (d, 0, 0) rotates only the frame pairs.  [AI-cache] [NC-cache] */
+
+/* Fills cs (device, n_tok * head_dim/2 float pairs, 16-byte aligned) with the
+ * (cos, sin) of every pair of tokens 0 .. n_tok-1 at coords (device int32
+ * [n_tok][3]); angle and trig in fp64, rounded to fp32.
+ * Errors: KVR_EINVAL (null, n_tok < 1, bad axis_pairs, base <= 1), KVR_EALIGN,
+ * KVR_EUNSUPPORTED (head_dim). */
+int32_t kv_rope3d_table_fill(float *cs, const int32_t *coords, int32_t n_tok, int32_t head_dim,
+                             const int32_t axis_pairs[3], double base, void *stream);
+
+/* kv_write_rope_quant with the rotation of new token j taken from row j of
+ * cs_rows (device [n_new][head_dim/2][2] fp32, 16-byte aligned; e.g. from
+ * kv_rope3d_table_fill) instead of a position.  Slots, quantisation,
+ * arguments and errors are those of kv_write_rope_quant. */
+int32_t kv_write_rope_quant_rows(const kvr_cache *cache, const kvr_ring *before,
+                                 int32_t layer0, int32_t n_layers,
+                                 const void *k_new, const void *v_new, kvr_dtype dtype,
+                                 int64_t layer_stride_elems, int32_t n_new,
+                                 const float *cs_rows, void *stream);
+
+/* kv_delta_rebase with one shift per axis (host int64[3]): every valid K row is
+ * dequantised, rotated by -delta[a] on the pairs of axis a (cos/sin of
+ * -delta[a] * theta formed in fp64, rounded to fp32) and re-quantised.
+ * delta = (d, 0, 0) is the frame-only reset; with axis_pairs = (head_dim/2, 0,
+ * 0) this is kv_delta_rebase(d) bit for bit.  Errors as kv_delta_rebase, plus
+ * KVR_EINVAL for a null delta or bad axis_pairs. */
+int32_t kv_delta_rebase_axes(const kvr_cache *cache, const kvr_ring *ring, int32_t layer0,
+                             int32_t n_layers, const int64_t delta[3], const int32_t axis_pairs[3],
+                             double rope_base, void *stream);
+
+/* attn_fp8_window with query i rotated by row i of q_cs_rows (device
+ * [n_q][head_dim/2][2] fp32, 16-byte aligned; the chunk's own rows when the
+ * queries are the chunk's new tokens) instead of a position.  Everything else
+ * -- keys, splits, workspace, output, errors -- as attn_fp8_window. */
+int32_t attn_fp8_window_rows(const kvr_cache *cache, int32_t layer, int32_t slot_start,
+                             int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
+                             const float *q_cs_rows, float softmax_scale, uint16_t *out,
+                             int32_t n_splits, void *ws, size_t ws_bytes, void *stream);
 
 /* Text of the last error on this thread ("" if none). */
 const char *kvr_last_error(void);

@@ -283,7 +283,10 @@ __device__ __forceinline__ void wait_tiles(int later) {
     else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * OPT) : "memory");
 }
 
-template <int D, bool BF16>
+// QTAB: the queries' rotation comes from (cos, sin) rows, one per query
+// (a.q_cs, [n_q][D/2][2] fp32: the 3-D form, where the angle of a pair is its
+// own axis coordinate times its frequency), instead of position times frequency.
+template <int D, bool BF16, bool QTAB>
 __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     using L = Lds<D>;
     constexpr int CH = L::CH;
@@ -337,9 +340,12 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     // for Q does not hold back the tile stream.
     constexpr int QV = NH * 32;                           // Q elements per lane
     constexpr int QW = BF16 ? QV / 8 : QV / 4;            // 16-byte words per lane
+    constexpr int CW = QTAB ? QV / 4 : 1;                 // 16-byte words of (cos, sin) per lane
     u32x4 qraw[QW];
+    u32x4 csraw[CW];
     {
-        const int64_t row = ((int64_t)min(qi, a.n_q - 1) * a.n_heads + head) * D;
+        const int64_t qrow = min(qi, a.n_q - 1);
+        const int64_t row = (qrow * a.n_heads + head) * D;
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
             const int d0 = 64 * h + 32 * g;
@@ -347,6 +353,16 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
                                     : reinterpret_cast<const u32x4 *>(reinterpret_cast<const float *>(a.q) + row + d0);
 #pragma unroll
             for (int c = 0; c < QW / NH; ++c) qraw[(QW / NH) * h + c] = gload16(src + c);
+        }
+        if constexpr (QTAB) {
+            // the (cos, sin) of the lane's pairs 32h + 16g .. +15 of each slice h:
+            // 128 contiguous bytes per slice
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+                const u32x4 *src = reinterpret_cast<const u32x4 *>(a.q_cs + 2 * (qrow * (D / 2) + 32 * h + 16 * g));
+#pragma unroll
+                for (int c = 0; c < 8; ++c) csraw[8 * h + c] = gload16(src + c);
+            }
         }
     }
 
@@ -357,6 +373,12 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     for (int k = 0; k < P; ++k)
         issue_tile<D>(a, kh, vh, scales_h, min(t0 + k, t1 - 1), tiles + k * L::BUF, wave);
     qwait<P * ops_per_tile<D>()>(qraw);
+    if constexpr (QTAB) {
+        // issued before the tiles, so the wait above covered them too; order
+        // their uses after it
+#pragma unroll
+        for (int i = 0; i < CW; ++i) asm volatile("" : "+v"(csraw[i]));
+    }
 
     float qv[QV];
 #pragma unroll
@@ -375,7 +397,18 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     // angle (position times theta_i / 2pi, revolutions) is formed in fp64 and
     // reduced to [-1/2, 1/2] before the hardware sine and cosine.  theta for
     // the g = 1 half is theta_{32h+i} * base^(-32/D) (exact to an ulp of fp64).
-    {
+    if constexpr (QTAB) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const u32x4 w = csraw[8 * h + i / 2];
+                const float cc = __uint_as_float(w[2 * (i % 2)]), ss = __uint_as_float(w[2 * (i % 2) + 1]);
+                const float x0 = qv[32 * h + 2 * i], x1 = qv[32 * h + 2 * i + 1];
+                qv[32 * h + 2 * i] = x0 * cc - x1 * ss;
+                qv[32 * h + 2 * i + 1] = x0 * ss + x1 * cc;
+            }
+    } else {
         const double pos = (double)(a.q_pos0 + qi);
         const double gmul = g ? a.rev_step : 1.0;
 #pragma unroll
@@ -878,12 +911,23 @@ hipError_t launch_attention_main(const AttnArgs &a, int head_dim, hipStream_t s)
     const int n_qb = (a.n_q + kQB - 1) / kQB;
     const dim3 grid(n_qb * a.n_heads * a.n_splits), block(kThreads);
     const bool bf16 = a.dtype == KVR_BF16;
+    const bool tab = a.q_cs != nullptr;
     if (head_dim == 128) {
-        if (bf16) hipLaunchKernelGGL((attn_kernel<128, true>), grid, block, Lds<128>::TOTAL, s, a);
-        else hipLaunchKernelGGL((attn_kernel<128, false>), grid, block, Lds<128>::TOTAL, s, a);
+        if (tab) {
+            if (bf16) hipLaunchKernelGGL((attn_kernel<128, true, true>), grid, block, Lds<128>::TOTAL, s, a);
+            else hipLaunchKernelGGL((attn_kernel<128, false, true>), grid, block, Lds<128>::TOTAL, s, a);
+        } else {
+            if (bf16) hipLaunchKernelGGL((attn_kernel<128, true, false>), grid, block, Lds<128>::TOTAL, s, a);
+            else hipLaunchKernelGGL((attn_kernel<128, false, false>), grid, block, Lds<128>::TOTAL, s, a);
+        }
     } else {
-        if (bf16) hipLaunchKernelGGL((attn_kernel<64, true>), grid, block, Lds<64>::TOTAL, s, a);
-        else hipLaunchKernelGGL((attn_kernel<64, false>), grid, block, Lds<64>::TOTAL, s, a);
+        if (tab) {
+            if (bf16) hipLaunchKernelGGL((attn_kernel<64, true, true>), grid, block, Lds<64>::TOTAL, s, a);
+            else hipLaunchKernelGGL((attn_kernel<64, false, true>), grid, block, Lds<64>::TOTAL, s, a);
+        } else {
+            if (bf16) hipLaunchKernelGGL((attn_kernel<64, true, false>), grid, block, Lds<64>::TOTAL, s, a);
+            else hipLaunchKernelGGL((attn_kernel<64, false, false>), grid, block, Lds<64>::TOTAL, s, a);
+        }
     }
     return hipGetLastError();
 }

@@ -19,9 +19,16 @@ struct CosSinTable {                 // (cos, sin) pairs of one rotation, fp32
     float cs[2 * kMaxHalfDim];
 };
 
+struct AxisTheta {                   // 3-D form: theta and coordinate axis (0 t, 1 y, 2 x) per pair
+    double t[kMaxHalfDim];
+    int32_t axis[kMaxHalfDim];
+};
+
 // ---- upkeep.hip ----------------------------------------------------------
 hipError_t launch_rope_table(float *cs, int64_t pos0, int32_t n_pos, int32_t head_dim,
                              const ThetaTable &theta, hipStream_t s);
+hipError_t launch_rope3d_table(float *cs, const int32_t *coords, int32_t n_tok, int32_t head_dim,
+                               const AxisTheta &theta, hipStream_t s);
 
 struct WriteArgs {
     uint8_t *k_codes, *v_codes;
@@ -60,6 +67,7 @@ struct AttnArgs {
     ThetaTable rev;                   // theta_i / (2 pi): rotary frequencies in revolutions (fp64)
     double rev_step;                  // base^(-32/D) = theta_{i+16} / theta_i
     int64_t q_pos0;                   // rotary position of query 0
+    const float *q_cs;                // or (cos, sin) rows of the queries [n_q][D/2][2] (then q_pos0 unused)
     uint16_t *out;                    // [n_q][H][D] bf16
     uint16_t *part_o;                 // [splits][n_q][H][D] fp16, normalised rows
     float *part_ml;                   // [splits][n_q][H][2]

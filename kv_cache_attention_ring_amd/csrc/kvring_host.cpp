@@ -276,7 +276,7 @@ void set_partials(kvr::AttnArgs &a, void *ws, int32_t n_heads, int32_t D, int32_
 int32_t attn_setup(kvr::AttnArgs &a, const kvr_cache *cache, int32_t layer, int32_t slot_start,
                    int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
                    int64_t q_pos_start, float softmax_scale, double rope_base, uint16_t *out,
-                   int32_t n_splits, void *ws, size_t ws_bytes) {
+                   int32_t n_splits, void *ws, size_t ws_bytes, const float *q_cs = nullptr) {
     if (int32_t e = check_cache(cache)) return e;
     const int32_t W = cache->window, D = cache->head_dim;
     if (int32_t e = check_dtype(dtype)) return e;
@@ -296,7 +296,9 @@ int32_t attn_setup(kvr::AttnArgs &a, const kvr_cache *cache, int32_t layer, int3
     n_splits = effective_splits(cache->n_heads, n_q, n_valid, n_splits, &tps);
     if (int32_t e = check_workspace(kvr::attn_workspace_bytes(cache->n_heads, D, n_q, n_splits), ws, ws_bytes))
         return e;
+    if (q_cs && !aligned16(q_cs)) return fail(KVR_EALIGN, "query rotary rows not 16-byte aligned");
     a = kvr::AttnArgs{};
+    a.q_cs = q_cs;
     const int64_t lay = (int64_t)layer * cache->n_heads * W;
     a.k_codes = cache->k_codes + lay * D;
     a.v_codes = cache->v_codes + lay * D;
@@ -384,6 +386,114 @@ int32_t attn_fp8_window_merge(const kvr_cache *cache, int32_t n_q, int32_t n_val
     if (int32_t e = merge_setup(a, cache, n_q, n_valid, n_splits, out, ws, ws_bytes)) return e;
     return launch_status(kvr::launch_attention_merge(a, cache->head_dim, static_cast<hipStream_t>(stream)),
                          "attention merge");
+}
+
+// ---- 3-D (frame, row, column) rotary encoding -------------------------------
+// The D/2 pairs are cut into n_t, n_y, n_x contiguous groups, one per axis;
+// group a is the 1-D rule of its slice at that axis's coordinate (pair k of
+// the group: theta = base^(-k / n_a)).
+namespace {
+
+int32_t check_axis_pairs(const int32_t *np, int32_t D) {
+    if (!np) return fail(KVR_EINVAL, "axis_pairs is NULL");
+    if (np[0] < 1 || np[1] < 0 || np[2] < 0 || np[0] + np[1] + np[2] != D / 2)
+        return fail(KVR_EINVAL, "axis_pairs (%d, %d, %d) must be >= (1, 0, 0) and sum to %d", np[0], np[1],
+                    np[2], D / 2);
+    return KVR_OK;
+}
+
+kvr::AxisTheta make_axis_theta(const int32_t *np, double base) {
+    kvr::AxisTheta th{};
+    int i = 0;
+    for (int ax = 0; ax < 3; ++ax)
+        for (int k = 0; k < np[ax]; ++k, ++i) {
+            th.t[i] = pow(base, -(double)k / (double)np[ax]);
+            th.axis[i] = ax;
+        }
+    return th;
+}
+
+}  // namespace
+
+int32_t kv_rope3d_table_fill(float *cs, const int32_t *coords, int32_t n_tok, int32_t head_dim,
+                             const int32_t *axis_pairs, double base, void *stream) {
+    if (int32_t e = check_head_dim(head_dim)) return e;
+    if (int32_t e = check_axis_pairs(axis_pairs, head_dim)) return e;
+    if (!cs || !coords) return fail(KVR_EINVAL, "table or coordinates pointer is NULL");
+    if (!aligned16(cs)) return fail(KVR_EALIGN, "table must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(coords) & 3u) != 0) return fail(KVR_EALIGN, "coordinates not 4-byte aligned");
+    if (n_tok < 1 || n_tok >= kMaxExtent) return fail(KVR_EINVAL, "n_tok %d out of range", n_tok);
+    if (!(base > 1.0) || !isfinite(base)) return fail(KVR_EINVAL, "rotary base must be > 1");
+    return launch_status(kvr::launch_rope3d_table(cs, coords, n_tok, head_dim, make_axis_theta(axis_pairs, base),
+                                                  static_cast<hipStream_t>(stream)),
+                         "3-D rope table");
+}
+
+int32_t kv_write_rope_quant_rows(const kvr_cache *cache, const kvr_ring *before, int32_t layer0,
+                                 int32_t n_layers, const void *k_new, const void *v_new,
+                                 kvr_dtype dtype, int64_t layer_stride_elems, int32_t n_new,
+                                 const float *cs_rows, void *stream) {
+    if (!cs_rows) return fail(KVR_EINVAL, "rotary rows pointer is NULL");
+    if (!aligned16(cs_rows)) return fail(KVR_EALIGN, "rotary rows not 16-byte aligned");
+    if (!cache) return fail(KVR_EINVAL, "cache is NULL");
+    // the position form's validation, against a one-off table descriptor that
+    // holds exactly the chunk's rows at the ring's next positions
+    kvr_rope_table t{};
+    t.cs = const_cast<float *>(cs_rows);
+    t.pos0 = before ? before->pos_next : 0;
+    t.n_pos = n_new;
+    t.head_dim = cache->head_dim;
+    t.base = 10000.0;
+    return kv_write_rope_quant(cache, before, layer0, n_layers, k_new, v_new, dtype, layer_stride_elems,
+                               n_new, &t, stream);
+}
+
+int32_t kv_delta_rebase_axes(const kvr_cache *cache, const kvr_ring *ring, int32_t layer0,
+                             int32_t n_layers, const int64_t *delta, const int32_t *axis_pairs,
+                             double rope_base, void *stream) {
+    if (int32_t e = check_cache(cache)) return e;
+    const int32_t W = cache->window, D = cache->head_dim;
+    if (int32_t e = check_ring(ring, W)) return e;
+    if (int32_t e = check_axis_pairs(axis_pairs, D)) return e;
+    if (!delta) return fail(KVR_EINVAL, "delta is NULL");
+    if (layer0 < 0 || n_layers < 1 || layer0 + n_layers > cache->n_layers)
+        return fail(KVR_EINVAL, "layers [%d,%d) outside cache of %d", layer0, layer0 + n_layers,
+                    cache->n_layers);
+    if (!(rope_base > 1.0) || !isfinite(rope_base)) return fail(KVR_EINVAL, "rotary base must be > 1");
+    if (ring->n_valid == 0) return ok();
+    // cos/sin of -delta[axis] * theta per pair: fp64 angle and trig, rounded to fp32
+    kvr::CosSinTable rot{};
+    const kvr::AxisTheta th = make_axis_theta(axis_pairs, rope_base);
+    for (int i = 0; i < D / 2; ++i) {
+        const double ang = (double)(-delta[th.axis[i]]) * th.t[i];
+        rot.cs[2 * i] = (float)cos(ang);
+        rot.cs[2 * i + 1] = (float)sin(ang);
+    }
+    kvr::RebaseArgs a{};
+    a.k_codes = cache->k_codes;
+    a.k_scales = cache->k_scales;
+    a.n_heads = cache->n_heads;
+    a.window = W;
+    a.start = kvr_ring_logical_start(ring, W);
+    a.n_valid = ring->n_valid;
+    a.layer0 = layer0;
+    a.n_layers = n_layers;
+    return launch_status(kvr::launch_rebase(a, rot, D, static_cast<hipStream_t>(stream)), "rebase");
+}
+
+int32_t attn_fp8_window_rows(const kvr_cache *cache, int32_t layer, int32_t slot_start,
+                             int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
+                             const float *q_cs_rows, float softmax_scale, uint16_t *out,
+                             int32_t n_splits, void *ws, size_t ws_bytes, void *stream) {
+    if (!q_cs_rows) return fail(KVR_EINVAL, "query rotary rows pointer is NULL");
+    kvr::AttnArgs a;
+    if (int32_t e = attn_setup(a, cache, layer, slot_start, n_valid, q, dtype, n_q, 0, softmax_scale,
+                               10000.0, out, n_splits, ws, ws_bytes, q_cs_rows))
+        return e;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (int32_t e = launch_status(kvr::launch_attention_main(a, cache->head_dim, s), "attention"))
+        return e;
+    return launch_status(kvr::launch_attention_merge(a, cache->head_dim, s), "attention merge");
 }
 
 // ---- (a5) naive per-call upkeep -------------------------------------------

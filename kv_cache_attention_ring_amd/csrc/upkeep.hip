@@ -146,6 +146,24 @@ __global__ void __launch_bounds__(kBlock) rope_table_kernel(float2 *cs, int64_t 
     cs[idx] = make_float2((float)c, (float)s);
 }
 
+// ---------------------------------------------------------------------------
+// 3-D rotary rows: cs[tok][i] = (cos, sin)(coords[tok][axis_i] * theta_i), the
+// pair's own axis coordinate (frame, row, column) times its frequency; fp64
+// angle and trig, rounded to fp32.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kBlock) rope3d_table_kernel(float2 *cs, const int32_t *coords,
+                                                              int32_t n_tok, int32_t half,
+                                                              AxisTheta th) {
+    const int64_t idx = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (idx >= (int64_t)n_tok * half) return;
+    const int64_t tok = idx / half;
+    const int i = (int)(idx - tok * half);
+    const double ang = (double)coords[3 * tok + th.axis[i]] * th.t[i];
+    double s, c;
+    sincos(ang, &s, &c);
+    cs[idx] = make_float2((float)c, (float)s);
+}
+
 // The three row kernels below take a 2-D grid, and each 8-lane row group
 // handles kUnroll rows, issuing all of their loads before any arithmetic, so a
 // wave keeps kUnroll rows of data in flight (the kernels are bound by HBM
@@ -307,6 +325,16 @@ hipError_t launch_rope_table(float *cs, int64_t pos0, int32_t n_pos, int32_t hea
     const int grid = (int)((n + kBlock - 1) / kBlock);
     hipLaunchKernelGGL(rope_table_kernel, dim3(grid), dim3(kBlock), 0, s,
                        reinterpret_cast<float2 *>(cs), pos0, n_pos, half, theta);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope3d_table(float *cs, const int32_t *coords, int32_t n_tok, int32_t head_dim,
+                               const AxisTheta &theta, hipStream_t s) {
+    const int half = head_dim / 2;
+    const int64_t n = (int64_t)n_tok * half;
+    const int grid = (int)((n + kBlock - 1) / kBlock);
+    hipLaunchKernelGGL(rope3d_table_kernel, dim3(grid), dim3(kBlock), 0, s,
+                       reinterpret_cast<float2 *>(cs), coords, n_tok, half, theta);
     return hipGetLastError();
 }
 

@@ -73,6 +73,13 @@ _SIGS = {
     "attn_fp8_window_merge": (_I32, [ctypes.POINTER(kvr_cache), _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "naive_upkeep": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32,
                             ctypes.POINTER(kvr_rope_table), _P, _P, _P, _P, _P, _P, _P]),
+    "kv_rope3d_table_fill": (_I32, [_P, _P, _I32, _I32, ctypes.POINTER(_I32), _F64, _P]),
+    "kv_write_rope_quant_rows": (_I32, [ctypes.POINTER(kvr_cache), ctypes.POINTER(kvr_ring), _I32, _I32,
+                                        _P, _P, _I32, _I64, _I32, _P, _P]),
+    "kv_delta_rebase_axes": (_I32, [ctypes.POINTER(kvr_cache), ctypes.POINTER(kvr_ring), _I32, _I32,
+                                    ctypes.POINTER(_I64), ctypes.POINTER(_I32), _F64, _P]),
+    "attn_fp8_window_rows": (_I32, [ctypes.POINTER(kvr_cache), _I32, _I32, _I32, _P, _I32, _I32, _P,
+                                    _F32, _P, _I32, _P, _SZ, _P]),
     "kvr_last_error": (ctypes.c_char_p, []),
     "kvr_version": (ctypes.c_char_p, []),
 }
@@ -213,6 +220,81 @@ def kv_write_rope_quant(cache: KVCache, before: kvr_ring, layer0: int, k_new: to
     _check(lib().kv_write_rope_quant(ctypes.byref(c), ctypes.byref(before), layer0, n_layers,
                                      _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dtype_code(k_new),
                                      stride, n_new, ctypes.byref(t), _stream(stream)))
+
+
+def _new_rows(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor):
+    if k_new.shape != v_new.shape or k_new.dtype != v_new.dtype:
+        raise KVRError(KVR_EINVAL, "k_new and v_new must match in shape and dtype")
+    if k_new.dim() == 3:
+        n_layers, (n_new, _, _) = 1, k_new.shape
+        stride = k_new.numel()
+    elif k_new.dim() == 4:
+        n_layers, n_new = k_new.shape[0], k_new.shape[1]
+        stride = k_new[0].numel()
+    else:
+        raise KVRError(KVR_EINVAL, "k_new must be [N][H][D] or [L][N][H][D]")
+    if k_new.shape[-2:] != (cache.n_heads, cache.head_dim):
+        raise KVRError(KVR_EINVAL, f"k_new trailing shape {tuple(k_new.shape[-2:])} != "
+                                   f"({cache.n_heads}, {cache.head_dim})")
+    return n_layers, n_new, stride
+
+
+def _axes(v, ct):
+    a = (ct * 3)(*[int(x) for x in v])
+    if len(v) != 3:
+        raise KVRError(KVR_EINVAL, "three axes (t, y, x) expected")
+    return a
+
+
+class Rope3DRows:
+    """Device (cos, sin) rows [n_tok][D/2][2] of tokens at (t, y, x) coordinates
+    (kv_rope3d_table_fill); coords: int [n_tok][3] (host or device)."""
+
+    def __init__(self, coords, head_dim: int, axis_pairs, base: float = 10000.0, device="cuda",
+                 stream=None):
+        c = torch.as_tensor(coords, dtype=torch.int32).reshape(-1, 3).to(device).contiguous()
+        self.coords = c
+        self.n_tok, self.head_dim, self.base = c.shape[0], head_dim, float(base)
+        self.axis_pairs = tuple(int(x) for x in axis_pairs)
+        self.cs = torch.empty((self.n_tok, head_dim // 2, 2), dtype=torch.float32, device=device)
+        _check(lib().kv_rope3d_table_fill(_dev(self.cs, "cs"), _dev(c, "coords"), self.n_tok, head_dim,
+                                          _axes(self.axis_pairs, _I32), self.base, _stream(stream)))
+
+
+def kv_write_rope_quant_rows(cache: KVCache, before: kvr_ring, layer0: int, k_new: torch.Tensor,
+                             v_new: torch.Tensor, cs_rows: torch.Tensor, stream=None) -> None:
+    """As kv_write_rope_quant, token j rotated by cs_rows[j] ([N][D/2][2] fp32)."""
+    n_layers, n_new, stride = _new_rows(cache, k_new, v_new)
+    if cs_rows.dtype != torch.float32 or cs_rows.shape != (n_new, cache.head_dim // 2, 2):
+        raise KVRError(KVR_EINVAL, "cs_rows must be fp32 [n_new][head_dim/2][2]")
+    c = cache.desc()
+    _check(lib().kv_write_rope_quant_rows(ctypes.byref(c), ctypes.byref(before), layer0, n_layers,
+                                          _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dtype_code(k_new),
+                                          stride, n_new, _dev(cs_rows, "cs_rows"), _stream(stream)))
+
+
+def kv_delta_rebase_axes(cache: KVCache, ring: kvr_ring, layer0: int, n_layers: int, delta, axis_pairs,
+                         rope_base: float = 10000.0, stream=None) -> None:
+    """Rotate every valid K row by -delta[a] on the pairs of axis a (delta = (t, y, x))."""
+    c = cache.desc()
+    _check(lib().kv_delta_rebase_axes(ctypes.byref(c), ctypes.byref(ring), layer0, n_layers,
+                                      _axes(delta, _I64), _axes(axis_pairs, _I32), float(rope_base),
+                                      _stream(stream)))
+
+
+def attn_fp8_window_rows(cache: KVCache, layer: int, slot_start: int, n_valid: int, q: torch.Tensor,
+                         q_cs_rows: torch.Tensor, out: torch.Tensor | None = None, n_splits: int = 0,
+                         ws: torch.Tensor | None = None, softmax_scale: float | None = None,
+                         stream=None) -> torch.Tensor:
+    """As attn_fp8_window, query i rotated by q_cs_rows[i] ([n_q][D/2][2] fp32)."""
+    args, out, _, _c = _attn_args(cache, layer, slot_start, n_valid, q, 0, 10000.0, out, n_splits, ws,
+                                  softmax_scale, stream)
+    if q_cs_rows.dtype != torch.float32 or q_cs_rows.shape != (q.shape[0], cache.head_dim // 2, 2):
+        raise KVRError(KVR_EINVAL, "q_cs_rows must be fp32 [n_q][head_dim/2][2]")
+    # the position form's (q_pos_start, rope_base) pair is replaced by the rows
+    rows_args = args[:7] + (_dev(q_cs_rows, "q_cs_rows"), args[8]) + args[10:]
+    _check(lib().attn_fp8_window_rows(*rows_args))
+    return out
 
 
 def kv_delta_rebase(cache: KVCache, ring: kvr_ring, layer0: int, n_layers: int, delta: int,

@@ -1,0 +1,197 @@
+"""GPU parity of the 3-D (frame, row, column) rotary form, through the C ABI,
+against the CPU oracle on the same seeded inputs (bars in tests/_parity.py).
+
+Cases: the per-token (cos, sin) rows; with all pairs temporal, the rows equal
+the 1-D table and the row-driven write equals the position-driven write bit
+for bit; the small workload end to end with 3-D coordinates (8 steps, a frame
+reset after step 4, 4 attention passes per step, one and two key splits) and
+its W = 100 variant that wraps mid-chunk; one production-shape layer (12
+heads, D 128, W 5788, 757 tokens per chunk as one 28-column latent frame):
+write, attention on sampled queries of every head, the frame-only rebase.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_attention_ring_amd import inputs
+from kv_cache_attention_ring_amd import kvring as K
+
+from _parity import assert_attention, assert_codes, assert_scales
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    K.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _f32(t):
+    return t.detach().float().cpu().numpy()
+
+
+def _check_cache(cache, orc, what):
+    torch.cuda.synchronize()
+    for name in ("k", "v"):
+        assert_codes(_np(getattr(cache, f"{name}_codes"))[0], getattr(orc, f"{name}_codes"), f"{what} {name}")
+        assert_scales(_np(getattr(cache, f"{name}_scales"))[0], getattr(orc, f"{name}_scales"), f"{what} {name}")
+
+
+def test_rope3d_rows_match_oracle():
+    rng = np.random.default_rng(5)
+    for D in (64, 128):
+        _say(f"3-D rope rows D={D}")
+        n = 6000
+        coords = np.stack([rng.integers(-40000, 40000, n), rng.integers(0, 64, n), rng.integers(0, 64, n)], 1)
+        npr = inputs.axis_pairs(D)
+        rows = K.Rope3DRows(coords, D, npr)
+        torch.cuda.synchronize()
+        got = _np(rows.cs)
+        want = oracle.rope3d_cs(coords, D, npr)
+        same = (got.view(np.uint32) == want.view(np.uint32)).mean()
+        ulps = np.abs(got.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+        assert same >= 0.9999 and ulps.max() <= 1, (same, ulps.max())
+
+
+def test_all_temporal_rows_are_the_1d_form():
+    """axis_pairs (D/2, 0, 0): rows == the position table's rows, and the
+    row-driven write == the position-driven write, bit for bit."""
+    shp = inputs.TINY_WRAP
+    H, D, W, N = shp.n_heads, shp.head_dim, shp.window, shp.n_new
+    rope = K.RopeTable(-256, 4096, D)
+    a, b = K.KVCache(1, H, D, W), K.KVCache(1, H, D, W)
+    ring = K.kvr_ring_init()
+    for step in range(9):
+        _say(f"1-D equivalence step {step}")
+        k, v = inputs.np_chunk(shp, step)
+        kd, vd = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+        pos = ring.pos_next + np.arange(N)
+        rows = K.Rope3DRows(np.stack([pos, np.full(N, 7), np.full(N, 3)], 1), D, (D // 2, 0, 0))
+        torch.cuda.synchronize()
+        p0 = ring.pos_next - rope.pos0
+        assert torch.equal(rows.cs, rope.cs[p0:p0 + N])
+        K.kv_write_rope_quant_rows(a, ring, 0, kd, vd, rows.cs)
+        K.kv_write_rope_quant(b, ring, 0, kd, vd, rope)
+        K.kvr_ring_after_write(ring, W, N)
+    K.kv_delta_rebase_axes(a, ring, 0, 1, (33, 0, 0), (D // 2, 0, 0))
+    K.kv_delta_rebase(b, ring, 0, 1, 33)
+    torch.cuda.synchronize()
+    for n in ("k_codes", "v_codes", "k_scales", "v_scales"):
+        assert torch.equal(getattr(a, n), getattr(b, n)), n
+
+
+class Run3D:
+    """Row-driven ring path and the 3-D oracle side by side on one layer."""
+
+    def __init__(self, shape, cols, dtype=torch.float32):
+        self.s, self.cols, self.dtype = shape, cols, dtype
+        H, D, W = shape.n_heads, shape.head_dim, shape.window
+        self.npr = inputs.axis_pairs(D)
+        self.cache = K.KVCache(1, H, D, W)
+        self.ring = K.kvr_ring_init()
+        self.orc = oracle.LayerCache(H, D, W)
+        self.total = 0
+        self.t_shift = 0            # frame resets so far
+        self.rows = None
+
+    def step(self, step, k, v):
+        N = k.shape[0]
+        coords = inputs.chunk_coords(N, step, self.cols) - [self.t_shift, 0, 0]
+        self.coords = coords
+        self.rows = K.Rope3DRows(coords, self.s.head_dim, self.npr)
+        kd = torch.from_numpy(k).to(self.dtype).cuda()
+        vd = torch.from_numpy(v).to(self.dtype).cuda()
+        K.kv_write_rope_quant_rows(self.cache, self.ring, 0, kd, vd, self.rows.cs)
+        oracle.write3d(self.orc, self.total, coords, self.npr, _f32(kd), _f32(vd))
+        K.kvr_ring_after_write(self.ring, self.s.window, N)
+        self.total += N
+
+    def rebase(self, d):
+        start = K.kvr_ring_logical_start(self.ring, self.s.window)
+        K.kv_delta_rebase_axes(self.cache, self.ring, 0, 1, (d, 0, 0), self.npr)
+        oracle.rebase3d(self.orc, start, self.ring.n_valid, (d, 0, 0), self.npr)
+        self.t_shift += d
+
+    def attention(self, q, n_splits=0, rows=None):
+        W = self.s.window
+        qd = torch.from_numpy(q).to(self.dtype).cuda() if isinstance(q, np.ndarray) else q.cuda()
+        start = K.kvr_ring_logical_start(self.ring, W)
+        out = K.attn_fp8_window_rows(self.cache, 0, start, self.ring.n_valid, qd, self.rows.cs, n_splits=n_splits)
+        torch.cuda.synchronize()
+        ref = oracle.attention3d(self.orc, start, self.ring.n_valid, _f32(qd), self.coords, self.npr, rows=rows)
+        got = _f32(out)
+        if rows is not None:
+            got = np.stack([got[i, h] for i, h in rows])
+        return got, ref
+
+
+@pytest.mark.parametrize("shape", [inputs.TINY, inputs.TINY_WRAP], ids=["w96", "w100"])
+def test_small_workload_3d(shape):
+    run = Run3D(shape, cols=5)
+    for step in range(8):
+        _say(f"3-D small {shape.window} step {step}")
+        k, v = inputs.np_chunk(shape, step)
+        run.step(step, k, v)
+        _check_cache(run.cache, run.orc, f"step {step}")
+        for p in range(shape.passes):
+            q = inputs.np_queries(shape, step, p)
+            got, ref = run.attention(q, n_splits=1 + (p % 2))
+            assert_attention(got, ref, f"step {step} pass {p}")
+        if step == 3:
+            _say("3-D small frame rebase by 2")
+            run.rebase(2)
+            _check_cache(run.cache, run.orc, "after frame rebase")
+
+
+@pytest.fixture(scope="module")
+def page_run():
+    shp = inputs.PAGE_LAYER
+    run = Run3D(shp, cols=inputs.FRAME_COLS, dtype=torch.bfloat16)
+    for step in range(8):
+        _say(f"3-D page prefill chunk {step}")
+        k, v = inputs.torch_chunk(shp, step, 0, "cpu")
+        run.step(step, _f32(k[0]), _f32(v[0]))
+    torch.cuda.synchronize()
+    return run
+
+
+def test_page_write_3d(page_run):
+    _say("3-D page write parity")
+    assert page_run.ring.head == (8 * 757) % 5788
+    _check_cache(page_run.cache, page_run.orc, "3-D page")
+
+
+def test_page_attention_3d(page_run):
+    shp = page_run.s
+    rng = np.random.default_rng(3)
+    qs = np.unique(np.concatenate([[0, 27, 28, 255, 256, shp.n_new - 1], rng.integers(0, shp.n_new, 36)]))
+    rows = [(int(i), h) for h in range(shp.n_heads) for i in qs]
+    for p in range(2):
+        _say(f"3-D page attention pass {p}")
+        q = inputs.torch_queries(shp, 8, p, 0, "cpu")
+        for n_splits in ((0, 1) if p == 0 else (0,)):
+            got, ref = page_run.attention(q, n_splits=n_splits, rows=rows)
+            mx, mean = assert_attention(got, ref, f"3-D page pass {p} splits {n_splits}")
+            _say(f"  splits={n_splits} max-abs {mx:.4g} mean-abs {mean:.4g}")
+
+
+def test_page_frame_rebase_3d(page_run):
+    d = inputs.rebase_delta_t()
+    _say(f"3-D page frame rebase by {d}")
+    run = page_run
+    v_before = (run.cache.v_codes.clone(), run.cache.v_scales.clone())
+    run.rebase(d)
+    _check_cache(run.cache, run.orc, "3-D page after frame rebase")
+    assert torch.equal(run.cache.v_codes, v_before[0]) and torch.equal(run.cache.v_scales, v_before[1])
