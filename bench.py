@@ -68,6 +68,8 @@ def parse():
     ap.add_argument("--every-pass-steps", type=int, default=5,
                     help="steps timed with the chunk written again on every denoise pass (0 = skip)")
     ap.add_argument("--rebase-iters", type=int, default=20)
+    ap.add_argument("--rope3d-steps", type=int, default=10,
+                    help="timed steps of the 3-D (frame, row, column) rotary form (0 = skip)")
     ap.add_argument("--splits", type=int, default=0, help="attention key splits (0 = default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-naive", action="store_true")
@@ -350,6 +352,51 @@ def main():
         naive = run_naive(args, K, inputs, shp, rope, chunks, qpool, outs, ws, torch, dev, pre)
 
     # ---- CPU oracle on a bounded sample -----------------------------------------------
+    # ---- the 3-D (frame, row, column) rotary form ----------------------------------
+    # the same step with every token at (t, y, x): one latent frame per chunk on a
+    # 28-column grid; per step one (cos, sin) row fill for the chunk's tokens, the
+    # row-driven write of 60 layers and 240 row-driven attention calls; then the
+    # frame-only rebase of all 60 layers
+    rope3d = None
+    if args.rope3d_steps > 0:
+        npr = inputs.axis_pairs(D)
+        ring3 = ring.copy()
+
+        def step3d(frame):
+            rows = K.Rope3DRows(inputs.chunk_coords(N, frame), D, npr)
+            k, v = chunks[frame % pool]
+            K.kv_write_rope_quant_rows(cache, ring3, 0, k, v, rows.cs)
+            K.kvr_ring_after_write(ring3, W, N)
+            start = K.kvr_ring_logical_start(ring3, W)
+            for p in range(P):
+                for layer in range(L):
+                    K.attn_fp8_window_rows(cache, layer, start, ring3.n_valid, qpool[p * L + layer], rows.cs,
+                                           out=outs[layer], n_splits=args.splits, ws=ws)
+        for f in range(2):
+            step3d(f)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for f in range(args.rope3d_steps):
+            step3d(2 + f)
+        t1.record()
+        torch.cuda.synchronize()
+        ms3 = t0.elapsed_time(t1) / args.rope3d_steps
+        d_t = inputs.rebase_delta_t()
+        for i in range(3):
+            K.kv_delta_rebase_axes(cache, ring3, 0, L, (d_t if i % 2 == 0 else -d_t, 0, 0), npr)
+        torch.cuda.synchronize()
+        r0.record()
+        for i in range(args.rebase_iters):
+            K.kv_delta_rebase_axes(cache, ring3, 0, L, (d_t if i % 2 == 0 else -d_t, 0, 0), npr)
+        r1.record()
+        torch.cuda.synchronize()
+        reb3 = r0.elapsed_time(r1) / args.rebase_iters
+        rope3d = {"ms_per_step": round(ms3, 5), "steps": args.rope3d_steps, "axis_pairs": list(npr),
+                  "frame_cols": inputs.FRAME_COLS, "frame_rebase_ms": round(reb3, 4),
+                  "frame_rebase_GBps": round(reb_bytes / (reb3 * 1e-3) / 1e9, 1), "frame_delta": d_t}
+        log(f"3-D rotary form: {ms3:.4f} ms/step; frame rebase by {d_t}: {reb3:.4f} ms")
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(K, inputs, shp, cache, qpool, ring, chunks, torch)
@@ -405,6 +452,7 @@ def main():
         },
         "naive": naive,
         "write_every_pass": every_pass,
+        "rope3d": rope3d,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
