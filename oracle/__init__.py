@@ -96,6 +96,15 @@ def lib():
                                            ctypes.c_int, ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
                                            _c_f32p, _c_i64p, _c_i32p, ctypes.c_double,
                                            ctypes.c_double, _c_i32p, ctypes.c_int, _c_f64p]
+        L.orc_write3d_list.argtypes = [_c_u8p, _c_u8p, _c_f32p, _c_f32p, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, _c_i32p, _c_i64p, _c_i32p, _c_f32p, _c_f32p,
+                                       ctypes.c_int, ctypes.c_double]
+        L.orc_rebase3d_list.argtypes = [_c_u8p, _c_f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        _c_i32p, ctypes.c_int32, _c_i64p, _c_i32p, ctypes.c_double]
+        L.orc_attention_list3d.argtypes = [_c_u8p, _c_u8p, _c_f32p, _c_f32p, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, _c_i32p, ctypes.c_int32,
+                                           _c_f32p, _c_i64p, _c_i32p, ctypes.c_double,
+                                           ctypes.c_double, _c_i32p, ctypes.c_int, _c_f64p]
         _lib = L
     return _lib
 
@@ -338,6 +347,83 @@ def attention3d(cache: LayerCache, start: int, n_valid: int, q, q_coords, npairs
     if rows is None:
         return out.reshape(n_q, H, D)
     return out
+
+
+# --------------------------------------------------------------------------
+# explicit slot lists (a fixed prefix beside the ring)
+# --------------------------------------------------------------------------
+def _slots(slots) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(slots, np.int32).reshape(-1))
+
+
+def write3d_list(cache: LayerCache, slots, coords, npairs, k_new, v_new, base: float = 10000.0) -> None:
+    """Token j of the chunk (coordinates coords[j]) into slot slots[j]."""
+    k = _f32(k_new)
+    v = _f32(v_new)
+    N = k.shape[0]
+    sl = _slots(slots)
+    assert sl.size == N and k.shape == (N, cache.H, cache.D) and v.shape == k.shape
+    assert sl.min() >= 0 and sl.max() < cache.W
+    c = np.ascontiguousarray(np.asarray(coords, np.int64).reshape(N, 3))
+    lib().orc_write3d_list(_p(cache.k_codes, _c_u8p), _p(cache.v_codes, _c_u8p),
+                           _p(cache.k_scales, _c_f32p), _p(cache.v_scales, _c_f32p),
+                           cache.H, cache.D, cache.W, _p(sl, _c_i32p), _p(c, _c_i64p),
+                           _p(_npairs(npairs), _c_i32p), _p(k, _c_f32p), _p(v, _c_f32p), N, float(base))
+
+
+def rebase3d_list(cache: LayerCache, slots, delta, npairs, base: float = 10000.0) -> None:
+    """The K rows at the listed slots rotated by -delta (a (t, y, x) triple), re-quantised."""
+    sl = _slots(slots)
+    assert sl.size == 0 or (sl.min() >= 0 and sl.max() < cache.W)
+    d = np.ascontiguousarray(np.asarray(delta, np.int64).reshape(3))
+    lib().orc_rebase3d_list(_p(cache.k_codes, _c_u8p), _p(cache.k_scales, _c_f32p), cache.H, cache.D,
+                            cache.W, _p(sl, _c_i32p), sl.size, _p(d, _c_i64p), _p(_npairs(npairs), _c_i32p),
+                            float(base))
+
+
+def attention3d_list(cache: LayerCache, slots, q, q_coords, npairs, sm_scale: float | None = None,
+                     base: float = 10000.0, rows=None) -> np.ndarray:
+    """fp64 attention over the keys at the listed slots, query i rotated at q_coords[i]."""
+    qq = _f32(q)
+    n_q, H, D = qq.shape
+    sl = _slots(slots)
+    assert sl.size >= 1 and sl.min() >= 0 and sl.max() < cache.W
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(D)
+    if rows is None:
+        qh = np.array([(i, h) for i in range(n_q) for h in range(H)], np.int32).reshape(-1, 2)
+    else:
+        qh = np.ascontiguousarray(np.asarray(rows, np.int32).reshape(-1, 2))
+    c = np.ascontiguousarray(np.asarray(q_coords, np.int64).reshape(n_q, 3))
+    out = np.zeros((qh.shape[0], D), np.float64)
+    lib().orc_attention_list3d(_p(cache.k_codes, _c_u8p), _p(cache.v_codes, _c_u8p),
+                               _p(cache.k_scales, _c_f32p), _p(cache.v_scales, _c_f32p),
+                               H, D, cache.W, _p(sl, _c_i32p), sl.size, _p(qq, _c_f32p), _p(c, _c_i64p),
+                               _p(_npairs(npairs), _c_i32p), float(base), float(sm_scale),
+                               _p(qh, _c_i32p), qh.shape[0], _p(out, _c_f64p))
+    if rows is None:
+        return out.reshape(n_q, H, D)
+    return out
+
+
+class PrefixRing:
+    """Brute-force slot model of a cache whose slots [0, n_prefix) hold a fixed
+    prefix and whose slots [n_prefix, W) are a ring of the last W - n_prefix
+    tokens (the deque model of RingDeque, offset by the prefix)."""
+
+    def __init__(self, W: int, n_prefix: int):
+        assert 0 <= n_prefix < W
+        self.P, self.ring = n_prefix, RingDeque(W - n_prefix)
+
+    def write(self, n: int):
+        return [self.P + s for s in self.ring.write(n)]
+
+    def key_slots(self):
+        """Prefix slots, then the ring's valid slots in logical order."""
+        return list(range(self.P)) + [self.P + s for s in self.ring.logical_slots()]
+
+    def ring_slots(self):
+        return [self.P + s for s in self.ring.logical_slots()]
 
 
 def window_dequant(cache: LayerCache, start: int, n_valid: int):

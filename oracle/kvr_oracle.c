@@ -469,6 +469,113 @@ void orc_attention_rows3d(const uint8_t *k_codes, const uint8_t *v_codes,
     }
 }
 
+/* ------------------------------------------------------------------------ */
+/* The same three steps over explicit slot lists: a cache whose first slots  */
+/* hold a fixed prefix (written once, never overwritten) and whose other     */
+/* slots form the ring.  Reading where the pages are silent: the prefix keeps */
+/* its own coordinates, so a frame reset rotates the ring's rows only.       */
+/* Pins: with the ring's slots in logical order these are orc_write3d,       */
+/* orc_rebase3d and orc_attention_rows3d bit for bit; attention does not     */
+/* depend on the order of the key list (keys are a set).                     */
+/* ------------------------------------------------------------------------ */
+/* new token j goes to slots[j] */
+void orc_write3d_list(uint8_t *k_codes, uint8_t *v_codes, float *k_scales, float *v_scales,
+                      int H, int D, int W, const int32_t *slots, const int64_t *coords,
+                      const int32_t npairs[3], const float *k_new, const float *v_new, int N,
+                      double base)
+{
+    (void)W;
+#pragma omp parallel
+    {
+        float *y = (float *)malloc(sizeof(float) * (size_t)D);
+#pragma omp for collapse(2) schedule(static)
+        for (int j = 0; j < N; ++j) {
+            for (int h = 0; h < H; ++h) {
+                const float *kr = k_new + ((size_t)j * H + h) * D;
+                const float *vr = v_new + ((size_t)j * H + h) * D;
+                size_t row = (size_t)h * W + slots[j];
+                orc_rope3d_row(kr, y, D, coords + 3 * (size_t)j, npairs, base);
+                orc_quant_row(y, D, k_codes + row * D, &k_scales[row]);
+                orc_quant_row(vr, D, v_codes + row * D, &v_scales[row]);
+            }
+        }
+        free(y);
+    }
+}
+
+/* the K rows at slots[0 .. n-1] rotated by R(-delta) and re-quantised */
+void orc_rebase3d_list(uint8_t *k_codes, float *k_scales, int H, int D, int W,
+                       const int32_t *slots, int32_t n, const int64_t delta[3],
+                       const int32_t npairs[3], double base)
+{
+    const int64_t neg[3] = {-delta[0], -delta[1], -delta[2]};
+#pragma omp parallel
+    {
+        float *x = (float *)malloc(sizeof(float) * (size_t)D);
+#pragma omp for collapse(2) schedule(static)
+        for (int h = 0; h < H; ++h) {
+            for (int i = 0; i < n; ++i) {
+                size_t row = (size_t)h * W + slots[i];
+                orc_dequant_row(k_codes + row * D, k_scales[row], D, x);
+                orc_rope3d_row(x, x, D, neg, npairs, base);
+                orc_quant_row(x, D, k_codes + row * D, &k_scales[row]);
+            }
+        }
+        free(x);
+    }
+}
+
+/* attention of the listed (query, head) pairs over the keys at slots[0 .. n_keys-1] */
+void orc_attention_list3d(const uint8_t *k_codes, const uint8_t *v_codes,
+                          const float *k_scales, const float *v_scales,
+                          int H, int D, int W, const int32_t *slots, int32_t n_keys,
+                          const float *q, const int64_t *q_coords, const int32_t npairs[3],
+                          double base, double sm_scale, const int32_t *qh, int n_list,
+                          double *out)
+{
+#pragma omp parallel
+    {
+        float *qr = (float *)malloc(sizeof(float) * (size_t)D);
+        float *kh = (float *)malloc(sizeof(float) * (size_t)D);
+        double *sc = (double *)malloc(sizeof(double) * (size_t)(n_keys > 0 ? n_keys : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int t = 0; t < n_list; ++t) {
+            int i = qh[2 * t], h = qh[2 * t + 1];
+            double *o = out + (size_t)t * D;
+            orc_rope3d_row(q + ((size_t)i * H + h) * D, qr, D, q_coords + 3 * (size_t)i, npairs, base);
+            double m = -INFINITY;
+            for (int j = 0; j < n_keys; ++j) {
+                size_t row = (size_t)h * W + slots[j];
+                orc_dequant_row(k_codes + row * D, k_scales[row], D, kh);
+                double s = 0.0;
+                for (int d = 0; d < D; ++d) s += (double)qr[d] * (double)kh[d];
+                s *= sm_scale;
+                sc[j] = s;
+                if (s > m) m = s;
+            }
+            double l = 0.0;
+            for (int j = 0; j < n_keys; ++j) {
+                sc[j] = exp(sc[j] - m);
+                l += sc[j];
+            }
+            for (int d = 0; d < D; ++d) o[d] = 0.0;
+            for (int j = 0; j < n_keys; ++j) {
+                size_t row = (size_t)h * W + slots[j];
+                double w = sc[j] / l;
+                const uint8_t *vc = v_codes + row * D;
+                float vsc = v_scales[row];
+                for (int d = 0; d < D; ++d) {
+                    float vh = (float)orc_e4m3_decode(vc[d]) * vsc;
+                    o[d] += w * (double)vh;
+                }
+            }
+        }
+        free(qr);
+        free(kh);
+        free(sc);
+    }
+}
+
 /* rows x [n][D] rotated at 3-D coordinates coords[n][3] into y [n][D] */
 void orc_rope3d_rows(const float *x, float *y, int64_t n, int D, const int64_t *coords,
                      const int32_t npairs[3], double base)

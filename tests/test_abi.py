@@ -242,6 +242,82 @@ def test_rope_table_validation():
     assert lib.kv_rope_table_fill(FAKE, 0, 10, 128, 1.0, None) == K.KVR_EINVAL
 
 
+def _ax(*v, ct=ctypes.c_int32):
+    return (ct * 3)(*v)
+
+
+@no_gpu
+def test_rope3d_table_validation():
+    lib = K.lib()
+    coords = FAKE + 0x1000000
+    ok_pairs = _ax(22, 21, 21)
+    assert lib.kv_rope3d_table_fill(FAKE, coords, 0, 128, ok_pairs, 1e4, None) == K.KVR_EINVAL
+    assert lib.kv_rope3d_table_fill(FAKE, coords, 10, 100, ok_pairs, 1e4, None) == K.KVR_EUNSUPPORTED
+    assert lib.kv_rope3d_table_fill(FAKE + 4, coords, 10, 128, ok_pairs, 1e4, None) == K.KVR_EALIGN
+    assert lib.kv_rope3d_table_fill(FAKE, coords + 2, 10, 128, ok_pairs, 1e4, None) == K.KVR_EALIGN
+    assert lib.kv_rope3d_table_fill(FAKE, 0, 10, 128, ok_pairs, 1e4, None) == K.KVR_EINVAL
+    assert lib.kv_rope3d_table_fill(FAKE, coords, 10, 128, ok_pairs, 1.0, None) == K.KVR_EINVAL
+    # the groups must cover head_dim/2 pairs, with at least one frame pair
+    assert lib.kv_rope3d_table_fill(FAKE, coords, 10, 128, _ax(22, 21, 20), 1e4, None) == K.KVR_EINVAL
+    assert lib.kv_rope3d_table_fill(FAKE, coords, 10, 128, _ax(0, 32, 32), 1e4, None) == K.KVR_EINVAL
+    assert lib.kv_rope3d_table_fill(FAKE, coords, 10, 128, _ax(66, -1, -1), 1e4, None) == K.KVR_EINVAL
+    assert "axis_pairs" in K.kvr_last_error()
+    assert lib.kv_rope3d_table_fill(FAKE, coords, 10, 128, None, 1e4, None) == K.KVR_EINVAL
+
+
+@no_gpu
+def test_row_driven_write_validation():
+    lib = K.lib()
+    c, r = _cache(), K.kvr_ring_init()
+    rows = FAKE + 0x4000000
+
+    def call(cache=c, ring=r, n_new=757, cs=rows, k=FAKE + 0x5000000):
+        return lib.kv_write_rope_quant_rows(ctypes.byref(cache), ctypes.byref(ring), 0, 1, k,
+                                            FAKE + 0x6000000, K.KVR_BF16, 0, n_new, cs, None)
+    assert call(cs=0) == K.KVR_EINVAL
+    assert call(cs=rows + 8) == K.KVR_EALIGN
+    assert call(n_new=0) == K.KVR_EINVAL
+    assert call(n_new=5789) == K.KVR_EINVAL
+    assert call(k=FAKE + 8) == K.KVR_EALIGN
+    assert call(ring=K.kvr_ring(5788, 0, 0)) == K.KVR_EINVAL
+    assert call(cache=_cache(D=96)) == K.KVR_EUNSUPPORTED
+
+
+@no_gpu
+def test_axis_rebase_validation():
+    lib = K.lib()
+    c = _cache()
+    r = K.kvr_ring(0, 5788, 100)
+    d = _ax(5, 0, 0, ct=ctypes.c_int64)
+
+    def call(n_layers=1, delta=d, pairs=_ax(22, 21, 21), base=1e4, ring=r, cache=c):
+        return lib.kv_delta_rebase_axes(ctypes.byref(cache), ctypes.byref(ring), 0, n_layers, delta, pairs,
+                                        base, None)
+    assert call(n_layers=2) == K.KVR_EINVAL
+    assert call(delta=None) == K.KVR_EINVAL
+    assert call(pairs=_ax(21, 21, 21)) == K.KVR_EINVAL
+    assert call(pairs=None) == K.KVR_EINVAL
+    assert call(base=0.5) == K.KVR_EINVAL
+    assert call(ring=K.kvr_ring(0, 6000, 100)) == K.KVR_EINVAL
+    assert call(cache=_cache(D=32)) == K.KVR_EUNSUPPORTED
+
+
+@no_gpu
+def test_row_driven_attention_validation():
+    lib = K.lib()
+    c = _cache()
+    rows = FAKE + 0xA000000
+
+    def call(cs=rows, n_valid=5788, n_splits=1, q=FAKE + 0x7000000, ws=None, ws_bytes=0):
+        return lib.attn_fp8_window_rows(ctypes.byref(c), 0, 0, n_valid, q, K.KVR_BF16, 757, cs, 0.088,
+                                        FAKE + 0x8000000, n_splits, ws, ws_bytes, None)
+    assert call(cs=0) == K.KVR_EINVAL
+    assert call(cs=rows + 4) == K.KVR_EALIGN
+    assert call(n_valid=0) == K.KVR_EINVAL
+    assert call(q=FAKE + 2) == K.KVR_EALIGN
+    assert call(n_splits=4) == K.KVR_EINVAL                    # workspace required
+
+
 def test_page_shape_constants_fixture():
     from kv_cache_attention_ring_amd import inputs
     vals = {}

@@ -183,3 +183,79 @@ def test_attention3d_all_temporal_is_1d_and_frame_rebase_keeps_outputs():
     c4 = c3.copy()
     oracle.rebase3d(c4, 0, 4 * N, (0, 0, 0), npr, BASE)
     assert np.array_equal(c4.k_codes, c3.k_codes) and np.array_equal(c4.k_scales, c3.k_scales)
+
+
+# ---------------------------------------------------------------------------
+# a fixed prefix beside the ring (explicit slot lists)
+# ---------------------------------------------------------------------------
+def test_slot_lists_reduce_to_the_ring_functions():
+    """With no prefix and the ring's slots in logical order, the list forms are
+    the ring forms bit for bit."""
+    shp = inputs.TINY_WRAP
+    H, D, W, N = shp.n_heads, shp.head_dim, shp.window, shp.n_new
+    npr = inputs.axis_pairs(D)
+    a, b = oracle.LayerCache(H, D, W), oracle.LayerCache(H, D, W)
+    pr = oracle.PrefixRing(W, 0)
+    for s in range(9):
+        k, v = inputs.np_chunk(shp, s)
+        cc = inputs.chunk_coords(N, s, cols=5)
+        oracle.write3d_list(a, pr.write(N), cc, npr, k, v)
+        oracle.write3d(b, s * N, cc, npr, k, v)
+    for f in ("k_codes", "v_codes", "k_scales", "v_scales"):
+        assert np.array_equal(getattr(a, f), getattr(b, f)), f
+    start, n_valid = pr.ring_slots()[0], pr.ring.n_valid
+    q = inputs.np_queries(shp, 9, 0, workload="test")
+    x = oracle.attention3d_list(a, pr.key_slots(), q, cc, npr)
+    y = oracle.attention3d(b, start, n_valid, q, cc, npr)
+    assert np.array_equal(x, y)
+    oracle.rebase3d_list(a, pr.ring_slots(), (4, 0, 0), npr)
+    oracle.rebase3d(b, start, n_valid, (4, 0, 0), npr)
+    assert np.array_equal(a.k_codes, b.k_codes) and np.array_equal(a.k_scales, b.k_scales)
+
+
+def test_prefix_ring_slots_and_key_order_invariance():
+    W, P, N = 100, 12, 16
+    pr = oracle.PrefixRing(W, P)
+    seen = []
+    for _ in range(12):
+        new = pr.write(N)
+        assert all(P <= s < W for s in new)
+        seen += new
+    # the ring holds the last W - P tokens in slots P + (t mod (W - P))
+    assert seen == [P + t % (W - P) for t in range(12 * N)]
+    ks = pr.key_slots()
+    assert ks[:P] == list(range(P)) and sorted(ks) == list(range(W))
+    # attention over a set of keys does not depend on their order
+    rng = np.random.default_rng(21)
+    H, D = 2, 64
+    c = oracle.LayerCache(H, D, W)
+    c.k_codes[:] = rng.integers(0, 0x7F, c.k_codes.shape).astype(np.uint8) & 0x77
+    c.v_codes[:] = rng.integers(0, 0xFF, c.v_codes.shape).astype(np.uint8) & 0xF7
+    c.k_scales[:] = rng.uniform(0.001, 0.005, c.k_scales.shape)
+    c.v_scales[:] = rng.uniform(0.001, 0.005, c.v_scales.shape)
+    q = rng.standard_normal((5, H, D)).astype(np.float32)
+    qc = np.stack([np.arange(5), np.zeros(5), np.arange(5)], 1)
+    npr = inputs.axis_pairs(D)
+    a = oracle.attention3d_list(c, ks, q, qc, npr)
+    b = oracle.attention3d_list(c, rng.permutation(ks), q, qc, npr)
+    assert np.abs(a - b).max() <= 1e-12
+
+
+def test_frame_rebase_leaves_the_prefix():
+    shp = inputs.TINY
+    H, D, W, N = shp.n_heads, shp.head_dim, shp.window, shp.n_new
+    P = 10
+    npr = inputs.axis_pairs(D)
+    c = oracle.LayerCache(H, D, W)
+    pr = oracle.PrefixRing(W, P)
+    kp, vp = inputs.np_chunk(shp, 99)
+    oracle.write3d_list(c, range(P), np.stack([np.full(P, -1), np.arange(P) // 5, np.arange(P) % 5], 1),
+                        npr, kp[:P], vp[:P])
+    for s in range(3):
+        k, v = inputs.np_chunk(shp, s)
+        oracle.write3d_list(c, pr.write(N), inputs.chunk_coords(N, s, cols=5), npr, k, v)
+    before = c.copy()
+    oracle.rebase3d_list(c, pr.ring_slots(), (3, 0, 0), npr)
+    assert np.array_equal(c.k_codes[:, :P], before.k_codes[:, :P])
+    assert np.array_equal(c.k_scales[:, :P], before.k_scales[:, :P])
+    assert not np.array_equal(c.k_codes[:, P:], before.k_codes[:, P:])
