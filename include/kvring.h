@@ -56,13 +56,20 @@ extern "C" {
 
 typedef enum { KVR_F32 = 0, KVR_BF16 = 1 } kvr_dtype;
 
-/* Device cache buffers and their shape.  [AI-cache] */
+/* Device cache buffers and their shape.  [AI-cache]
+ * n_prefix (0 for a pure ring): slots [0, n_prefix) of every head hold a
+ * fixed prefix written once with kv_write_prefix_rows and never moved; the
+ * ring is slots [n_prefix, window), capacity window - n_prefix.  Ring state
+ * (kvr_ring) and the ring arguments of every call (head, slot_start,
+ * n_valid) are relative to the ring: ring slot s is cache slot n_prefix + s,
+ * and the kvr_ring_* functions take the ring capacity as their window. */
 typedef struct {
     uint8_t *k_codes;   /* [L][H][W][D] */
     uint8_t *v_codes;   /* [L][H][W][D] */
     float   *k_scales;  /* [L][H][W]    */
     float   *v_scales;  /* [L][H][W]    */
     int32_t  n_layers, n_heads, head_dim, window;
+    int32_t  n_prefix;  /* 0 <= n_prefix < window */
 } kvr_cache;
 
 /* Ring state, a host POD shared by all layers of a cache.  [AI-cache]
@@ -144,7 +151,9 @@ int32_t kv_delta_rebase(const kvr_cache *cache, const kvr_ring *ring, int32_t la
  * [AI-cache] [NC-cache] [AI-latency].  For every head h and query i < n_q:
  *   O[i][h] = sum_j softmax_j(softmax_scale * q_i . k^_j) v^_j
  * over the n_valid cached keys of `layer` at slots (slot_start + j) mod window
- * (non-causal; every query sees every valid key), q_i rotated at position
+ * (non-causal; every query sees every valid key; with a prefix, the n_prefix
+ * prefix rows come first and the ring's keys are at cache slots n_prefix +
+ * (slot_start + j) mod (window - n_prefix)), q_i rotated at position
  * q_pos_start + i with frequencies rope_base^(-2i/head_dim), k^ / v^ the
  * dequantised cache rows.  Keys are visited in
  * this logical order, so a linear window (slot_start = 0) holding the same
@@ -253,6 +262,19 @@ int32_t attn_fp8_window_rows(const kvr_cache *cache, int32_t layer, int32_t slot
                              int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
                              const float *q_cs_rows, float softmax_scale, uint16_t *out,
                              int32_t n_splits, void *ws, size_t ws_bytes, void *stream);
+
+/* Writes n_tok prefix tokens (rotation of token j from row j of cs_rows,
+ * device [n_tok][head_dim/2][2] fp32) to prefix slots slot0 .. slot0+n_tok-1
+ * of layers layer0 .. layer0+n_layers-1, quantised as in kv_write_rope_quant.
+ * The prefix is the reading taken for the window's fixed, non-rolling part:
+ * its rows keep their own coordinates, so no rebase touches them; attention
+ * sees them before the ring's keys.  Errors: KVR_EINVAL (null, slot range not
+ * inside [0, n_prefix), layer range), KVR_EALIGN, KVR_EUNSUPPORTED.
+ * [AI-cache] [NC-cache] */
+int32_t kv_write_prefix_rows(const kvr_cache *cache, int32_t slot0, int32_t layer0, int32_t n_layers,
+                             const void *k_new, const void *v_new, kvr_dtype dtype,
+                             int64_t layer_stride_elems, int32_t n_tok, const float *cs_rows,
+                             void *stream);
 
 /* Text of the last error on this thread ("" if none). */
 const char *kvr_last_error(void);

@@ -218,10 +218,13 @@ __device__ __forceinline__ void qwait(u32x4 (&q)[W]) {
 // clobber keeps the compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Cache slot of key idx in logical order: the prefix rows first, then the
+// ring's keys, oldest first (ring slot s is cache slot prefix + s).
 __device__ __forceinline__ int slot_of(const AttnArgs &a, int idx) {
     idx = idx < a.n_valid ? idx : a.n_valid - 1;       // keys past the window: any valid row
-    const int s = a.slot_start + idx;
-    return s >= a.window ? s - a.window : s;
+    if (idx < a.prefix) return idx;
+    const int s = a.slot_start + idx - a.prefix;
+    return a.prefix + (s >= a.cap ? s - a.cap : s);
 }
 
 // Tile streaming.  Every wave loads its eighth of each tile straight into

@@ -37,6 +37,7 @@ struct WriteArgs {
     int64_t layer_stride;            // elements between consecutive layers of k_new/v_new
     const float *cs;                 // rotary table row of position pos_next (pair-major)
     int32_t n_heads, window, head, n_new, layer0, n_layers;
+    int32_t prefix, cap;             // ring slot s is cache slot prefix + s, s < cap
     int32_t dtype;
 };
 hipError_t launch_write(const WriteArgs &a, int head_dim, hipStream_t s);
@@ -45,6 +46,7 @@ struct RebaseArgs {
     uint8_t *k_codes;
     float *k_scales;
     int32_t n_heads, window, start, n_valid, layer0, n_layers;
+    int32_t prefix, cap;             // ring slot s is cache slot prefix + s, s < cap
 };
 hipError_t launch_rebase(const RebaseArgs &a, const CosSinTable &rot, int head_dim, hipStream_t s);
 
@@ -71,7 +73,8 @@ struct AttnArgs {
     uint16_t *out;                    // [n_q][H][D] bf16
     uint16_t *part_o;                 // [splits][n_q][H][D] fp16, normalised rows
     float *part_ml;                   // [splits][n_q][H][2]
-    int32_t n_heads, window, slot_start, n_valid, n_q, dtype;
+    int32_t n_heads, window, slot_start, n_valid, n_q, dtype;   // n_valid: prefix + ring keys
+    int32_t prefix, cap;              // key i < prefix: slot i; else prefix + (slot_start + i - prefix) mod cap
     int32_t n_splits, tiles_per_split;
     float softmax_scale;
 };

@@ -59,8 +59,13 @@ int32_t check_cache(const kvr_cache *c) {
         c->n_heads >= kMaxExtent || c->n_layers >= kMaxExtent)
         return fail(KVR_EINVAL, "cache shape out of range (L=%d H=%d W=%d)", c->n_layers,
                     c->n_heads, c->window);
+    if (c->n_prefix < 0 || c->n_prefix >= c->window)
+        return fail(KVR_EINVAL, "n_prefix %d not in [0,%d)", c->n_prefix, c->window);
     return KVR_OK;
 }
+
+// Ring capacity of a cache: the slots after the fixed prefix.
+int32_t ring_cap(const kvr_cache *c) { return c->window - c->n_prefix; }
 
 int32_t check_ring(const kvr_ring *r, int32_t W) {
     if (!r) return fail(KVR_EINVAL, "ring is NULL");
@@ -178,7 +183,7 @@ int32_t kv_write_rope_quant(const kvr_cache *cache, const kvr_ring *before, int3
                             kvr_dtype dtype, int64_t layer_stride_elems, int32_t n_new,
                             const kvr_rope_table *rope, void *stream) {
     if (int32_t e = check_cache(cache)) return e;
-    const int32_t W = cache->window, D = cache->head_dim;
+    const int32_t W = ring_cap(cache), D = cache->head_dim;
     if (int32_t e = check_ring(before, W)) return e;
     if (int32_t e = check_dtype(dtype)) return e;
     if (!k_new || !v_new) return fail(KVR_EINVAL, "k_new/v_new is NULL");
@@ -203,7 +208,9 @@ int32_t kv_write_rope_quant(const kvr_cache *cache, const kvr_ring *before, int3
     a.layer_stride = n_layers > 1 ? layer_stride_elems : 0;
     a.cs = cs;
     a.n_heads = cache->n_heads;
-    a.window = W;
+    a.window = cache->window;
+    a.prefix = cache->n_prefix;
+    a.cap = W;
     a.head = before->head;
     a.n_new = n_new;
     a.layer0 = layer0;
@@ -216,7 +223,7 @@ int32_t kv_write_rope_quant(const kvr_cache *cache, const kvr_ring *before, int3
 int32_t kv_delta_rebase(const kvr_cache *cache, const kvr_ring *ring, int32_t layer0,
                         int32_t n_layers, int64_t delta, double rope_base, void *stream) {
     if (int32_t e = check_cache(cache)) return e;
-    const int32_t W = cache->window, D = cache->head_dim;
+    const int32_t W = ring_cap(cache), D = cache->head_dim;
     if (int32_t e = check_ring(ring, W)) return e;
     if (layer0 < 0 || n_layers < 1 || layer0 + n_layers > cache->n_layers)
         return fail(KVR_EINVAL, "layers [%d,%d) outside cache of %d", layer0, layer0 + n_layers,
@@ -235,7 +242,9 @@ int32_t kv_delta_rebase(const kvr_cache *cache, const kvr_ring *ring, int32_t la
     a.k_codes = cache->k_codes;
     a.k_scales = cache->k_scales;
     a.n_heads = cache->n_heads;
-    a.window = W;
+    a.window = cache->window;
+    a.prefix = cache->n_prefix;
+    a.cap = W;
     a.start = kvr_ring_logical_start(ring, W);
     a.n_valid = ring->n_valid;
     a.layer0 = layer0;
@@ -246,9 +255,9 @@ int32_t kv_delta_rebase(const kvr_cache *cache, const kvr_ring *ring, int32_t la
 // ---- (a3) FP8 window attention --------------------------------------------
 size_t attn_fp8_window_workspace_bytes(const kvr_cache *cache, int32_t n_q, int32_t n_valid,
                                        int32_t n_splits) {
-    if (!cache || n_q < 1 || n_valid < 1 || n_splits < 0) return 0;
+    if (!cache || n_q < 1 || n_valid < 0 || n_splits < 0 || n_valid + cache->n_prefix < 1) return 0;
     int32_t tps;
-    n_splits = effective_splits(cache->n_heads, n_q, n_valid, n_splits, &tps);
+    n_splits = effective_splits(cache->n_heads, n_q, n_valid + cache->n_prefix, n_splits, &tps);
     return kvr::attn_workspace_bytes(cache->n_heads, cache->head_dim, n_q, n_splits);
 }
 
@@ -278,13 +287,15 @@ int32_t attn_setup(kvr::AttnArgs &a, const kvr_cache *cache, int32_t layer, int3
                    int64_t q_pos_start, float softmax_scale, double rope_base, uint16_t *out,
                    int32_t n_splits, void *ws, size_t ws_bytes, const float *q_cs = nullptr) {
     if (int32_t e = check_cache(cache)) return e;
-    const int32_t W = cache->window, D = cache->head_dim;
+    const int32_t W = ring_cap(cache), D = cache->head_dim;
     if (int32_t e = check_dtype(dtype)) return e;
     if (layer < 0 || layer >= cache->n_layers)
         return fail(KVR_EINVAL, "layer %d outside cache of %d", layer, cache->n_layers);
-    if (n_valid < 1 || n_valid > W) return fail(KVR_EINVAL, "n_valid %d not in [1,%d]", n_valid, W);
+    if (n_valid < (cache->n_prefix > 0 ? 0 : 1) || n_valid > W)
+        return fail(KVR_EINVAL, "n_valid %d not in [%d,%d]", n_valid, cache->n_prefix > 0 ? 0 : 1, W);
     if (slot_start < 0 || slot_start >= W)
         return fail(KVR_EINVAL, "slot_start %d not in [0,%d)", slot_start, W);
+    const int32_t n_keys = n_valid + cache->n_prefix;
     if (n_q < 1 || n_q >= kMaxExtent) return fail(KVR_EINVAL, "n_q %d out of range", n_q);
     if (!q || !out) return fail(KVR_EINVAL, "q/out is NULL");
     if (!aligned16(q) || !aligned16(out)) return fail(KVR_EALIGN, "q/out not 16-byte aligned");
@@ -293,7 +304,7 @@ int32_t attn_setup(kvr::AttnArgs &a, const kvr_cache *cache, int32_t layer, int3
     if (!(rope_base > 1.0) || !isfinite(rope_base)) return fail(KVR_EINVAL, "rotary base must be > 1");
     if (n_splits < 0) return fail(KVR_EINVAL, "n_splits %d < 0", n_splits);
     int32_t tps;
-    n_splits = effective_splits(cache->n_heads, n_q, n_valid, n_splits, &tps);
+    n_splits = effective_splits(cache->n_heads, n_q, n_keys, n_splits, &tps);
     if (int32_t e = check_workspace(kvr::attn_workspace_bytes(cache->n_heads, D, n_q, n_splits), ws, ws_bytes))
         return e;
     if (q_cs && !aligned16(q_cs)) return fail(KVR_EALIGN, "query rotary rows not 16-byte aligned");
@@ -311,9 +322,11 @@ int32_t attn_setup(kvr::AttnArgs &a, const kvr_cache *cache, int32_t layer, int3
     a.q_pos0 = q_pos_start;
     a.out = out;
     a.n_heads = cache->n_heads;
-    a.window = W;
+    a.window = cache->window;
+    a.prefix = cache->n_prefix;
+    a.cap = W;
     a.slot_start = slot_start;
-    a.n_valid = n_valid;
+    a.n_valid = n_keys;
     a.n_q = n_q;
     a.dtype = dtype;
     a.n_splits = n_splits;
@@ -328,8 +341,10 @@ int32_t attn_setup(kvr::AttnArgs &a, const kvr_cache *cache, int32_t layer, int3
 int32_t merge_setup(kvr::AttnArgs &a, const kvr_cache *cache, int32_t n_q, int32_t n_valid,
                     int32_t n_splits, uint16_t *out, void *ws, size_t ws_bytes) {
     if (int32_t e = check_cache(cache)) return e;
-    const int32_t W = cache->window, D = cache->head_dim;
-    if (n_valid < 1 || n_valid > W) return fail(KVR_EINVAL, "n_valid %d not in [1,%d]", n_valid, W);
+    const int32_t W = ring_cap(cache), D = cache->head_dim;
+    if (n_valid < (cache->n_prefix > 0 ? 0 : 1) || n_valid > W)
+        return fail(KVR_EINVAL, "n_valid %d not in [%d,%d]", n_valid, cache->n_prefix > 0 ? 0 : 1, W);
+    n_valid += cache->n_prefix;
     if (n_q < 1 || n_q >= kMaxExtent) return fail(KVR_EINVAL, "n_q %d out of range", n_q);
     if (!out) return fail(KVR_EINVAL, "out is NULL");
     if (!aligned16(out)) return fail(KVR_EALIGN, "out not 16-byte aligned");
@@ -339,7 +354,7 @@ int32_t merge_setup(kvr::AttnArgs &a, const kvr_cache *cache, int32_t n_q, int32
     a = kvr::AttnArgs{};
     a.out = out;
     a.n_heads = cache->n_heads;
-    a.window = W;
+    a.window = cache->window;
     a.n_valid = n_valid;
     a.n_q = n_q;
     a.n_splits = n_splits;
@@ -448,11 +463,54 @@ int32_t kv_write_rope_quant_rows(const kvr_cache *cache, const kvr_ring *before,
                                n_new, &t, stream);
 }
 
+int32_t kv_write_prefix_rows(const kvr_cache *cache, int32_t slot0, int32_t layer0, int32_t n_layers,
+                             const void *k_new, const void *v_new, kvr_dtype dtype,
+                             int64_t layer_stride_elems, int32_t n_tok, const float *cs_rows,
+                             void *stream) {
+    if (int32_t e = check_cache(cache)) return e;
+    const int32_t D = cache->head_dim;
+    if (int32_t e = check_dtype(dtype)) return e;
+    if (!cs_rows || !k_new || !v_new) return fail(KVR_EINVAL, "rotary rows or new rows pointer is NULL");
+    if (!aligned16(cs_rows) || !aligned16(k_new) || !aligned16(v_new))
+        return fail(KVR_EALIGN, "rotary rows or new rows not 16-byte aligned");
+    if (n_tok < 1 || slot0 < 0 || slot0 + n_tok > cache->n_prefix)
+        return fail(KVR_EINVAL, "prefix slots [%d,%d) not inside [0,%d)", slot0, slot0 + n_tok,
+                    cache->n_prefix);
+    if (layer0 < 0 || n_layers < 1 || layer0 + n_layers > cache->n_layers)
+        return fail(KVR_EINVAL, "layers [%d,%d) outside cache of %d", layer0, layer0 + n_layers,
+                    cache->n_layers);
+    const int64_t per_layer = (int64_t)n_tok * cache->n_heads * D;
+    if (n_layers > 1 && (layer_stride_elems < per_layer || layer_stride_elems % 8 != 0))
+        return fail(KVR_EINVAL, "layer_stride_elems %lld must be >= %lld and a multiple of 8",
+                    (long long)layer_stride_elems, (long long)per_layer);
+    // the write kernel with a ring of the whole window starting at slot0: the
+    // tokens land in slots slot0 .. slot0 + n_tok - 1 without wrapping
+    kvr::WriteArgs a{};
+    a.k_codes = cache->k_codes;
+    a.v_codes = cache->v_codes;
+    a.k_scales = cache->k_scales;
+    a.v_scales = cache->v_scales;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.layer_stride = n_layers > 1 ? layer_stride_elems : 0;
+    a.cs = cs_rows;
+    a.n_heads = cache->n_heads;
+    a.window = cache->window;
+    a.prefix = 0;
+    a.cap = cache->window;
+    a.head = slot0;
+    a.n_new = n_tok;
+    a.layer0 = layer0;
+    a.n_layers = n_layers;
+    a.dtype = dtype;
+    return launch_status(kvr::launch_write(a, D, static_cast<hipStream_t>(stream)), "prefix write");
+}
+
 int32_t kv_delta_rebase_axes(const kvr_cache *cache, const kvr_ring *ring, int32_t layer0,
                              int32_t n_layers, const int64_t *delta, const int32_t *axis_pairs,
                              double rope_base, void *stream) {
     if (int32_t e = check_cache(cache)) return e;
-    const int32_t W = cache->window, D = cache->head_dim;
+    const int32_t W = ring_cap(cache), D = cache->head_dim;
     if (int32_t e = check_ring(ring, W)) return e;
     if (int32_t e = check_axis_pairs(axis_pairs, D)) return e;
     if (!delta) return fail(KVR_EINVAL, "delta is NULL");
@@ -473,7 +531,9 @@ int32_t kv_delta_rebase_axes(const kvr_cache *cache, const kvr_ring *ring, int32
     a.k_codes = cache->k_codes;
     a.k_scales = cache->k_scales;
     a.n_heads = cache->n_heads;
-    a.window = W;
+    a.window = cache->window;
+    a.prefix = cache->n_prefix;
+    a.cap = W;
     a.start = kvr_ring_logical_start(ring, W);
     a.n_valid = ring->n_valid;
     a.layer0 = layer0;

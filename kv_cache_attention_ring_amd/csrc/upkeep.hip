@@ -210,7 +210,8 @@ __global__ void __launch_bounds__(kBlock) write_kernel(WriteArgs a) {
     uint8_t *codes = kv ? a.v_codes : a.k_codes;
     float *scales = kv ? a.v_scales : a.k_scales;
     int slot = a.head + j;
-    if (slot >= a.window) slot -= a.window;
+    if (slot >= a.cap) slot -= a.cap;
+    slot += a.prefix;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
         const int h = kUnroll * hg + u;
@@ -243,8 +244,8 @@ __global__ void __launch_bounds__(kBlock) rebase_kernel(RebaseArgs a, CosSinTabl
     for (int u = 0; u < kUnroll; ++u) {
         const int i = min(i0 + u * kRowsPerIter, a.n_valid - 1);
         int slot = a.start + i;
-        if (slot >= a.window) slot -= a.window;
-        rows[u] = lh * a.window + slot;
+        if (slot >= a.cap) slot -= a.cap;
+        rows[u] = lh * a.window + a.prefix + slot;
         const uint8_t *src = a.k_codes + rows[u] * D + lane8 * EPT;
         if constexpr (EPT == 16) {
             const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v *>(src));

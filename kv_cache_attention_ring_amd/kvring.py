@@ -42,7 +42,8 @@ class kvr_cache(ctypes.Structure):
     _fields_ = [("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
                 ("k_scales", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
                 ("n_layers", ctypes.c_int32), ("n_heads", ctypes.c_int32),
-                ("head_dim", ctypes.c_int32), ("window", ctypes.c_int32)]
+                ("head_dim", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("n_prefix", ctypes.c_int32)]
 
 
 class kvr_rope_table(ctypes.Structure):
@@ -80,6 +81,8 @@ _SIGS = {
                                     ctypes.POINTER(_I64), ctypes.POINTER(_I32), _F64, _P]),
     "attn_fp8_window_rows": (_I32, [ctypes.POINTER(kvr_cache), _I32, _I32, _I32, _P, _I32, _I32, _P,
                                     _F32, _P, _I32, _P, _SZ, _P]),
+    "kv_write_prefix_rows": (_I32, [ctypes.POINTER(kvr_cache), _I32, _I32, _I32, _P, _P, _I32, _I64, _I32,
+                                    _P, _P]),
     "kvr_last_error": (ctypes.c_char_p, []),
     "kvr_version": (ctypes.c_char_p, []),
 }
@@ -134,20 +137,25 @@ def _dev(t: torch.Tensor, name: str) -> int:
 # device-memory holders (allocation is the caller's, i.e. torch's)
 # ---------------------------------------------------------------------------
 class KVCache:
-    """FP8 K/V codes [L][H][W][D] (uint8) and fp32 scales [L][H][W], on a device."""
+    """FP8 K/V codes [L][H][W][D] (uint8) and fp32 scales [L][H][W], on a device.
+    With n_prefix > 0, slots [0, n_prefix) hold a fixed prefix and the ring is
+    the other ring_window = window - n_prefix slots."""
 
-    def __init__(self, n_layers: int, n_heads: int, head_dim: int, window: int, device="cuda"):
+    def __init__(self, n_layers: int, n_heads: int, head_dim: int, window: int, device="cuda",
+                 n_prefix: int = 0):
         self.shape = (n_layers, n_heads, window, head_dim)
         self.k_codes = torch.zeros(self.shape, dtype=torch.uint8, device=device)
         self.v_codes = torch.zeros(self.shape, dtype=torch.uint8, device=device)
         self.k_scales = torch.zeros(self.shape[:3], dtype=torch.float32, device=device)
         self.v_scales = torch.zeros(self.shape[:3], dtype=torch.float32, device=device)
         self.n_layers, self.n_heads, self.head_dim, self.window = n_layers, n_heads, head_dim, window
+        self.n_prefix = int(n_prefix)
+        self.ring_window = window - self.n_prefix
 
     def desc(self) -> kvr_cache:
         return kvr_cache(self.k_codes.data_ptr(), self.v_codes.data_ptr(),
                          self.k_scales.data_ptr(), self.v_scales.data_ptr(),
-                         self.n_layers, self.n_heads, self.head_dim, self.window)
+                         self.n_layers, self.n_heads, self.head_dim, self.window, self.n_prefix)
 
     @property
     def nbytes(self) -> int:
@@ -271,6 +279,18 @@ def kv_write_rope_quant_rows(cache: KVCache, before: kvr_ring, layer0: int, k_ne
     _check(lib().kv_write_rope_quant_rows(ctypes.byref(c), ctypes.byref(before), layer0, n_layers,
                                           _dev(k_new, "k_new"), _dev(v_new, "v_new"), _dtype_code(k_new),
                                           stride, n_new, _dev(cs_rows, "cs_rows"), _stream(stream)))
+
+
+def kv_write_prefix_rows(cache: KVCache, slot0: int, layer0: int, k_new: torch.Tensor, v_new: torch.Tensor,
+                         cs_rows: torch.Tensor, stream=None) -> None:
+    """Prefix tokens j -> prefix slots slot0 + j, rotated by cs_rows[j] ([n][D/2][2] fp32)."""
+    n_layers, n_tok, stride = _new_rows(cache, k_new, v_new)
+    if cs_rows.dtype != torch.float32 or cs_rows.shape != (n_tok, cache.head_dim // 2, 2):
+        raise KVRError(KVR_EINVAL, "cs_rows must be fp32 [n_tok][head_dim/2][2]")
+    c = cache.desc()
+    _check(lib().kv_write_prefix_rows(ctypes.byref(c), int(slot0), layer0, n_layers, _dev(k_new, "k_new"),
+                                      _dev(v_new, "v_new"), _dtype_code(k_new), stride, n_tok,
+                                      _dev(cs_rows, "cs_rows"), _stream(stream)))
 
 
 def kv_delta_rebase_axes(cache: KVCache, ring: kvr_ring, layer0: int, n_layers: int, delta, axis_pairs,

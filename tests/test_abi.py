@@ -318,6 +318,35 @@ def test_row_driven_attention_validation():
     assert call(n_splits=4) == K.KVR_EINVAL                    # workspace required
 
 
+@no_gpu
+def test_prefix_validation():
+    lib = K.lib()
+    rows = FAKE + 0x4000000
+
+    def pre(n_prefix=489, slot0=0, n_tok=489, cs=rows):
+        c = K.kvr_cache(FAKE, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000, 1, 12, 128, 5788, n_prefix)
+        return lib.kv_write_prefix_rows(ctypes.byref(c), slot0, 0, 1, FAKE + 0x5000000, FAKE + 0x6000000,
+                                        K.KVR_BF16, 0, n_tok, cs, None)
+    assert pre(n_prefix=5788) == K.KVR_EINVAL              # the ring needs at least one slot
+    assert pre(n_prefix=-1) == K.KVR_EINVAL
+    assert pre(n_tok=490) == K.KVR_EINVAL                  # past the prefix
+    assert pre(slot0=400, n_tok=100) == K.KVR_EINVAL
+    assert pre(n_tok=0) == K.KVR_EINVAL
+    assert pre(n_prefix=0, n_tok=1) == K.KVR_EINVAL        # no prefix to write
+    assert pre(cs=rows + 4) == K.KVR_EALIGN
+    # the ring of a prefixed cache has window - n_prefix slots
+    c = K.kvr_cache(FAKE, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000, 1, 12, 128, 5788, 489)
+    assert _write(c, K.kvr_ring(5299, 0, 0), 757, _table()) == K.KVR_EINVAL
+    assert _write(c, K.kvr_ring(0, 0, 0), 5300, _table()) == K.KVR_EINVAL
+    assert _attn(c, 5300) == K.KVR_EINVAL
+    assert _attn(c, 5299, slot_start=5299) == K.KVR_EINVAL
+    # with a prefix, a call over the prefix alone (empty ring) is valid input;
+    # its workspace covers the prefix keys
+    assert lib.attn_fp8_window_workspace_bytes(ctypes.byref(c), 757, 0, 2) == _ws_bytes(2 * 757 * 12, 128)
+    r = K.kvr_ring(0, 5300, 0)
+    assert lib.kv_delta_rebase(ctypes.byref(c), ctypes.byref(r), 0, 1, 5, 1e4, None) == K.KVR_EINVAL
+
+
 def test_page_shape_constants_fixture():
     from kv_cache_attention_ring_amd import inputs
     vals = {}

@@ -195,3 +195,113 @@ def test_page_frame_rebase_3d(page_run):
     run.rebase(d)
     _check_cache(run.cache, run.orc, "3-D page after frame rebase")
     assert torch.equal(run.cache.v_codes, v_before[0]) and torch.equal(run.cache.v_scales, v_before[1])
+
+
+# ---------------------------------------------------------------------------
+# a fixed prefix beside the ring
+# ---------------------------------------------------------------------------
+class PrefixRun3D:
+    """Prefix + ring cache (3-D rows) and the oracle's slot-list form side by side."""
+
+    def __init__(self, shape, n_prefix, cols, dtype=torch.float32, pre_workload="test"):
+        self.s, self.P, self.cols, self.dtype = shape, n_prefix, cols, dtype
+        H, D, W = shape.n_heads, shape.head_dim, shape.window
+        self.cap = W - n_prefix
+        self.npr = inputs.axis_pairs(D)
+        self.cache = K.KVCache(1, H, D, W, n_prefix=n_prefix)
+        self.ring = K.kvr_ring_init()
+        self.orc = oracle.LayerCache(H, D, W)
+        self.model = oracle.PrefixRing(W, n_prefix)
+        self.t_shift = 0
+        # the prefix: one frame at t = -1, written in two pieces
+        pre_shape = inputs.Shape("pre", 1, H, D, W, n_prefix)
+        kp, vp = inputs.np_chunk(pre_shape, 0, workload=pre_workload)
+        if dtype == torch.bfloat16:
+            kp = _f32(torch.from_numpy(kp).to(dtype))
+            vp = _f32(torch.from_numpy(vp).to(dtype))
+        j = np.arange(n_prefix)
+        pc = np.stack([np.full(n_prefix, -1), j // cols, j % cols], 1)
+        rows = K.Rope3DRows(pc, D, self.npr)
+        h = n_prefix // 2
+        for a, b in ((0, h), (h, n_prefix)):
+            K.kv_write_prefix_rows(self.cache, a, 0, torch.from_numpy(kp[a:b]).to(dtype).cuda(),
+                                   torch.from_numpy(vp[a:b]).to(dtype).cuda(), rows.cs[a:b].contiguous())
+        oracle.write3d_list(self.orc, range(n_prefix), pc, self.npr, kp, vp)
+
+    def step(self, step, k, v):
+        N = k.shape[0]
+        coords = inputs.chunk_coords(N, step, self.cols) - [self.t_shift, 0, 0]
+        self.coords = coords
+        self.rows = K.Rope3DRows(coords, self.s.head_dim, self.npr)
+        kd = torch.from_numpy(k).to(self.dtype).cuda()
+        vd = torch.from_numpy(v).to(self.dtype).cuda()
+        K.kv_write_rope_quant_rows(self.cache, self.ring, 0, kd, vd, self.rows.cs)
+        oracle.write3d_list(self.orc, self.model.write(N), coords, self.npr, _f32(kd), _f32(vd))
+        K.kvr_ring_after_write(self.ring, self.cap, N)
+
+    def rebase(self, d):
+        K.kv_delta_rebase_axes(self.cache, self.ring, 0, 1, (d, 0, 0), self.npr)
+        oracle.rebase3d_list(self.orc, self.model.ring_slots(), (d, 0, 0), self.npr)
+        self.t_shift += d
+
+    def attention(self, q, n_splits=0, rows=None):
+        qd = torch.from_numpy(q).to(self.dtype).cuda() if isinstance(q, np.ndarray) else q.cuda()
+        start = K.kvr_ring_logical_start(self.ring, self.cap)
+        assert self.ring.n_valid == self.model.ring.n_valid
+        if self.ring.n_valid:
+            assert self.P + start == self.model.ring_slots()[0]
+        out = K.attn_fp8_window_rows(self.cache, 0, start, self.ring.n_valid, qd, self.rows.cs,
+                                     n_splits=n_splits)
+        torch.cuda.synchronize()
+        ref = oracle.attention3d_list(self.orc, self.model.key_slots(), _f32(qd), self.coords, self.npr,
+                                      rows=rows)
+        got = _f32(out)
+        if rows is not None:
+            got = np.stack([got[i, h] for i, h in rows])
+        return got, ref
+
+
+def test_prefix_small_3d():
+    shp = inputs.TINY_WRAP                       # W 100: prefix 12, ring of 88 (chunks of 16 wrap mid-chunk)
+    run = PrefixRun3D(shp, 12, cols=5)
+    _check_cache(run.cache, run.orc, "prefix written")
+    # queries over the prefix alone (empty ring)
+    run.coords = inputs.chunk_coords(shp.n_new, 0, 5)
+    run.rows = K.Rope3DRows(run.coords, shp.head_dim, run.npr)
+    got, ref = run.attention(inputs.np_queries(shp, 0, 0, workload="test"))
+    assert_attention(got, ref, "prefix only")
+    for step in range(9):
+        _say(f"prefix small step {step}")
+        k, v = inputs.np_chunk(shp, step)
+        run.step(step, k, v)
+        _check_cache(run.cache, run.orc, f"prefix step {step}")
+        for p in range(2):
+            got, ref = run.attention(inputs.np_queries(shp, step, p), n_splits=1 + p)
+            assert_attention(got, ref, f"prefix step {step} pass {p}")
+        if step == 4:
+            pre = (run.cache.k_codes[0, :, :12].clone(), run.cache.k_scales[0, :, :12].clone())
+            run.rebase(3)
+            _check_cache(run.cache, run.orc, "prefix after frame rebase")
+            assert torch.equal(run.cache.k_codes[0, :, :12], pre[0])
+            assert torch.equal(run.cache.k_scales[0, :, :12], pre[1])
+
+
+def test_prefix_page_3d():
+    """5788 slots = a 489-token prefix + a ring of 7 x 757."""
+    shp = inputs.PAGE_LAYER
+    run = PrefixRun3D(shp, 489, cols=inputs.FRAME_COLS, dtype=torch.bfloat16)
+    for step in range(8):
+        _say(f"prefix page chunk {step}")
+        k, v = inputs.torch_chunk(shp, step, 0, "cpu")
+        run.step(step, _f32(k[0]), _f32(v[0]))
+    assert run.ring.n_valid == 5299 and run.ring.head == 757
+    _check_cache(run.cache, run.orc, "prefix page")
+    rng = np.random.default_rng(9)
+    qs = np.unique(np.concatenate([[0, 255, 256, shp.n_new - 1], rng.integers(0, shp.n_new, 20)]))
+    rows = [(int(i), h) for h in range(shp.n_heads) for i in qs]
+    q = inputs.torch_queries(shp, 8, 0, 0, "cpu")
+    got, ref = run.attention(q, rows=rows)
+    mx, mean = assert_attention(got, ref, "prefix page attention")
+    _say(f"  max-abs {mx:.4g} mean-abs {mean:.4g}")
+    run.rebase(inputs.rebase_delta_t())
+    _check_cache(run.cache, run.orc, "prefix page after frame rebase")
