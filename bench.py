@@ -397,6 +397,50 @@ def main():
                   "frame_rebase_GBps": round(reb_bytes / (reb3 * 1e-3) / 1e9, 1), "frame_delta": d_t}
         log(f"3-D rotary form: {ms3:.4f} ms/step; frame rebase by {d_t}: {reb3:.4f} ms")
 
+        # the window as a fixed 489-token prefix (one frame at t = -1, written
+        # once) and a ring of 7 x 757 slots; attention sees prefix + ring
+        n_pre = W - 7 * N
+        cap = W - n_pre
+        pcache = K.KVCache(L, H, D, W, device=dev, n_prefix=n_pre)
+        jj = torch.arange(n_pre)
+        prow = K.Rope3DRows(torch.stack([torch.full((n_pre,), -1), jj // inputs.FRAME_COLS,
+                                         jj % inputs.FRAME_COLS], 1), D, npr)
+        pk, pv = inputs.torch_chunk(inputs.Shape("prefix", L, H, D, W, n_pre), 0, 0, dev, n_layers=L)
+        K.kv_write_prefix_rows(pcache, 0, 0, pk, pv, prow.cs)
+        pring = K.kvr_ring_init()
+
+        def step_prefix(frame):
+            rows = K.Rope3DRows(inputs.chunk_coords(N, frame), D, npr)
+            k, v = chunks[frame % pool]
+            K.kv_write_rope_quant_rows(pcache, pring, 0, k, v, rows.cs)
+            K.kvr_ring_after_write(pring, cap, N)
+            start = K.kvr_ring_logical_start(pring, cap)
+            for p in range(P):
+                for layer in range(L):
+                    K.attn_fp8_window_rows(pcache, layer, start, pring.n_valid, qpool[p * L + layer], rows.cs,
+                                           out=outs[layer], n_splits=args.splits, ws=ws)
+        for f in range(8):                                   # fill the ring
+            step_prefix(f)
+        torch.cuda.synchronize()
+        t0.record()
+        for f in range(args.rope3d_steps):
+            step_prefix(8 + f)
+        t1.record()
+        torch.cuda.synchronize()
+        msp = t0.elapsed_time(t1) / args.rope3d_steps
+        r0.record()
+        for i in range(args.rebase_iters):
+            K.kv_delta_rebase_axes(pcache, pring, 0, L, (d_t if i % 2 == 0 else -d_t, 0, 0), npr)
+        r1.record()
+        torch.cuda.synchronize()
+        rebp = r0.elapsed_time(r1) / args.rebase_iters
+        rebp_bytes = 2 * (L * H * cap * D + L * H * cap * 4)
+        rope3d["prefix"] = {"prefix_slots": n_pre, "ring_slots": cap, "ms_per_step": round(msp, 5),
+                            "frame_rebase_ms": round(rebp, 4),
+                            "frame_rebase_GBps": round(rebp_bytes / (rebp * 1e-3) / 1e9, 1)}
+        log(f"3-D form with a {n_pre}-slot prefix: {msp:.4f} ms/step; frame rebase of the ring {rebp:.4f} ms")
+        del pcache, pk, pv
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(K, inputs, shp, cache, qpool, ring, chunks, torch)

@@ -218,13 +218,21 @@ __device__ __forceinline__ void qwait(u32x4 (&q)[W]) {
 // clobber keeps the compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Cache slot of key idx in logical order: the prefix rows first, then the
-// ring's keys, oldest first (ring slot s is cache slot prefix + s).
+// Cache slot of key idx in logical order: with PREFIX, the prefix rows first,
+// then the ring's keys, oldest first (ring slot s is cache slot prefix + s);
+// without, the ring alone (prefix 0, capacity = window).  A separate
+// instantiation keeps the mapping of a pure ring free of the prefix test.
+template <bool PREFIX>
 __device__ __forceinline__ int slot_of(const AttnArgs &a, int idx) {
     idx = idx < a.n_valid ? idx : a.n_valid - 1;       // keys past the window: any valid row
-    if (idx < a.prefix) return idx;
-    const int s = a.slot_start + idx - a.prefix;
-    return a.prefix + (s >= a.cap ? s - a.cap : s);
+    if constexpr (PREFIX) {
+        if (idx < a.prefix) return idx;
+        const int s = a.slot_start + idx - a.prefix;
+        return a.prefix + (s >= a.cap ? s - a.cap : s);
+    } else {
+        const int s = a.slot_start + idx;
+        return s >= a.window ? s - a.window : s;
+    }
 }
 
 // Tile streaming.  Every wave loads its eighth of each tile straight into
@@ -240,7 +248,7 @@ __device__ __forceinline__ int slot_of(const AttnArgs &a, int idx) {
 template <int D>
 constexpr int ops_per_tile() { return D == 128 ? 3 : 2; }
 
-template <int D>
+template <int D, bool PREFIX>
 __device__ __forceinline__ void issue_tile(const AttnArgs &a, const uint8_t *kh, const uint8_t *vh,
                                            const float *scales_h, int tile, uint8_t *buf, int wave) {
     using L = Lds<D>;
@@ -250,7 +258,7 @@ __device__ __forceinline__ void issue_tile(const AttnArgs &a, const uint8_t *kh,
         const int p0 = 64 * wave;
         const int p = p0 + lane;
         const int row = p / CH, pos = p % CH;
-        const uint32_t srow = (uint32_t)slot_of(a, tile * kKT + row) * D;
+        const uint32_t srow = (uint32_t)slot_of<PREFIX>(a, tile * kKT + row) * D;
         const uint32_t offk = srow + 16 * (pos ^ (swz_k<D>(row) & (CH - 1)));
         const uint32_t offv = srow + 16 * (pos ^ (swz_v<D>(row) & (CH - 1)));
         __builtin_amdgcn_global_load_lds(kh + offk, (LDS_AS void *)(buf + 16 * p0), 16, 0, 0);
@@ -260,13 +268,13 @@ __device__ __forceinline__ void issue_tile(const AttnArgs &a, const uint8_t *kh,
         const int p0 = 64 * (wave % 4);
         const int p = p0 + lane;
         const int row = p / CH, pos = p % CH;
-        const uint32_t off = (uint32_t)slot_of(a, tile * kKT + row) * D +
+        const uint32_t off = (uint32_t)slot_of<PREFIX>(a, tile * kKT + row) * D +
                              16 * (pos ^ ((is_k ? swz_k<D>(row) : swz_v<D>(row)) & (CH - 1)));
         __builtin_amdgcn_global_load_lds((is_k ? kh : vh) + off,
                                          (LDS_AS void *)(buf + (is_k ? 0 : L::K_BYTES) + 16 * p0), 16, 0, 0);
     }
     const int key = 16 * (wave % 4) + lane % 16;
-    __builtin_amdgcn_global_load_lds(scales_h + slot_of(a, tile * kKT + key),
+    __builtin_amdgcn_global_load_lds(scales_h + slot_of<PREFIX>(a, tile * kKT + key),
                                      (LDS_AS void *)(buf + L::F_OFF + 256 * wave), 4, 0, 0);
 }
 
@@ -289,7 +297,8 @@ __device__ __forceinline__ void wait_tiles(int later) {
 // QTAB: the queries' rotation comes from (cos, sin) rows, one per query
 // (a.q_cs, [n_q][D/2][2] fp32: the 3-D form, where the angle of a pair is its
 // own axis coordinate times its frequency), instead of position times frequency.
-template <int D, bool BF16, bool QTAB>
+// PREFIX: keys start with the cache's fixed prefix rows (see slot_of).
+template <int D, bool BF16, bool QTAB, bool PREFIX>
 __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     using L = Lds<D>;
     constexpr int CH = L::CH;
@@ -374,7 +383,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     // P tiles reloads its last tile into the spare buffers)
 #pragma unroll
     for (int k = 0; k < P; ++k)
-        issue_tile<D>(a, kh, vh, scales_h, min(t0 + k, t1 - 1), tiles + k * L::BUF, wave);
+        issue_tile<D, PREFIX>(a, kh, vh, scales_h, min(t0 + k, t1 - 1), tiles + k * L::BUF, wave);
     qwait<P * ops_per_tile<D>()>(qraw);
     if constexpr (QTAB) {
         // issued before the tiles, so the wait above covered them too; order
@@ -751,7 +760,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
         if (u + P < n) {                               // stream tile t0+u+P
             int bl = bcur + P;
             bl = bl >= kNBuf ? bl - kNBuf : bl;
-            issue_tile<D>(a, kh, vh, scales_h, t0 + u + P, tiles + bl * L::BUF, wave);
+            issue_tile<D, PREFIX>(a, kh, vh, scales_h, t0 + u + P, tiles + bl * L::BUF, wave);
         }
         __builtin_amdgcn_s_setprio(1);                 // the MFMA half-step issues first
         half_m(t0 + u, buf1, vt_base + vcur * L::VT_BYTES, yes{}, yes{});
@@ -910,27 +919,23 @@ static void launch_merge_d(const AttnArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(combine_kernel<D>, dim3((rows + RPB - 1) / RPB), dim3(256), 0, s, a);
 }
 
+template <int D, bool BF16, bool QTAB>
+static void launch_main_d(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
+    if (a.prefix > 0) hipLaunchKernelGGL((attn_kernel<D, BF16, QTAB, true>), grid, block, Lds<D>::TOTAL, s, a);
+    else hipLaunchKernelGGL((attn_kernel<D, BF16, QTAB, false>), grid, block, Lds<D>::TOTAL, s, a);
+}
+
 hipError_t launch_attention_main(const AttnArgs &a, int head_dim, hipStream_t s) {
     const int n_qb = (a.n_q + kQB - 1) / kQB;
     const dim3 grid(n_qb * a.n_heads * a.n_splits), block(kThreads);
     const bool bf16 = a.dtype == KVR_BF16;
     const bool tab = a.q_cs != nullptr;
     if (head_dim == 128) {
-        if (tab) {
-            if (bf16) hipLaunchKernelGGL((attn_kernel<128, true, true>), grid, block, Lds<128>::TOTAL, s, a);
-            else hipLaunchKernelGGL((attn_kernel<128, false, true>), grid, block, Lds<128>::TOTAL, s, a);
-        } else {
-            if (bf16) hipLaunchKernelGGL((attn_kernel<128, true, false>), grid, block, Lds<128>::TOTAL, s, a);
-            else hipLaunchKernelGGL((attn_kernel<128, false, false>), grid, block, Lds<128>::TOTAL, s, a);
-        }
+        if (tab) bf16 ? launch_main_d<128, true, true>(a, grid, block, s) : launch_main_d<128, false, true>(a, grid, block, s);
+        else bf16 ? launch_main_d<128, true, false>(a, grid, block, s) : launch_main_d<128, false, false>(a, grid, block, s);
     } else {
-        if (tab) {
-            if (bf16) hipLaunchKernelGGL((attn_kernel<64, true, true>), grid, block, Lds<64>::TOTAL, s, a);
-            else hipLaunchKernelGGL((attn_kernel<64, false, true>), grid, block, Lds<64>::TOTAL, s, a);
-        } else {
-            if (bf16) hipLaunchKernelGGL((attn_kernel<64, true, false>), grid, block, Lds<64>::TOTAL, s, a);
-            else hipLaunchKernelGGL((attn_kernel<64, false, false>), grid, block, Lds<64>::TOTAL, s, a);
-        }
+        if (tab) bf16 ? launch_main_d<64, true, true>(a, grid, block, s) : launch_main_d<64, false, true>(a, grid, block, s);
+        else bf16 ? launch_main_d<64, true, false>(a, grid, block, s) : launch_main_d<64, false, false>(a, grid, block, s);
     }
     return hipGetLastError();
 }

@@ -27,7 +27,8 @@ import numpy as np
 BASE_SEED = 20261105
 
 _TENSOR_IDS = {"k": 1, "v": 2, "q": 3, "scale_k": 4, "scale_v": 5, "delta": 6, "src": 7}
-_WORKLOAD_IDS = {"tiny": 1, "layer": 2, "step": 3, "rebase": 4, "naive": 5, "wrap": 6, "test": 7}
+_WORKLOAD_IDS = {"tiny": 1, "layer": 2, "step": 3, "rebase": 4, "naive": 5, "wrap": 6, "test": 7,
+                 "prefix": 8}
 
 
 @dataclasses.dataclass(frozen=True)
