@@ -8,6 +8,10 @@ reset after step 4, 4 attention passes per step, one and two key splits) and
 its W = 100 variant that wraps mid-chunk; one production-shape layer (12
 heads, D 128, W 5788, 757 tokens per chunk as one 28-column latent frame):
 write, attention on sampled queries of every head, the frame-only rebase.
+A fixed prefix beside the ring: a W = 100 cache with a 12-slot prefix (ring of
+88, chunks of 16 wrap mid-chunk, prefix-only attention, the frame rebase leaves
+the prefix), the production window as 489 + 7 x 757, and head_dim 64 bf16 with
+ragged query counts and 0, 1, 3 splits; the 60-layer row-driven write.
 """
 import numpy as np
 import pytest
@@ -305,3 +309,56 @@ def test_prefix_page_3d():
     _say(f"  max-abs {mx:.4g} mean-abs {mean:.4g}")
     run.rebase(inputs.rebase_delta_t())
     _check_cache(run.cache, run.orc, "prefix page after frame rebase")
+
+
+# ---------------------------------------------------------------------------
+# more shapes: head_dim 64, bf16, ragged query counts, split counts, 60 layers
+# ---------------------------------------------------------------------------
+def test_prefix_bf16_head_dim_64_ragged_queries():
+    """D 64, 3 heads, W 300 = 40 prefix + a ring of 260 (chunks of 50 wrap mid-
+    chunk); queries: the first 37 of the chunk's tokens, and all 50; splits 0, 1, 3."""
+    shp = inputs.Shape("test", 1, 3, 64, 300, 50)
+    run = PrefixRun3D(shp, 40, cols=7, dtype=torch.bfloat16)
+    for step in range(8):
+        _say(f"D64 prefix step {step}")
+        k, v = inputs.np_chunk(shp, step)
+        kb = _f32(torch.from_numpy(k).to(torch.bfloat16))
+        vb = _f32(torch.from_numpy(v).to(torch.bfloat16))
+        run.step(step, kb, vb)
+        _check_cache(run.cache, run.orc, f"D64 step {step}")
+        q = inputs.np_queries(shp, step, 0)
+        for n_q, splits in ((37, 0), (50, 1), (50, 3)):
+            coords, rows = run.coords, run.rows
+            run.coords, run.rows = coords[:n_q], K.Rope3DRows(coords[:n_q], 64, run.npr)
+            got, ref = run.attention(np.ascontiguousarray(q[:n_q]), n_splits=splits)
+            assert_attention(got, ref, f"D64 step {step} n_q {n_q} splits {splits}")
+            run.coords, run.rows = coords, rows
+        if step == 5:
+            run.rebase(2)
+            _check_cache(run.cache, run.orc, "D64 after frame rebase")
+
+
+def test_rows_write_60_layers_batched():
+    """The 60-layer row-driven write of one step in one launch (sampled layers)."""
+    shp = inputs.PAGE_STEP
+    H, D, W, N, L = shp.n_heads, shp.head_dim, shp.window, shp.n_new, shp.n_layers
+    npr = inputs.axis_pairs(D)
+    cache = K.KVCache(L, H, D, W)
+    ring = K.kvr_ring(5299, 5788, 5299)          # full ring, the chunk wraps at the end
+    coords = inputs.chunk_coords(N, 41)
+    rows = K.Rope3DRows(coords, D, npr)
+    k, v = inputs.torch_chunk(shp, 0, 0, "cpu", n_layers=L)
+    _say("60-layer batched row-driven write")
+    K.kv_write_rope_quant_rows(cache, ring, 0, k.cuda(), v.cuda(), rows.cs)
+    torch.cuda.synchronize()
+    slots = (5299 + np.arange(N)) % W
+    for layer in (0, 31, 59):
+        orc = oracle.LayerCache(H, D, W)
+        oracle.write3d(orc, 5299, coords, npr, _f32(k[layer]), _f32(v[layer]))
+        for n in ("k", "v"):
+            assert_codes(_np(getattr(cache, f"{n}_codes"))[layer][:, slots],
+                         getattr(orc, f"{n}_codes")[:, slots], f"layer {layer} {n}")
+            assert_scales(_np(getattr(cache, f"{n}_scales"))[layer][:, slots],
+                          getattr(orc, f"{n}_scales")[:, slots], f"layer {layer} {n}")
+    untouched = np.setdiff1d(np.arange(W), slots)
+    assert not _np(cache.k_codes)[:, :, untouched].any()
