@@ -12,7 +12,8 @@ element with the bars in tests/_parity.py.  Cases:
   * the 60-layer batched write of a full step (sampled layers);
   * edge cases: ring not yet full, one valid key, one query, ragged query
     counts, fp32 inputs at D 128, all-zero rows, scores that grow along the
-    window past the lazy-rescale threshold.
+    window past the lazy-rescale threshold, a chunk as large as the window
+    (also wrapping from a non-zero head) and 3000 queries over it.
 """
 import numpy as np
 import pytest
@@ -532,3 +533,34 @@ def test_step_batched_write_60_layers():
     # slots outside the chunk were not touched
     untouched = np.setdiff1d(np.arange(W), (5299 + np.arange(N)) % W)
     assert not _np(cache.k_codes)[:, :, untouched].any()
+
+
+def test_extreme_sizes():
+    """A chunk as large as the window (every slot rewritten in one write, twice,
+    the second time wrapping from a non-zero head), and 3000 queries (12 query
+    blocks) over it; one and several splits."""
+    shp = inputs.Shape("test", 1, 2, 128, 200, 200)
+    run = SmallRun(shp, dtype=torch.bfloat16)
+    for step in range(2):
+        _say(f"extreme: chunk == window, step {step}")
+        k, v = inputs.np_chunk(shp, step)
+        kb = _f32(torch.from_numpy(k).to(torch.bfloat16))
+        vb = _f32(torch.from_numpy(v).to(torch.bfloat16))
+        run.step(kb, vb)
+        run.check_cache(f"chunk == window step {step}")
+        if step == 0:
+            # shift the head so the second full-window chunk wraps in the middle
+            run.step(kb[:70].copy(), vb[:70].copy())
+    n_q = 3000
+    q = np.random.default_rng(77).standard_normal((n_q, 2, 128)).astype(np.float32)
+    qd = torch.from_numpy(q).to(torch.bfloat16).cuda()
+    start = K.kvr_ring_logical_start(run.ring, 200)
+    rows = [(i, h) for i in (0, 1, 255, 256, 1023, 1024, 2047, 2999) for h in range(2)]
+    ref = oracle.attention(run.orc, start, 200, _f32(qd), 0, rows=rows)
+    for splits in (1, 0, 4):
+        _say(f"extreme: n_q={n_q} splits={splits}")
+        out = K.attn_fp8_window(run.cache, 0, start, 200, qd, 0, run.rope.base, n_splits=splits)
+        torch.cuda.synchronize()
+        got = _f32(out)
+        assert np.isfinite(got).all()
+        assert_attention(np.stack([got[i, h] for i, h in rows]), ref, f"n_q={n_q} splits={splits}")
