@@ -172,12 +172,6 @@ __device__ __forceinline__ void split4(float a, float b, float c, float d, uint3
     lo = pack4_fp8(a - h01[0], b - h01[1], c - h23[0], d - h23[1]);
 }
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
 // ds_read_b64_tr_b8 issued from inline assembly.  The compiler treats a
 // transposing read of a direct-to-LDS (global_load_lds) target as aliasing
 // every load still in flight and waits for all of them (vmcnt(0)) first,
@@ -790,24 +784,29 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     const float f = ltot > 0.0f ? 1.0f / ltot : 0.0f;
     const bool to_out = a.n_splits == 1;
     uint8_t *ob = tiles + wave * L::OUT_WAVE;
+    // the format is uniform: one straight-line pass per format
+    auto stage = [&](auto BF) {
 #pragma unroll
-    for (int d = 0; d < ND; ++d)
+        for (int d = 0; d < ND; ++d)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int u = 8 * d + 2 * q + g;              // 8-byte unit of d = 4u .. 4u+3
-            const float x0 = o[d][4 * q] * f, x1 = o[d][4 * q + 1] * f;
-            const float x2 = o[d][4 * q + 2] * f, x3 = o[d][4 * q + 3] * f;
-            uint32_t w0, w1;
-            if (to_out) {
-                w0 = f32_to_bf16_rne(x0) | ((uint32_t)f32_to_bf16_rne(x1) << 16);
-                w1 = f32_to_bf16_rne(x2) | ((uint32_t)f32_to_bf16_rne(x3) << 16);
-            } else {
-                w0 = __builtin_bit_cast(uint32_t, h2{(_Float16)x0, (_Float16)x1});
-                w1 = __builtin_bit_cast(uint32_t, h2{(_Float16)x2, (_Float16)x3});
+            for (int q = 0; q < 4; ++q) {
+                const int u = 8 * d + 2 * q + g;          // 8-byte unit of d = 4u .. 4u+3
+                const float x0 = o[d][4 * q] * f, x1 = o[d][4 * q + 1] * f;
+                const float x2 = o[d][4 * q + 2] * f, x3 = o[d][4 * q + 3] * f;
+                uint32_t w0, w1;
+                if constexpr (decltype(BF)::value) {      // round to nearest even
+                    w0 = pack_bf16(x0, x1);
+                    w1 = pack_bf16(x2, x3);
+                } else {
+                    w0 = __builtin_bit_cast(uint32_t, h2{(_Float16)x0, (_Float16)x1});
+                    w1 = __builtin_bit_cast(uint32_t, h2{(_Float16)x2, (_Float16)x3});
+                }
+                *reinterpret_cast<v2i *>(ob + col * (2 * D) + 8 * (u ^ ((2 * col) & (D / 4 - 2)))) =
+                    v2i{(int)w0, (int)w1};
             }
-            *reinterpret_cast<v2i *>(ob + col * (2 * D) + 8 * (u ^ ((2 * col) & (D / 4 - 2)))) =
-                v2i{(int)w0, (int)w1};
-        }
+    };
+    if (to_out) stage(std::true_type{});
+    else stage(std::false_type{});
     if (!to_out && g == 0 && q_ok) {
         const int64_t row = ((int64_t)split * a.n_q + qi) * a.n_heads + head;
         a.part_ml[2 * row] = kShift - cofs;             // running max, log2 units
@@ -889,7 +888,7 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
     u32x4 w;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-        w[k] = f32_to_bf16_rne(acc[2 * k] * inv) | ((uint32_t)f32_to_bf16_rne(acc[2 * k + 1] * inv) << 16);
+        w[k] = pack_bf16(acc[2 * k] * inv, acc[2 * k + 1] * inv);
     *reinterpret_cast<u32x4 *>(a.out + qh * D + e) = w;
 }
 
