@@ -9,7 +9,9 @@ element with the bars in tests/_parity.py.  Cases:
   * one attention layer at the production shape (12 heads, D 128, W 5788,
     N 757): all writes, 4 passes on sampled queries of every head, default and
     single split, determinism, the naive path, the rebase;
-  * the 60-layer batched write of a full step (sampled layers);
+  * the 60-layer batched write of a full step (sampled layers), and the full-
+    step configuration the benchmark times: 42 steps of 60-layer writes, all
+    4 passes of layers 0 and 59 at steps 1 and 42, then the 60-layer rebase;
   * edge cases: ring not yet full, one valid key, one query, ragged query
     counts, fp32 inputs at D 128, all-zero rows, scores that grow along the
     window past the lazy-rescale threshold, a chunk as large as the window
@@ -564,3 +566,53 @@ def test_extreme_sizes():
         got = _f32(out)
         assert np.isfinite(got).all()
         assert_attention(np.stack([got[i, h] for i, h in rows]), ref, f"n_q={n_q} splits={splits}")
+
+
+def test_full_step_parity_layers_0_and_59():
+    """The full-step configuration the benchmark times: a 60-layer cache, one
+    60-layer write per step with the ring head advancing 757 slots, then the
+    pass-major attention calls with the default splits.  All 4 passes of layers
+    0 and 59 are checked at steps 1 and 42 (positions up to ~37K, the ring
+    wrapped many times) on sampled queries of every head, then a rebase of all
+    60 layers by a drawn delta is checked on both layers."""
+    shp = inputs.PAGE_STEP
+    H, D, W, N, L, P = shp.n_heads, shp.head_dim, shp.window, shp.n_new, shp.n_layers, shp.passes
+    cache = K.KVCache(L, H, D, W)
+    rope = K.RopeTable(-inputs.DELTA_MAX - 1024, 45 * N + inputs.DELTA_MAX + 2048, D)
+    ring = K.kvr_ring_init()
+    orcs = {0: oracle.LayerCache(H, D, W), 59: oracle.LayerCache(H, D, W)}
+    total = 0
+    rng = np.random.default_rng(42)
+    for step in range(1, 43):
+        k, v = inputs.torch_chunk(shp, step, 0, "cuda", n_layers=L)
+        K.kv_write_rope_quant(cache, ring, 0, k, v, rope)
+        for layer, orc in orcs.items():
+            oracle.write(orc, total, ring.pos_next, _f32(k[layer]), _f32(v[layer]))
+        K.kvr_ring_after_write(ring, W, N)
+        total += N
+        if step not in (1, 42):
+            continue
+        start = K.kvr_ring_logical_start(ring, W)
+        qs = np.unique(np.concatenate([[0, 255, 256, N - 1], rng.integers(0, N, 12)]))
+        rows = [(int(i), h) for h in range(H) for i in qs]
+        for p in range(P):
+            for layer in (0, 59):
+                _say(f"full step {step} pass {p} layer {layer}")
+                q = inputs.torch_queries(shp, step, p, layer, "cuda")
+                out = K.attn_fp8_window(cache, layer, start, ring.n_valid, q, ring.pos_next - N, rope.base)
+                torch.cuda.synchronize()
+                got = _f32(out)
+                ref = oracle.attention(orcs[layer], start, ring.n_valid, _f32(q), ring.pos_next - N, rows=rows)
+                assert_attention(np.stack([got[i, h] for i, h in rows]), ref, f"step {step} pass {p} layer {layer}")
+    for layer, orc in orcs.items():
+        assert_codes(_np(cache.k_codes[layer]), orc.k_codes, f"layer {layer} k after 42 steps")
+        assert_scales(_np(cache.v_scales[layer]), orc.v_scales, f"layer {layer} v after 42 steps")
+    delta = inputs.rebase_delta()
+    _say(f"full-step rebase of 60 layers by {delta}")
+    start = K.kvr_ring_logical_start(ring, W)
+    K.kv_delta_rebase(cache, ring, 0, L, delta)
+    torch.cuda.synchronize()
+    for layer, orc in orcs.items():
+        oracle.rebase(orc, start, ring.n_valid, delta)
+        assert_codes(_np(cache.k_codes[layer]), orc.k_codes, f"layer {layer} rebase")
+        assert_scales(_np(cache.k_scales[layer]), orc.k_scales, f"layer {layer} rebase")
