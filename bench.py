@@ -590,14 +590,27 @@ def cpu_baseline(K, inputs, shp, cache, qpool, ring, chunks, torch):
     t = time.perf_counter()
     oracle.write(lc.copy(), 0, ring.pos_next, kn, vn)
     t_write = time.perf_counter() - t
+    # one layer's rebase (12 x 5788 K rows) and one naive per-call rebuild
+    rb = lc.copy()
+    t = time.perf_counter()
+    oracle.rebase(rb, start, ring.n_valid, inputs.rebase_delta())
+    t_rebase = time.perf_counter() - t
+    lin_k = np.ascontiguousarray(np.repeat(kn[:1].transpose(1, 0, 2), W, axis=1))   # [H][W][D] fp32
+    lin_v = np.ascontiguousarray(np.repeat(vn[:1].transpose(1, 0, 2), W, axis=1))
+    t = time.perf_counter()
+    oracle.naive(lin_k, lin_v, kn, vn, W, ring.pos_next)
+    t_naive = time.perf_counter() - t
     ms = (P * L * t_attn + L * t_write) * 1e3
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
-    log(f"oracle: attention call {t_attn:.2f} s, layer write {t_write * 1e3:.1f} ms -> {ms:.0f} ms/step")
+    log(f"oracle: attention call {t_attn:.2f} s, layer write {t_write * 1e3:.1f} ms -> {ms:.0f} ms/step; "
+        f"layer rebase {t_rebase * 1e3:.1f} ms, naive call {t_naive * 1e3:.1f} ms")
     return {"value": round(ms, 1), "unit": "ms/step", "cores": min(threads, cores), "kind": "oracle",
             "sample": "one full attention call (757 queries x 12 heads x 5788 keys, fp64) and one "
                       "layer's write, timed on the host, scaled x240 calls and x60 layers "
-                      "(extrapolated)",
-            "attention_call_s": round(t_attn, 3), "layer_write_ms": round(t_write * 1e3, 2)}
+                      "(extrapolated); also one layer's rebase (x60) and one naive rebuild (x240)",
+            "attention_call_s": round(t_attn, 3), "layer_write_ms": round(t_write * 1e3, 2),
+            "rebase_ms_extrapolated": round(L * t_rebase * 1e3, 1),
+            "naive_upkeep_ms_per_step_extrapolated": round(P * L * t_naive * 1e3, 1)}
 
 
 if __name__ == "__main__":
