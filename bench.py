@@ -68,6 +68,8 @@ def parse():
     ap.add_argument("--every-pass-steps", type=int, default=5,
                     help="steps timed with the chunk written again on every denoise pass (0 = skip)")
     ap.add_argument("--rebase-iters", type=int, default=20)
+    ap.add_argument("--graph-steps", type=int, default=10,
+                    help="replays of one whole step captured as a graph (0 = skip)")
     ap.add_argument("--rope3d-steps", type=int, default=10,
                     help="timed steps of the 3-D (frame, row, column) rotary form (0 = skip)")
     ap.add_argument("--splits", type=int, default=0, help="attention key splits (0 = default)")
@@ -251,6 +253,61 @@ def main():
         every_pass = {"ms_per_step": round(ep_ms, 5), "steps": args.every_pass_steps,
                       "writes_per_step": P, "upkeep_bytes_per_step": P * L * (2 * N * H * D * 2 + 2 * N * H * D + 2 * N * H * 4)}
         log(f"write on every pass: {ep_ms:.4f} ms/step ({P} writes of 60 layers per step)")
+
+    # ---- the whole step as one captured graph -----------------------------------
+    # one step (the 60-layer write + 240 calls at the ring state of the step after
+    # the last timed one) captured once and replayed; each replay redoes the same
+    # work on the same slots, so its outputs must equal those of the same step
+    # launched eagerly, bit for bit
+    graph = None
+    if args.graph_steps > 0:
+        ring_g = ring.copy()
+        kg, vg = chunks[sidx % pool]
+        after = ring_g.copy()
+        K.kvr_ring_after_write(after, W, N)
+        start_g = K.kvr_ring_logical_start(after, W)
+
+        def step_fixed():
+            K.kv_write_rope_quant(cache, ring_g, 0, kg, vg, rope)
+            for p in range(P):
+                for layer in range(L):
+                    K.attn_fp8_window(cache, layer, start_g, after.n_valid, qpool[p * L + layer],
+                                      after.pos_next - N, rope.base, out=outs[layer], n_splits=args.splits, ws=ws)
+        step_fixed()
+        torch.cuda.synchronize()
+        eager = [o.clone() for o in outs]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step_fixed()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step_fixed()
+        for o in outs:
+            o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        same = all(torch.equal(a, b) for a, b in zip(outs, eager))
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record()
+        for _ in range(args.graph_steps):
+            g.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        gms = g0.elapsed_time(g1) / args.graph_steps
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.graph_steps):
+            step_fixed()
+        e1.record()
+        torch.cuda.synchronize()
+        ems = e0.elapsed_time(e1) / args.graph_steps
+        graph = {"ms_per_step_replayed": round(gms, 5), "ms_per_step_launched": round(ems, 5),
+                 "steps": args.graph_steps, "replay_equals_eager": bool(same)}
+        log(f"whole step as a graph: {gms:.4f} ms/step replayed, {ems:.4f} launched; outputs equal: {same}")
+        del g
 
     # ---- per-kernel times, measured with events on the launch stream -----------
     # (1) every launch of one kind back to back between two events: the average
@@ -496,6 +553,7 @@ def main():
         },
         "naive": naive,
         "write_every_pass": every_pass,
+        "graph": graph,
         "rope3d": rope3d,
         "cpu_baseline": cpu,
     }

@@ -616,3 +616,65 @@ def test_full_step_parity_layers_0_and_59():
         oracle.rebase(orc, start, ring.n_valid, delta)
         assert_codes(_np(cache.k_codes[layer]), orc.k_codes, f"layer {layer} rebase")
         assert_scales(_np(cache.k_scales[layer]), orc.k_scales, f"layer {layer} rebase")
+
+
+def test_graph_replay_matches_eager():
+    """A step (the write of a chunk that wraps mid-chunk, four attention calls
+    with one and two splits) captured as a graph: every replay, with other
+    eager work and synchronisations between replays, gives the eager outputs
+    and cache bit for bit."""
+    shp = inputs.TINY_WRAP
+    H, D, W, N = shp.n_heads, shp.head_dim, shp.window, shp.n_new
+    cache = K.KVCache(1, H, D, W)
+    rope = K.RopeTable(-256, 4096, D)
+    ring = K.kvr_ring_init()
+    for step in range(6):                              # 96 tokens: the 7th chunk wraps
+        k, v = inputs.np_chunk(shp, step)
+        K.kv_write_rope_quant(cache, ring, 0, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), rope)
+        K.kvr_ring_after_write(ring, W, N)
+    k, v = (torch.from_numpy(a).cuda() for a in inputs.np_chunk(shp, 6))
+    qs = [torch.from_numpy(inputs.np_queries(shp, 6, p)).cuda() for p in range(4)]
+    after = ring.copy()
+    K.kvr_ring_after_write(after, W, N)
+    start = K.kvr_ring_logical_start(after, W)
+    outs = [torch.empty((N, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    ws = torch.empty(K.attn_fp8_window_workspace_bytes(cache, N, after.n_valid, 2), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        K.kv_write_rope_quant(cache, ring, 0, k, v, rope)
+        for p in range(4):
+            K.attn_fp8_window(cache, 0, start, after.n_valid, qs[p], after.pos_next - N, rope.base,
+                              out=outs[p], n_splits=1 + p % 2, ws=ws)
+
+    _say("graph: eager step")
+    step()
+    torch.cuda.synchronize()
+    want = [o.clone() for o in outs] + [cache.k_codes.clone(), cache.k_scales.clone()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    _say("graph: capture")
+    with torch.cuda.graph(g):
+        step()
+    other = K.KVCache(1, H, D, W)
+    slots = torch.tensor([K.kvr_ring_slot(ring, W, j) for j in range(N)], device="cuda")
+    assert int(slots[0]) == 96 and int(slots[-1]) == 11      # the chunk wraps
+    for r in range(3):
+        _say(f"graph: replay {r}")
+        for o in outs:
+            o.fill_(7.0)
+        cache.k_codes[0, :, slots] = 0                 # undone by the replay's write
+        # eager work of the program between replays
+        K.kv_write_rope_quant(other, K.kvr_ring_init(), 0, k, v, rope)
+        K.attn_fp8_window(other, 0, 0, N, qs[r], 0, rope.base)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [o for o in outs] + [cache.k_codes, cache.k_scales]
+        for i, (a, b) in enumerate(zip(got, want)):
+            assert torch.equal(a, b), f"replay {r}: tensor {i} differs from the eager run"
