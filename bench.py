@@ -68,6 +68,7 @@ def parse():
     ap.add_argument("--every-pass-steps", type=int, default=5,
                     help="steps timed with the chunk written again on every denoise pass (0 = skip)")
     ap.add_argument("--rebase-iters", type=int, default=20)
+    ap.add_argument("--seed", type=int, default=20261105, help="base seed of the synthetic inputs")
     ap.add_argument("--graph-steps", type=int, default=10,
                     help="replays of one whole step captured as a graph (0 = skip)")
     ap.add_argument("--rope3d-steps", type=int, default=10,
@@ -162,6 +163,7 @@ def main():
     from kv_cache_attention_ring_amd import kvring as K
 
     dev = "cuda"
+    inputs.set_base_seed(args.seed)
     shp = inputs.PAGE_STEP
     L, H, D, W, N, P = shp.n_layers, shp.n_heads, shp.head_dim, shp.window, shp.n_new, shp.passes
     pre = 8
@@ -519,7 +521,7 @@ def main():
             "workload": "full denoise step: 60 layer caches x 12 heads x head_dim 128, ring window "
                         "5788 slots, 757 new tokens per step; one 60-layer write + 240 attention calls",
             "layers": L, "heads": H, "head_dim": D, "window": W, "new_tokens": N, "passes": P,
-            "attention_splits": args.splits or "default",
+            "attention_splits": args.splits or "default", "seed": args.seed,
         },
         "roofline": {
             "kernel": "attn_kernel<128, bf16 Q> (attn_fp8_window_partial), per launch",

@@ -53,6 +53,12 @@ RESET_PERIOD = 42
 DELTA_MAX = RESET_PERIOD * 757
 
 
+def set_base_seed(seed: int) -> None:
+    """Change the base seed every sub-seed is derived from (default 20261105)."""
+    global BASE_SEED
+    BASE_SEED = int(seed)
+
+
 def _seed_seq(workload: str, step: int, layer: int, pss: int, tensor: str) -> np.random.SeedSequence:
     return np.random.SeedSequence([BASE_SEED, _WORKLOAD_IDS[workload], int(step) + 1000,
                                    int(layer), int(pss) + 10, _TENSOR_IDS[tensor]])
