@@ -500,6 +500,11 @@ def main():
         log(f"3-D form with a {n_pre}-slot prefix: {msp:.4f} ms/step; frame rebase of the ring {rebp:.4f} ms")
         del pcache, pk, pv
 
+    if naive is not None:
+        # the before/after comparison of the two upkeep designs on the same shapes
+        naive["upkeep_ratio_naive_over_write"] = round(naive["upkeep_ms_per_step"] / write_ms, 1)
+        naive["step_ratio_naive_over_ring"] = round(naive["ms_per_step"] / ms_step, 3)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(K, inputs, shp, cache, qpool, ring, chunks, torch)
