@@ -11,7 +11,9 @@ write, attention on sampled queries of every head, the frame-only rebase.
 A fixed prefix beside the ring: a W = 100 cache with a 12-slot prefix (ring of
 88, chunks of 16 wrap mid-chunk, prefix-only attention, the frame rebase leaves
 the prefix), the production window as 489 + 7 x 757, and head_dim 64 bf16 with
-ragged query counts and 0, 1, 3 splits; the 60-layer row-driven write.
+ragged query counts and 0, 1, 3 splits; the 60-layer row-driven write; 24
+drawn configurations (heads, head_dim, window, chunk, queries, splits, dtype,
+1-D ring or 3-D form with a random prefix) end to end.
 """
 import numpy as np
 import pytest
@@ -362,3 +364,88 @@ def test_rows_write_60_layers_batched():
                           getattr(orc, f"{n}_scales")[:, slots], f"layer {layer} {n}")
     untouched = np.setdiff1d(np.arange(W), slots)
     assert not _np(cache.k_codes)[:, :, untouched].any()
+
+
+def test_random_configurations():
+    """24 drawn configurations, each checked against the oracle end to end: heads
+    1..5, head_dim 64/128, windows 17..700, chunks 1..W (wrapping at random
+    places), query counts 1..600, splits 0/1/2/5, bf16 or fp32 inputs; half of
+    them on the 1-D ring, half on the 3-D form with a random prefix (possibly
+    none); a rebase (1-D) or frame rebase (3-D) partway through."""
+    for case in range(24):
+        rng = np.random.default_rng(1000 + case)
+        H = int(rng.integers(1, 6))
+        D = int(rng.choice([64, 128]))
+        W = int(rng.integers(17, 701))
+        three_d = case % 2 == 1
+        n_pre = int(rng.integers(0, W // 3)) if three_d and rng.random() < 0.7 else 0
+        cap = W - n_pre
+        N = int(rng.integers(1, cap + 1)) if rng.random() < 0.3 else int(rng.integers(1, max(2, cap // 3)))
+        n_q = int(rng.integers(1, 601))
+        splits = int(rng.choice([0, 1, 2, 5]))
+        dtype = torch.bfloat16 if rng.random() < 0.5 else torch.float32
+        steps = int(min(6, 2 + (2 * cap) // N))
+        _say(f"random case {case}: H={H} D={D} W={W} prefix={n_pre} N={N} n_q={n_q} splits={splits} "
+             f"{'3-D' if three_d else '1-D'} {dtype} steps={steps}")
+        shp = inputs.Shape("test", 1, H, D, W, N)
+        npr = inputs.axis_pairs(D)
+        cache = K.KVCache(1, H, D, W, n_prefix=n_pre)
+        orc = oracle.LayerCache(H, D, W)
+        model = oracle.PrefixRing(W, n_pre)
+        ring = K.kvr_ring_init()
+        rope = K.RopeTable(-4096, 16384, D)          # positions stay below 6 x 700
+
+        def as_dev(a):
+            t = torch.from_numpy(np.ascontiguousarray(a)).to(dtype)
+            return t.cuda(), _f32(t)
+
+        if n_pre:
+            kp, vp = inputs.np_chunk(inputs.Shape("test", 1, H, D, W, n_pre), 500 + case)
+            j = np.arange(n_pre)
+            pc = np.stack([np.full(n_pre, -1), j // 7, j % 7], 1)
+            (kd, kf), (vd, vf) = as_dev(kp), as_dev(vp)
+            K.kv_write_prefix_rows(cache, 0, 0, kd, vd, K.Rope3DRows(pc, D, npr).cs)
+            oracle.write3d_list(orc, range(n_pre), pc, npr, kf, vf)
+        t_shift = 0
+        for step in range(steps):
+            k, v = inputs.np_chunk(shp, step)
+            (kd, kf), (vd, vf) = as_dev(k), as_dev(v)
+            if three_d:
+                coords = inputs.chunk_coords(N, step, cols=7) - [t_shift, 0, 0]
+                rows = K.Rope3DRows(coords, D, npr)
+                K.kv_write_rope_quant_rows(cache, ring, 0, kd, vd, rows.cs)
+                oracle.write3d_list(orc, model.write(N), coords, npr, kf, vf)
+            else:
+                K.kv_write_rope_quant(cache, ring, 0, kd, vd, rope)
+                oracle.write(orc, step * N, ring.pos_next, kf, vf)
+                model.write(N)
+            K.kvr_ring_after_write(ring, cap, N)
+            if step == steps // 2:
+                if three_d:
+                    K.kv_delta_rebase_axes(cache, ring, 0, 1, (2, 0, 0), npr)
+                    oracle.rebase3d_list(orc, model.ring_slots(), (2, 0, 0), npr)
+                    t_shift += 2
+                else:
+                    start = K.kvr_ring_logical_start(ring, cap)
+                    K.kv_delta_rebase(cache, ring, 0, 1, 37)
+                    oracle.rebase(orc, start, ring.n_valid, 37)
+                    K.kvr_ring_after_rebase(ring, 37)
+        _check_cache(cache, orc, f"random case {case}")
+        q = np.random.default_rng(case).standard_normal((n_q, H, D)).astype(np.float32)
+        qd, qf = as_dev(q)
+        start = K.kvr_ring_logical_start(ring, cap)
+        sel = np.unique(np.concatenate([[0, n_q - 1], rng.integers(0, n_q, 10)]))
+        rows_sel = [(int(i), h) for h in range(H) for i in sel]
+        if three_d:
+            qc = np.stack([np.full(n_q, steps - 1 - t_shift), np.arange(n_q) // 7, np.arange(n_q) % 7], 1)
+            out = K.attn_fp8_window_rows(cache, 0, start, ring.n_valid, qd, K.Rope3DRows(qc, D, npr).cs,
+                                         n_splits=splits)
+            ref = oracle.attention3d_list(orc, model.key_slots(), qf, qc, npr, rows=rows_sel)
+        else:
+            qpos = ring.pos_next - n_q
+            out = K.attn_fp8_window(cache, 0, start, ring.n_valid, qd, qpos, rope.base, n_splits=splits)
+            ref = oracle.attention(orc, start, ring.n_valid, qf, qpos, rows=rows_sel)
+        torch.cuda.synchronize()
+        got = _f32(out)
+        assert np.isfinite(got).all()
+        assert_attention(np.stack([got[i, h] for i, h in rows_sel]), ref, f"random case {case}")
