@@ -143,7 +143,8 @@ int32_t kv_write_rope_quant(const kvr_cache *cache, const kvr_ring *before,
  * -delta (cos/sin of -delta * theta_i formed in fp64, rounded to fp32; fp32
  * rotation, no FMA) and re-quantised as in kv_write_rope_quant.  V rows are
  * not touched (V carries no rotation).  Afterwards call kvr_ring_after_rebase.
- * Errors: KVR_EINVAL, KVR_EUNSUPPORTED. */
+ * Errors: KVR_EINVAL (also |delta| > 2^53, where the fp64 angle stops being
+ * exact), KVR_EUNSUPPORTED. */
 int32_t kv_delta_rebase(const kvr_cache *cache, const kvr_ring *ring, int32_t layer0,
                         int32_t n_layers, int64_t delta, double rope_base, void *stream);
 

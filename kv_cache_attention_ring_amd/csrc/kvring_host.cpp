@@ -41,6 +41,8 @@ int32_t launch_status(hipError_t e, const char *what) {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int32_t kMaxExtent = 1 << 24;
+// rotary shifts must be exact in the fp64 angle product
+constexpr int64_t kMaxDelta = (int64_t)1 << 53;
 
 int32_t check_head_dim(int32_t D) {
     if (D != 64 && D != 128) return fail(KVR_EUNSUPPORTED, "head_dim %d not in {64,128}", D);
@@ -229,6 +231,8 @@ int32_t kv_delta_rebase(const kvr_cache *cache, const kvr_ring *ring, int32_t la
         return fail(KVR_EINVAL, "layers [%d,%d) outside cache of %d", layer0, layer0 + n_layers,
                     cache->n_layers);
     if (!(rope_base > 1.0) || !isfinite(rope_base)) return fail(KVR_EINVAL, "rotary base must be > 1");
+    if (delta < -kMaxDelta || delta > kMaxDelta)
+        return fail(KVR_EINVAL, "delta %lld outside [-2^53, 2^53]", (long long)delta);
     if (ring->n_valid == 0) return ok();
     // cos/sin of -delta * theta_i: fp64 angle and trig, rounded to fp32
     kvr::CosSinTable rot{};
@@ -473,7 +477,7 @@ int32_t kv_write_prefix_rows(const kvr_cache *cache, int32_t slot0, int32_t laye
     if (!cs_rows || !k_new || !v_new) return fail(KVR_EINVAL, "rotary rows or new rows pointer is NULL");
     if (!aligned16(cs_rows) || !aligned16(k_new) || !aligned16(v_new))
         return fail(KVR_EALIGN, "rotary rows or new rows not 16-byte aligned");
-    if (n_tok < 1 || slot0 < 0 || slot0 + n_tok > cache->n_prefix)
+    if (n_tok < 1 || slot0 < 0 || (int64_t)slot0 + n_tok > cache->n_prefix)
         return fail(KVR_EINVAL, "prefix slots [%d,%d) not inside [0,%d)", slot0, slot0 + n_tok,
                     cache->n_prefix);
     if (layer0 < 0 || n_layers < 1 || layer0 + n_layers > cache->n_layers)
@@ -514,6 +518,9 @@ int32_t kv_delta_rebase_axes(const kvr_cache *cache, const kvr_ring *ring, int32
     if (int32_t e = check_ring(ring, W)) return e;
     if (int32_t e = check_axis_pairs(axis_pairs, D)) return e;
     if (!delta) return fail(KVR_EINVAL, "delta is NULL");
+    for (int ax = 0; ax < 3; ++ax)
+        if (delta[ax] < -kMaxDelta || delta[ax] > kMaxDelta)
+            return fail(KVR_EINVAL, "delta[%d] = %lld outside [-2^53, 2^53]", ax, (long long)delta[ax]);
     if (layer0 < 0 || n_layers < 1 || layer0 + n_layers > cache->n_layers)
         return fail(KVR_EINVAL, "layers [%d,%d) outside cache of %d", layer0, layer0 + n_layers,
                     cache->n_layers);

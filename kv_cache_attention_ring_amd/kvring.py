@@ -260,7 +260,10 @@ class Rope3DRows:
 
     def __init__(self, coords, head_dim: int, axis_pairs, base: float = 10000.0, device="cuda",
                  stream=None):
-        c = torch.as_tensor(coords, dtype=torch.int32).reshape(-1, 3).to(device).contiguous()
+        c64 = torch.as_tensor(coords).reshape(-1, 3)
+        if c64.dtype.is_floating_point or (c64.numel() and int(c64.abs().max()) >= 2 ** 31):
+            raise KVRError(KVR_EINVAL, "coordinates must be integers below 2^31 in magnitude")
+        c = c64.to(torch.int32).to(device).contiguous()
         self.coords = c
         self.n_tok, self.head_dim, self.base = c.shape[0], head_dim, float(base)
         self.axis_pairs = tuple(int(x) for x in axis_pairs)

@@ -300,6 +300,9 @@ def test_axis_rebase_validation():
     assert call(base=0.5) == K.KVR_EINVAL
     assert call(ring=K.kvr_ring(0, 6000, 100)) == K.KVR_EINVAL
     assert call(cache=_cache(D=32)) == K.KVR_EUNSUPPORTED
+    assert call(delta=_ax(-(2 ** 63), 0, 0, ct=ctypes.c_int64)) == K.KVR_EINVAL
+    assert call(delta=_ax(0, 2 ** 53 + 1, 0, ct=ctypes.c_int64)) == K.KVR_EINVAL
+    assert lib.kv_delta_rebase(ctypes.byref(c), ctypes.byref(r), 0, 1, -(2 ** 63), 1e4, None) == K.KVR_EINVAL
 
 
 @no_gpu
@@ -334,6 +337,7 @@ def test_prefix_validation():
     assert pre(n_tok=0) == K.KVR_EINVAL
     assert pre(n_prefix=0, n_tok=1) == K.KVR_EINVAL        # no prefix to write
     assert pre(cs=rows + 4) == K.KVR_EALIGN
+    assert pre(slot0=2 ** 31 - 10, n_tok=100) == K.KVR_EINVAL   # no int32 overflow in the range check
     # the ring of a prefixed cache has window - n_prefix slots
     c = K.kvr_cache(FAKE, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000, 1, 12, 128, 5788, 489)
     assert _write(c, K.kvr_ring(5299, 0, 0), 757, _table()) == K.KVR_EINVAL
@@ -359,3 +363,11 @@ def test_page_shape_constants_fixture():
     assert vals["calls_per_step"] == s.n_layers * s.passes
     assert vals["window_slots"] == s.window and vals["new_slots"] == s.n_new
     assert vals["reset_period_steps"] == inputs.RESET_PERIOD
+
+
+def test_rope3d_rows_rejects_bad_coordinates():
+    import numpy as np
+    with pytest.raises(K.KVRError):
+        K.Rope3DRows(np.array([[2 ** 31, 0, 0]]), 128, (22, 21, 21), device="cpu")
+    with pytest.raises(K.KVRError):
+        K.Rope3DRows(np.array([[0.5, 0, 0]]), 128, (22, 21, 21), device="cpu")
