@@ -167,7 +167,7 @@ def main():
     shp = inputs.PAGE_STEP
     L, H, D, W, N, P = shp.n_layers, shp.n_heads, shp.head_dim, shp.window, shp.n_new, shp.passes
     pre = 8
-    total_steps = pre + args.warmup + args.steps + 2 + (args.every_pass_steps + 1 if args.every_pass_steps > 0 else 0)
+    total_steps = pre + args.warmup + args.steps + 3 + (args.every_pass_steps + 1 if args.every_pass_steps > 0 else 0)
     pos_lo = -inputs.DELTA_MAX - 8 * N
     rope = K.RopeTable(pos_lo, total_steps * N - pos_lo, D, device=dev)
     cache = K.KVCache(L, H, D, W, device=dev)
@@ -403,7 +403,17 @@ def main():
     torch.cuda.synchronize()
     reb_ms = r0.elapsed_time(r1) / args.rebase_iters
     reb_gbs = reb_bytes / (reb_ms * 1e-3) / 1e9
-    log(f"rebase delta={delta}: {reb_ms:.4f} ms = {reb_gbs:.0f} GB/s")
+    # a reset comes once every 42 steps, right after a step's attention calls:
+    # one rebase timed on its own after a full step (and one back, untimed)
+    step(sidx)
+    sidx += 1
+    r0.record()
+    K.kv_delta_rebase(cache, ring, 0, L, delta)
+    r1.record()
+    K.kv_delta_rebase(cache, ring, 0, L, -delta)
+    torch.cuda.synchronize()
+    reb_single_ms = r0.elapsed_time(r1)
+    log(f"rebase delta={delta}: {reb_ms:.4f} ms = {reb_gbs:.0f} GB/s (one after a step: {reb_single_ms:.4f} ms)")
 
     # ---- naive per-call upkeep -------------------------------------------------------
     naive = None
@@ -556,6 +566,7 @@ def main():
             "rebase_ms": round(reb_ms, 4),
             "rebase_GBps": round(reb_gbs, 1),
             "rebase_frac_hbm": round(reb_gbs / HBM_PEAK_GBS, 4),
+            "rebase_ms_single_after_step": round(reb_single_ms, 4),
             "rebase_delta": delta,
         },
         "naive": naive,
