@@ -79,6 +79,9 @@ def parse():
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB and exit "
                          "(reference kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--mix-mb", type=int, default=0,
+                    help="only time PyTorch's bf16 -> FP8 conversion of this many MiB of bf16 (the write "
+                         "kernel's 2:1 read:write mix, a reference rate) and exit")
     ap.add_argument("--attn-calls", type=int, default=0,
                     help="only time this many attention calls on one production-shape layer "
                          "(12 heads x 128, window 5788, 757 queries) and exit (for counter runs)")
@@ -145,10 +148,36 @@ def copy_only(mib):
                       "copy_GBps_read_plus_write": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
+def mix_only(mib):
+    """PyTorch's own bf16 -> FP8 (E4M3) conversion of a mib-MiB bf16 tensor: a
+    streaming kernel with the write kernel's 2:1 read:write byte mix, timed over
+    four distinct sources so the reads come from HBM (a reference rate for the
+    write kernel)."""
+    import torch
+    n = (mib << 20) // 2
+    srcs = [torch.randn(n, device="cuda").to(torch.bfloat16) for _ in range(4)]
+    dst = torch.empty(n, dtype=torch.float8_e4m3fn, device="cuda")
+    for s in srcs:
+        dst.copy_(s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(12):
+        dst.copy_(srcs[i % 4])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 12
+    print(json.dumps({"mix_read_bytes": 2 * n, "mix_write_bytes": n, "mix_ms": round(ms, 4),
+                      "mix_GBps_read_plus_write": round(3 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_mb:
         copy_only(args.copy_mb)
+        return
+    if args.mix_mb:
+        mix_only(args.mix_mb)
         return
     if args.attn_calls:
         attn_only(args.attn_calls, args.splits)

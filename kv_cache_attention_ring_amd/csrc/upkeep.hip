@@ -123,14 +123,17 @@ __device__ __forceinline__ void quantize_store(const float (&y)[EPT], uint8_t *c
             w[k] = (uint32_t)pk;
         }
     }
-    // codes and scales are written once and not read again by this launch:
-    // nontemporal stores
+    // the codes are written once and not read again by this launch, a whole
+    // 128-byte row per 8 lanes: nontemporal stores.  The 4-byte scales of
+    // consecutive rows come from different waves: ordinary stores, so they
+    // merge into whole lines in L2 before going to HBM (nontemporal scale
+    // stores measured ~5% slower for the write and the rebase)
     if constexpr (EPT == 16) {
         __builtin_nontemporal_store(u32x4v{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4v *>(codes_dst));
     } else {
         __builtin_nontemporal_store(u32x2v{w[0], w[1]}, reinterpret_cast<u32x2v *>(codes_dst));
     }
-    if (lane0) __builtin_nontemporal_store(scale, scale_dst);
+    if (lane0) *scale_dst = scale;
 }
 
 // ---------------------------------------------------------------------------
@@ -257,7 +260,7 @@ __global__ void __launch_bounds__(kBlock) rebase_kernel(RebaseArgs a, CosSinTabl
             const u32x2v v = __builtin_nontemporal_load(reinterpret_cast<const u32x2v *>(src));
             w[u][0] = v[0]; w[u][1] = v[1];
         }
-        sc[u] = __builtin_nontemporal_load(a.k_scales + rows[u]);   // read once: nontemporal
+        sc[u] = a.k_scales[rows[u]];          // 4 bytes of a line shared by 32 rows: ordinary load
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
