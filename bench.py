@@ -460,16 +460,23 @@ def main():
         npr = inputs.axis_pairs(D)
         ring3 = ring.copy()
 
-        def step3d(frame):
+        def step3d(frame, lanes=True):
+            # one row fill per step; the queries' rows are rearranged once into
+            # the attention kernel's load layout and shared by all 240 calls
             rows = K.Rope3DRows(inputs.chunk_coords(N, frame), D, npr)
+            qr = K.kv_rope_query_lanes(rows.cs) if lanes else None
             k, v = chunks[frame % pool]
             K.kv_write_rope_quant_rows(cache, ring3, 0, k, v, rows.cs)
             K.kvr_ring_after_write(ring3, W, N)
             start = K.kvr_ring_logical_start(ring3, W)
             for p in range(P):
                 for layer in range(L):
-                    K.attn_fp8_window_rows(cache, layer, start, ring3.n_valid, qpool[p * L + layer], rows.cs,
-                                           out=outs[layer], n_splits=args.splits, ws=ws)
+                    if lanes:
+                        K.attn_fp8_window_lanes(cache, layer, start, ring3.n_valid, qpool[p * L + layer], qr,
+                                                out=outs[layer], n_splits=args.splits, ws=ws)
+                    else:
+                        K.attn_fp8_window_rows(cache, layer, start, ring3.n_valid, qpool[p * L + layer], rows.cs,
+                                               out=outs[layer], n_splits=args.splits, ws=ws)
         for f in range(2):
             step3d(f)
         torch.cuda.synchronize()
@@ -480,6 +487,12 @@ def main():
         t1.record()
         torch.cuda.synchronize()
         ms3 = t0.elapsed_time(t1) / args.rope3d_steps
+        t0.record()
+        for f in range(args.rope3d_steps):
+            step3d(2 + args.rope3d_steps + f, lanes=False)
+        t1.record()
+        torch.cuda.synchronize()
+        ms3_rows = t0.elapsed_time(t1) / args.rope3d_steps
         d_t = inputs.rebase_delta_t()
         for i in range(3):
             K.kv_delta_rebase_axes(cache, ring3, 0, L, (d_t if i % 2 == 0 else -d_t, 0, 0), npr)
@@ -490,10 +503,12 @@ def main():
         r1.record()
         torch.cuda.synchronize()
         reb3 = r0.elapsed_time(r1) / args.rebase_iters
-        rope3d = {"ms_per_step": round(ms3, 5), "steps": args.rope3d_steps, "axis_pairs": list(npr),
+        rope3d = {"ms_per_step": round(ms3, 5), "ms_per_step_rows_layout": round(ms3_rows, 5),
+                  "steps": args.rope3d_steps, "axis_pairs": list(npr),
                   "frame_cols": inputs.FRAME_COLS, "frame_rebase_ms": round(reb3, 4),
                   "frame_rebase_GBps": round(reb_bytes / (reb3 * 1e-3) / 1e9, 1), "frame_delta": d_t}
-        log(f"3-D rotary form: {ms3:.4f} ms/step; frame rebase by {d_t}: {reb3:.4f} ms")
+        log(f"3-D rotary form: {ms3:.4f} ms/step ({ms3_rows:.4f} with the rows read in their own layout); "
+            f"frame rebase by {d_t}: {reb3:.4f} ms")
 
         # the window as a fixed 489-token prefix (one frame at t = -1, written
         # once) and a ring of 7 x 757 slots; attention sees prefix + ring
@@ -509,14 +524,15 @@ def main():
 
         def step_prefix(frame):
             rows = K.Rope3DRows(inputs.chunk_coords(N, frame), D, npr)
+            qr = K.kv_rope_query_lanes(rows.cs)
             k, v = chunks[frame % pool]
             K.kv_write_rope_quant_rows(pcache, pring, 0, k, v, rows.cs)
             K.kvr_ring_after_write(pring, cap, N)
             start = K.kvr_ring_logical_start(pring, cap)
             for p in range(P):
                 for layer in range(L):
-                    K.attn_fp8_window_rows(pcache, layer, start, pring.n_valid, qpool[p * L + layer], rows.cs,
-                                           out=outs[layer], n_splits=args.splits, ws=ws)
+                    K.attn_fp8_window_lanes(pcache, layer, start, pring.n_valid, qpool[p * L + layer], qr,
+                                            out=outs[layer], n_splits=args.splits, ws=ws)
         for f in range(8):                                   # fill the ring
             step_prefix(f)
         torch.cuda.synchronize()

@@ -264,6 +264,24 @@ int32_t attn_fp8_window_rows(const kvr_cache *cache, int32_t layer, int32_t slot
                              const float *q_cs_rows, float softmax_scale, uint16_t *out,
                              int32_t n_splits, void *ws, size_t ws_bytes, void *stream);
 
+/* The queries' (cos, sin) rows in the layout the attention kernel loads
+ * them in (each of its loads then reads whole lines): kv_rope_query_lanes
+ * rearranges rows [n_q][head_dim/2][2] (e.g. the chunk's rows from
+ * kv_rope3d_table_fill) into `lanes` (device, 16-byte aligned, of
+ * kv_rope_query_lanes_bytes(n_q, head_dim) bytes; an opaque layout that only
+ * attn_fp8_window_lanes reads), once for every call that uses the same rows
+ * (e.g. all layers and passes of a step).  attn_fp8_window_lanes is
+ * attn_fp8_window_rows taking that buffer: same results bit for bit.
+ * Errors: KVR_EINVAL (null, n_q out of range), KVR_EALIGN, KVR_EUNSUPPORTED;
+ * the bytes function returns 0 for bad input.  [AI-cache] */
+size_t  kv_rope_query_lanes_bytes(int32_t n_q, int32_t head_dim);
+int32_t kv_rope_query_lanes(const float *cs_rows, int32_t n_q, int32_t head_dim, float *lanes,
+                            void *stream);
+int32_t attn_fp8_window_lanes(const kvr_cache *cache, int32_t layer, int32_t slot_start,
+                              int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
+                              const float *q_lanes, float softmax_scale, uint16_t *out,
+                              int32_t n_splits, void *ws, size_t ws_bytes, void *stream);
+
 /* Writes n_tok prefix tokens (rotation of token j from row j of cs_rows,
  * device [n_tok][head_dim/2][2] fp32) to prefix slots slot0 .. slot0+n_tok-1
  * of layers layer0 .. layer0+n_layers-1, quantised as in kv_write_rope_quant.

@@ -361,13 +361,22 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
             for (int c = 0; c < QW / NH; ++c) qraw[(QW / NH) * h + c] = gload16(src + c);
         }
         if constexpr (QTAB) {
-            // the (cos, sin) of the lane's pairs 32h + 16g .. +15 of each slice h:
-            // 128 contiguous bytes per slice
+            if (a.q_cs_lanes) {
+                // lane layout: load c of the wave reads 64 consecutive 16-byte
+                // words, one per lane (whole lines)
+                const u32x4 *src = reinterpret_cast<const u32x4 *>(a.q_cs) +
+                                   (int64_t)(qb * kNW + wave) * (8 * NH) * 64 + lane;
 #pragma unroll
-            for (int h = 0; h < NH; ++h) {
-                const u32x4 *src = reinterpret_cast<const u32x4 *>(a.q_cs + 2 * (qrow * (D / 2) + 32 * h + 16 * g));
+                for (int c = 0; c < 8 * NH; ++c) csraw[c] = gload16(src + 64 * c);
+            } else {
+                // the (cos, sin) of the lane's pairs 32h + 16g .. +15 of each slice h:
+                // 128 contiguous bytes per slice
 #pragma unroll
-                for (int c = 0; c < 8; ++c) csraw[8 * h + c] = gload16(src + c);
+                for (int h = 0; h < NH; ++h) {
+                    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.q_cs + 2 * (qrow * (D / 2) + 32 * h + 16 * g));
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) csraw[8 * h + c] = gload16(src + c);
+                }
             }
         }
     }
@@ -892,7 +901,36 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
     *reinterpret_cast<u32x4 *>(a.out + qh * D + e) = w;
 }
 
+// One 16-byte word per thread: word c of lane l of wave w of query block b is
+// the (cos, sin) of pairs 32 (c / 8) + 16 (l / 32) + 2 (c % 8) and + 1 of query
+// 256 b + 32 w + l % 32 (the last query for the padding of the last block).
+__global__ void __launch_bounds__(256) query_lanes_kernel(const float *cs, int n_q, int D, float *lanes,
+                                                           int64_t n_words) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= n_words) return;
+    const int lane = (int)(idx % 64);
+    const int nc = D / 8;
+    const int c = (int)((idx / 64) % nc);
+    const int64_t bw = idx / (64 * nc);               // b * 8 + w
+    const int q = (int)min<int64_t>(bw * kQW + lane % 32, (int64_t)n_q - 1);
+    const int p = 32 * (c / 8) + 16 * (lane / 32) + 2 * (c % 8);
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(cs + ((int64_t)q * (D / 2) + p) * 2);
+    *reinterpret_cast<f32x4 *>(lanes + idx * 4) = v;
+}
+
 }  // namespace
+
+size_t query_lanes_bytes(int n_q, int head_dim) {
+    const size_t n_qb = (size_t)(n_q + kQB - 1) / kQB;
+    return n_qb * kQB * (size_t)head_dim * 4;          // D/2 (cos, sin) pairs per query, padded block
+}
+
+hipError_t launch_query_lanes(const float *cs_rows, int n_q, int head_dim, float *lanes, hipStream_t s) {
+    const int64_t n_words = (int64_t)query_lanes_bytes(n_q, head_dim) / 16;
+    hipLaunchKernelGGL(query_lanes_kernel, dim3((unsigned)((n_words + 255) / 256)), dim3(256), 0, s, cs_rows, n_q,
+                       head_dim, lanes, n_words);
+    return hipGetLastError();
+}
 
 int attn_default_splits(int n_heads, int n_q, int n_valid) {
     const int n_qb = (n_q + kQB - 1) / kQB;

@@ -70,6 +70,7 @@ struct AttnArgs {
     double rev_step;                  // base^(-32/D) = theta_{i+16} / theta_i
     int64_t q_pos0;                   // rotary position of query 0
     const float *q_cs;                // or (cos, sin) rows of the queries [n_q][D/2][2] (then q_pos0 unused)
+    int32_t q_cs_lanes;               // 1: q_cs is in the lane layout of launch_query_lanes
     uint16_t *out;                    // [n_q][H][D] bf16
     uint16_t *part_o;                 // [splits][n_q][H][D] fp16, normalised rows
     float *part_ml;                   // [splits][n_q][H][2]
@@ -79,6 +80,11 @@ struct AttnArgs {
     float softmax_scale;
 };
 int attn_default_splits(int n_heads, int n_q, int n_valid);
+// (cos, sin) rows [n_q][D/2][2] rearranged so that the attention kernel's load
+// c of lane l of wave w of query block b reads 16 bytes at
+// ((b * 8 + w) * (D / 8) + c) * 64 + l (units of 16 bytes)
+size_t query_lanes_bytes(int n_q, int head_dim);
+hipError_t launch_query_lanes(const float *cs_rows, int n_q, int head_dim, float *lanes, hipStream_t s);
 size_t attn_workspace_bytes(int n_heads, int head_dim, int n_q, int n_splits);
 // the attention kernel (output rows when n_splits == 1, split partials else)
 hipError_t launch_attention_main(const AttnArgs &a, int head_dim, hipStream_t s);

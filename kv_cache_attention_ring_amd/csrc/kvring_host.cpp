@@ -289,7 +289,8 @@ void set_partials(kvr::AttnArgs &a, void *ws, int32_t n_heads, int32_t D, int32_
 int32_t attn_setup(kvr::AttnArgs &a, const kvr_cache *cache, int32_t layer, int32_t slot_start,
                    int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
                    int64_t q_pos_start, float softmax_scale, double rope_base, uint16_t *out,
-                   int32_t n_splits, void *ws, size_t ws_bytes, const float *q_cs = nullptr) {
+                   int32_t n_splits, void *ws, size_t ws_bytes, const float *q_cs = nullptr,
+                   bool q_cs_lanes = false) {
     if (int32_t e = check_cache(cache)) return e;
     const int32_t W = ring_cap(cache), D = cache->head_dim;
     if (int32_t e = check_dtype(dtype)) return e;
@@ -314,6 +315,7 @@ int32_t attn_setup(kvr::AttnArgs &a, const kvr_cache *cache, int32_t layer, int3
     if (q_cs && !aligned16(q_cs)) return fail(KVR_EALIGN, "query rotary rows not 16-byte aligned");
     a = kvr::AttnArgs{};
     a.q_cs = q_cs;
+    a.q_cs_lanes = q_cs_lanes ? 1 : 0;
     const int64_t lay = (int64_t)layer * cache->n_heads * W;
     a.k_codes = cache->k_codes + lay * D;
     a.v_codes = cache->v_codes + lay * D;
@@ -556,6 +558,35 @@ int32_t attn_fp8_window_rows(const kvr_cache *cache, int32_t layer, int32_t slot
     kvr::AttnArgs a;
     if (int32_t e = attn_setup(a, cache, layer, slot_start, n_valid, q, dtype, n_q, 0, softmax_scale,
                                10000.0, out, n_splits, ws, ws_bytes, q_cs_rows))
+        return e;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (int32_t e = launch_status(kvr::launch_attention_main(a, cache->head_dim, s), "attention"))
+        return e;
+    return launch_status(kvr::launch_attention_merge(a, cache->head_dim, s), "attention merge");
+}
+
+size_t kv_rope_query_lanes_bytes(int32_t n_q, int32_t head_dim) {
+    if (n_q < 1 || n_q >= kMaxExtent || (head_dim != 64 && head_dim != 128)) return 0;
+    return kvr::query_lanes_bytes(n_q, head_dim);
+}
+
+int32_t kv_rope_query_lanes(const float *cs_rows, int32_t n_q, int32_t head_dim, float *lanes, void *stream) {
+    if (int32_t e = check_head_dim(head_dim)) return e;
+    if (!cs_rows || !lanes) return fail(KVR_EINVAL, "rows or lanes pointer is NULL");
+    if (!aligned16(cs_rows) || !aligned16(lanes)) return fail(KVR_EALIGN, "rows or lanes not 16-byte aligned");
+    if (n_q < 1 || n_q >= kMaxExtent) return fail(KVR_EINVAL, "n_q %d out of range", n_q);
+    return launch_status(kvr::launch_query_lanes(cs_rows, n_q, head_dim, lanes, static_cast<hipStream_t>(stream)),
+                         "query lanes");
+}
+
+int32_t attn_fp8_window_lanes(const kvr_cache *cache, int32_t layer, int32_t slot_start,
+                              int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
+                              const float *q_lanes, float softmax_scale, uint16_t *out,
+                              int32_t n_splits, void *ws, size_t ws_bytes, void *stream) {
+    if (!q_lanes) return fail(KVR_EINVAL, "query lanes pointer is NULL");
+    kvr::AttnArgs a;
+    if (int32_t e = attn_setup(a, cache, layer, slot_start, n_valid, q, dtype, n_q, 0, softmax_scale,
+                               10000.0, out, n_splits, ws, ws_bytes, q_lanes, true))
         return e;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (int32_t e = launch_status(kvr::launch_attention_main(a, cache->head_dim, s), "attention"))

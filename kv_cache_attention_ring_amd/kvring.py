@@ -83,6 +83,10 @@ _SIGS = {
                                     _F32, _P, _I32, _P, _SZ, _P]),
     "kv_write_prefix_rows": (_I32, [ctypes.POINTER(kvr_cache), _I32, _I32, _I32, _P, _P, _I32, _I64, _I32,
                                     _P, _P]),
+    "kv_rope_query_lanes_bytes": (_SZ, [_I32, _I32]),
+    "kv_rope_query_lanes": (_I32, [_P, _I32, _I32, _P, _P]),
+    "attn_fp8_window_lanes": (_I32, [ctypes.POINTER(kvr_cache), _I32, _I32, _I32, _P, _I32, _I32, _P,
+                                     _F32, _P, _I32, _P, _SZ, _P]),
     "kvr_last_error": (ctypes.c_char_p, []),
     "kvr_version": (ctypes.c_char_p, []),
 }
@@ -317,6 +321,36 @@ def attn_fp8_window_rows(cache: KVCache, layer: int, slot_start: int, n_valid: i
     # the position form's (q_pos_start, rope_base) pair is replaced by the rows
     rows_args = args[:7] + (_dev(q_cs_rows, "q_cs_rows"), args[8]) + args[10:]
     _check(lib().attn_fp8_window_rows(*rows_args))
+    return out
+
+
+def kv_rope_query_lanes(cs_rows: torch.Tensor, stream=None) -> torch.Tensor:
+    """The queries' (cos, sin) rows [n_q][D/2][2] in the attention kernel's load
+    layout (an opaque device buffer for attn_fp8_window_lanes)."""
+    if cs_rows.dtype != torch.float32 or cs_rows.dim() != 3 or cs_rows.shape[2] != 2:
+        raise KVRError(KVR_EINVAL, "cs_rows must be fp32 [n_q][head_dim/2][2]")
+    n_q, D = cs_rows.shape[0], 2 * cs_rows.shape[1]
+    nbytes = int(lib().kv_rope_query_lanes_bytes(n_q, D))
+    if nbytes == 0:
+        raise KVRError(KVR_EINVAL, f"unsupported query rows shape {tuple(cs_rows.shape)}")
+    lanes = torch.empty(nbytes // 4, dtype=torch.float32, device=cs_rows.device)
+    _check(lib().kv_rope_query_lanes(_dev(cs_rows, "cs_rows"), n_q, D, _dev(lanes, "lanes"), _stream(stream)))
+    return lanes
+
+
+def attn_fp8_window_lanes(cache: KVCache, layer: int, slot_start: int, n_valid: int, q: torch.Tensor,
+                          q_lanes: torch.Tensor, out: torch.Tensor | None = None, n_splits: int = 0,
+                          ws: torch.Tensor | None = None, softmax_scale: float | None = None,
+                          stream=None) -> torch.Tensor:
+    """attn_fp8_window_rows with the rows already in the kernel's load layout
+    (kv_rope_query_lanes); same results bit for bit."""
+    args, out, _, _c = _attn_args(cache, layer, slot_start, n_valid, q, 0, 10000.0, out, n_splits, ws,
+                                  softmax_scale, stream)
+    need = int(lib().kv_rope_query_lanes_bytes(q.shape[0], cache.head_dim))
+    if q_lanes.dtype != torch.float32 or q_lanes.numel() * 4 < need:
+        raise KVRError(KVR_EINVAL, f"q_lanes must be an fp32 buffer of at least {need} bytes")
+    lanes_args = args[:7] + (_dev(q_lanes, "q_lanes"), args[8]) + args[10:]
+    _check(lib().attn_fp8_window_lanes(*lanes_args))
     return out
 
 

@@ -449,3 +449,35 @@ def test_random_configurations():
         got = _f32(out)
         assert np.isfinite(got).all()
         assert_attention(np.stack([got[i, h] for i, h in rows_sel]), ref, f"random case {case}")
+
+
+def test_query_lanes_equal_rows(page_run):
+    """attn_fp8_window_lanes (rows rearranged once into the kernel's load
+    layout) gives the bits of attn_fp8_window_rows: production layer with 757
+    queries, default and single split; head_dim 64 with 1, 33 and 300 queries."""
+    run = page_run
+    shp = run.s
+    q = inputs.torch_queries(shp, 8, 3, 0, "cpu").cuda()
+    start = K.kvr_ring_logical_start(run.ring, shp.window)
+    lanes = K.kv_rope_query_lanes(run.rows.cs)
+    for splits in (0, 1):
+        _say(f"query lanes vs rows, page, splits {splits}")
+        a = K.attn_fp8_window_rows(run.cache, 0, start, run.ring.n_valid, q, run.rows.cs, n_splits=splits)
+        b = K.attn_fp8_window_lanes(run.cache, 0, start, run.ring.n_valid, q, lanes, n_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+    small = inputs.Shape("test", 1, 3, 64, 300, 50)
+    srun = Run3D(small, cols=7, dtype=torch.bfloat16)
+    for step in range(7):
+        k, v = inputs.np_chunk(small, step)
+        srun.step(step, _f32(torch.from_numpy(k).to(torch.bfloat16)), _f32(torch.from_numpy(v).to(torch.bfloat16)))
+    start = K.kvr_ring_logical_start(srun.ring, small.window)
+    for n_q in (1, 33, 300):
+        _say(f"query lanes vs rows, D 64, n_q {n_q}")
+        coords = np.stack([np.full(n_q, 6), np.arange(n_q) // 7, np.arange(n_q) % 7], 1)
+        rows = K.Rope3DRows(coords, 64, srun.npr)
+        q = torch.randn((n_q, 3, 64), device="cuda").to(torch.bfloat16)
+        a = K.attn_fp8_window_rows(srun.cache, 0, start, srun.ring.n_valid, q, rows.cs)
+        b = K.attn_fp8_window_lanes(srun.cache, 0, start, srun.ring.n_valid, q, K.kv_rope_query_lanes(rows.cs))
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
