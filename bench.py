@@ -69,6 +69,8 @@ def parse():
                     help="steps timed with the chunk written again on every denoise pass (0 = skip)")
     ap.add_argument("--rebase-iters", type=int, default=20)
     ap.add_argument("--seed", type=int, default=20261105, help="base seed of the synthetic inputs")
+    ap.add_argument("--pos-steps", type=int, default=10,
+                    help="timed steps with the position form of the attention call (0 = skip)")
     ap.add_argument("--graph-steps", type=int, default=10,
                     help="replays of one whole step captured as a graph (0 = skip)")
     ap.add_argument("--rope3d-steps", type=int, default=10,
@@ -109,8 +111,9 @@ def attn_only(calls, splits):
     need = K.attn_fp8_window_workspace_bytes(cache, N, W, splits)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
     start = K.kvr_ring_logical_start(ring, W)
-    call = lambda i: K.attn_fp8_window(cache, 0, start, W, qs[i % 4], ring.pos_next - N, rope.base,
-                                       out=out, n_splits=splits, ws=ws)
+    lanes = K.kv_rope_query_lanes(K.rope_table_rows(rope, ring.pos_next - N, N))
+    call = lambda i: K.attn_fp8_window_lanes(cache, 0, start, W, qs[i % 4], lanes, out=out, n_splits=splits,
+                                             ws=ws)
     for i in range(3):
         call(i)
     torch.cuda.synchronize()
@@ -196,7 +199,8 @@ def main():
     shp = inputs.PAGE_STEP
     L, H, D, W, N, P = shp.n_layers, shp.n_heads, shp.head_dim, shp.window, shp.n_new, shp.passes
     pre = 8
-    total_steps = pre + args.warmup + args.steps + 3 + (args.every_pass_steps + 1 if args.every_pass_steps > 0 else 0)
+    total_steps = (pre + args.warmup + args.steps + args.pos_steps + 3 +
+                   (args.every_pass_steps + 1 if args.every_pass_steps > 0 else 0))
     pos_lo = -inputs.DELTA_MAX - 8 * N
     rope = K.RopeTable(pos_lo, total_steps * N - pos_lo, D, device=dev)
     cache = K.KVCache(L, H, D, W, device=dev)
@@ -222,16 +226,30 @@ def main():
         K.kv_write_rope_quant(cache, ring, 0, k, v, rope)
         K.kvr_ring_after_write(ring, W, N)
 
+    # The queries of every call of a step are the chunk's tokens at the chunk's
+    # positions: their (cos, sin) rows (a slice of the rotary table) are put in
+    # the attention kernel's load order once per step and shared by the 240 calls.
+    cur = {}
+
+    def set_lanes():
+        cur["lanes"] = K.kv_rope_query_lanes(K.rope_table_rows(rope, ring.pos_next - N, N))
+
     def attend(layer, pss, start):
+        K.attn_fp8_window_lanes(cache, layer, start, ring.n_valid, qpool[pss * L + layer], cur["lanes"],
+                                out=outs[layer], n_splits=args.splits, ws=ws)
+
+    def attend_pos(layer, pss, start):
+        # the position form: the kernel forms the rotation of each query itself
         K.attn_fp8_window(cache, layer, start, ring.n_valid, qpool[pss * L + layer], ring.pos_next - N,
                           rope.base, out=outs[layer], n_splits=args.splits, ws=ws)
 
-    def step(step_idx):
+    def step(step_idx, call=None):
         write(step_idx)
+        set_lanes()
         start = K.kvr_ring_logical_start(ring, W)
         for p in range(P):
             for layer in range(L):
-                attend(layer, p, start)
+                (call or attend)(layer, p, start)
 
     sidx = pre
     for _ in range(args.warmup):
@@ -255,6 +273,19 @@ def main():
     log(f"{args.steps} steps: {ms_step:.4f} ms/step (wall {wall_ms / args.steps:.4f}); median "
         f"{pct(per_step, 50):.4f}, p90 {pct(per_step, 90):.4f}, max {per_step[-1]:.4f}")
 
+    # ---- the same steps with the position form of the attention call ------------
+    pos_ms = None
+    if args.pos_steps > 0:
+        p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        p0.record()
+        for _ in range(args.pos_steps):
+            step(sidx, attend_pos)
+            sidx += 1
+        p1.record()
+        torch.cuda.synchronize()
+        pos_ms = p0.elapsed_time(p1) / args.pos_steps
+        log(f"position form: {pos_ms:.4f} ms/step")
+
     # ---- the chunk written on every denoise pass ------------------------------
     # each pass brings new K/V rows for the step's chunk: they are written to
     # the same slots at the same positions (ring state of the step's start)
@@ -264,6 +295,7 @@ def main():
         def step_every_pass(step_idx):
             before = ring.copy()
             K.kvr_ring_after_write(ring, W, N)
+            set_lanes()
             start = K.kvr_ring_logical_start(ring, W)
             for p in range(P):
                 k, v = chunks[(step_idx + p) % pool]
@@ -297,13 +329,14 @@ def main():
         after = ring_g.copy()
         K.kvr_ring_after_write(after, W, N)
         start_g = K.kvr_ring_logical_start(after, W)
+        lanes_g = K.kv_rope_query_lanes(K.rope_table_rows(rope, after.pos_next - N, N))
 
         def step_fixed():
             K.kv_write_rope_quant(cache, ring_g, 0, kg, vg, rope)
             for p in range(P):
                 for layer in range(L):
-                    K.attn_fp8_window(cache, layer, start_g, after.n_valid, qpool[p * L + layer],
-                                      after.pos_next - N, rope.base, out=outs[layer], n_splits=args.splits, ws=ws)
+                    K.attn_fp8_window_lanes(cache, layer, start_g, after.n_valid, qpool[p * L + layer], lanes_g,
+                                            out=outs[layer], n_splits=args.splits, ws=ws)
         step_fixed()
         torch.cuda.synchronize()
         eager = [o.clone() for o in outs]
@@ -357,6 +390,10 @@ def main():
         return e0.elapsed_time(e1) / (P * L)
 
     def partial(layer, p, start):
+        K.attn_fp8_window_lanes_partial(cache, layer, start, ring.n_valid, qpool[p * L + layer], cur["lanes"],
+                                        out=outs[layer], n_splits=args.splits, ws=ws)
+
+    def partial_pos(layer, p, start):
         K.attn_fp8_window_partial(cache, layer, start, ring.n_valid, qpool[p * L + layer], ring.pos_next - N,
                                   rope.base, out=outs[layer], n_splits=args.splits, ws=ws)
 
@@ -364,6 +401,7 @@ def main():
         K.attn_fp8_window_merge(cache, N, ring.n_valid, outs[layer], n_splits=args.splits, ws=ws)
 
     kern_ms = sum(batch_ms(partial) for _ in range(2)) / 2
+    kern_pos_ms = sum(batch_ms(partial_pos) for _ in range(2)) / 2
     merge_ms = sum(batch_ms(merge) for _ in range(2)) / 2
     call_batch_ms = sum(batch_ms(attend) for _ in range(2)) / 2
     n_meas = 2
@@ -376,6 +414,7 @@ def main():
         e[0].record()
         write(sidx)
         e[1].record()
+        set_lanes()
         start = K.kvr_ring_logical_start(ring, W)
         i = 2
         for p in range(P):
@@ -584,7 +623,7 @@ def main():
             "attention_splits": args.splits or "default", "seed": args.seed,
         },
         "roofline": {
-            "kernel": "attn_kernel<128, bf16 Q> (attn_fp8_window_partial), per launch",
+            "kernel": "attn_kernel<128, bf16 Q, rotation rows> (attn_fp8_window_lanes_partial), per launch",
             "bound": "mfma",
             "achieved": round(kern_tflops, 2),
             "peak": FP8_PEAK_TFLOPS,
@@ -602,6 +641,7 @@ def main():
             "attention_call_us": round(attn_ms * 1e3, 3),
             "attention_call_TFLOPs": round(attn_tflops, 2),
             "attention_kernel_us": round(kern_ms * 1e3, 3),
+            "attention_kernel_us_position_form": round(kern_pos_ms * 1e3, 3),
             "attention_merge_us": round(merge_ms * 1e3, 3),
             "attention_call_traffic_bytes": counted_traffic("attn_call_traffic_bytes"),
             "attention_call_us_median_single": round(pct(a_sorted, 50) * 1e3, 3),
@@ -614,6 +654,7 @@ def main():
             "rebase_ms_single_after_step": round(reb_single_ms, 4),
             "rebase_delta": delta,
         },
+        "position_form": None if pos_ms is None else {"ms_per_step": round(pos_ms, 5), "steps": args.pos_steps},
         "naive": naive,
         "write_every_pass": every_pass,
         "graph": graph,
@@ -651,12 +692,14 @@ def run_naive(args, K, inputs, shp, rope, chunks, qpool, outs, ws, torch, dev, p
     def nstep(sidx, with_attn=True):
         k, v = chunks[sidx % len(chunks)]
         n_valid = min(ring.n_valid + N, W)
+        # the same attention call as the ring path (query rows in load order)
+        lanes = K.kv_rope_query_lanes(K.rope_table_rows(rope, ring.pos_next, N)) if with_attn else None
         for p in range(P):
             for layer in range(L):
                 upkeep(layer, k, v)
                 if with_attn:
-                    K.attn_fp8_window(lin, layer, 0, n_valid, qpool[p * L + layer], ring.pos_next, rope.base,
-                                      out=outs[layer], n_splits=args.splits, ws=ws)
+                    K.attn_fp8_window_lanes(lin, layer, 0, n_valid, qpool[p * L + layer], lanes,
+                                            out=outs[layer], n_splits=args.splits, ws=ws)
         ping[0] = 1 - ping[0]
         K.kvr_ring_after_write(ring, W, N)
 

@@ -270,8 +270,12 @@ int32_t attn_fp8_window_rows(const kvr_cache *cache, int32_t layer, int32_t slot
  * kv_rope3d_table_fill) into `lanes` (device, 16-byte aligned, of
  * kv_rope_query_lanes_bytes(n_q, head_dim) bytes; an opaque layout that only
  * attn_fp8_window_lanes reads), once for every call that uses the same rows
- * (e.g. all layers and passes of a step).  attn_fp8_window_lanes is
- * attn_fp8_window_rows taking that buffer: same results bit for bit.
+ * (e.g. all layers and passes of a step: the queries are the chunk's tokens,
+ * at the chunk's positions, in every call).  attn_fp8_window_lanes is
+ * attn_fp8_window_rows taking that buffer: same results bit for bit.  The
+ * rows may equally be those of the 1-D rotary table at the chunk's positions
+ * (a slice of a kvr_rope_table): the attention kernel then loads the cos/sin
+ * it would otherwise form itself.
  * Errors: KVR_EINVAL (null, n_q out of range), KVR_EALIGN, KVR_EUNSUPPORTED;
  * the bytes function returns 0 for bad input.  [AI-cache] */
 size_t  kv_rope_query_lanes_bytes(int32_t n_q, int32_t head_dim);
@@ -281,6 +285,13 @@ int32_t attn_fp8_window_lanes(const kvr_cache *cache, int32_t layer, int32_t slo
                               int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
                               const float *q_lanes, float softmax_scale, uint16_t *out,
                               int32_t n_splits, void *ws, size_t ws_bytes, void *stream);
+/* The first of attn_fp8_window_lanes's two launches (the attention kernel),
+ * as attn_fp8_window_partial is for attn_fp8_window; attn_fp8_window_merge
+ * completes it. */
+int32_t attn_fp8_window_lanes_partial(const kvr_cache *cache, int32_t layer, int32_t slot_start,
+                                      int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
+                                      const float *q_lanes, float softmax_scale, uint16_t *out,
+                                      int32_t n_splits, void *ws, size_t ws_bytes, void *stream);
 
 /* Writes n_tok prefix tokens (rotation of token j from row j of cs_rows,
  * device [n_tok][head_dim/2][2] fp32) to prefix slots slot0 .. slot0+n_tok-1

@@ -579,6 +579,19 @@ int32_t kv_rope_query_lanes(const float *cs_rows, int32_t n_q, int32_t head_dim,
                          "query lanes");
 }
 
+int32_t attn_fp8_window_lanes_partial(const kvr_cache *cache, int32_t layer, int32_t slot_start,
+                                      int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
+                                      const float *q_lanes, float softmax_scale, uint16_t *out,
+                                      int32_t n_splits, void *ws, size_t ws_bytes, void *stream) {
+    if (!q_lanes) return fail(KVR_EINVAL, "query lanes pointer is NULL");
+    kvr::AttnArgs a;
+    if (int32_t e = attn_setup(a, cache, layer, slot_start, n_valid, q, dtype, n_q, 0, softmax_scale,
+                               10000.0, out, n_splits, ws, ws_bytes, q_lanes, true))
+        return e;
+    return launch_status(kvr::launch_attention_main(a, cache->head_dim, static_cast<hipStream_t>(stream)),
+                         "attention");
+}
+
 int32_t attn_fp8_window_lanes(const kvr_cache *cache, int32_t layer, int32_t slot_start,
                               int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
                               const float *q_lanes, float softmax_scale, uint16_t *out,

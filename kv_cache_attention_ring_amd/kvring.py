@@ -87,6 +87,8 @@ _SIGS = {
     "kv_rope_query_lanes": (_I32, [_P, _I32, _I32, _P, _P]),
     "attn_fp8_window_lanes": (_I32, [ctypes.POINTER(kvr_cache), _I32, _I32, _I32, _P, _I32, _I32, _P,
                                      _F32, _P, _I32, _P, _SZ, _P]),
+    "attn_fp8_window_lanes_partial": (_I32, [ctypes.POINTER(kvr_cache), _I32, _I32, _I32, _P, _I32, _I32, _P,
+                                             _F32, _P, _I32, _P, _SZ, _P]),
     "kvr_last_error": (ctypes.c_char_p, []),
     "kvr_version": (ctypes.c_char_p, []),
 }
@@ -352,6 +354,30 @@ def attn_fp8_window_lanes(cache: KVCache, layer: int, slot_start: int, n_valid: 
     lanes_args = args[:7] + (_dev(q_lanes, "q_lanes"), args[8]) + args[10:]
     _check(lib().attn_fp8_window_lanes(*lanes_args))
     return out
+
+
+def attn_fp8_window_lanes_partial(cache: KVCache, layer: int, slot_start: int, n_valid: int, q: torch.Tensor,
+                                  q_lanes: torch.Tensor, out: torch.Tensor | None = None, n_splits: int = 0,
+                                  ws: torch.Tensor | None = None, softmax_scale: float | None = None,
+                                  stream=None):
+    """The attention kernel of attn_fp8_window_lanes alone (merge with
+    attn_fp8_window_merge); returns (out, ws)."""
+    args, out, ws, _c = _attn_args(cache, layer, slot_start, n_valid, q, 0, 10000.0, out, n_splits, ws,
+                                   softmax_scale, stream)
+    need = int(lib().kv_rope_query_lanes_bytes(q.shape[0], cache.head_dim))
+    if q_lanes.dtype != torch.float32 or q_lanes.numel() * 4 < need:
+        raise KVRError(KVR_EINVAL, f"q_lanes must be an fp32 buffer of at least {need} bytes")
+    lanes_args = args[:7] + (_dev(q_lanes, "q_lanes"), args[8]) + args[10:]
+    _check(lib().attn_fp8_window_lanes_partial(*lanes_args))
+    return out, ws
+
+
+def rope_table_rows(rope: RopeTable, pos0: int, n: int) -> torch.Tensor:
+    """The table's (cos, sin) rows of positions pos0 .. pos0+n-1 (a view)."""
+    i = int(pos0) - rope.pos0
+    if i < 0 or i + n > rope.n_pos:
+        raise KVRError(KVR_EINVAL, f"positions [{pos0},{pos0 + n}) outside the rotary table")
+    return rope.cs[i:i + n]
 
 
 def kv_delta_rebase(cache: KVCache, ring: kvr_ring, layer0: int, n_layers: int, delta: int,

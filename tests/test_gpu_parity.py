@@ -678,3 +678,38 @@ def test_graph_replay_matches_eager():
         got = [o for o in outs] + [cache.k_codes, cache.k_scales]
         for i, (a, b) in enumerate(zip(got, want)):
             assert torch.equal(a, b), f"replay {r}: tensor {i} differs from the eager run"
+
+
+def test_position_rows_in_load_order(page_layer):
+    """The 1-D call with the queries' (cos, sin) taken from the rotary table at
+    the chunk's positions, rearranged once into the kernel's load order
+    (kv_rope_query_lanes + attn_fp8_window_lanes, what the benchmark's step
+    uses), against the oracle: production layer, all 4 passes, default and
+    single split; and the small W = 100 workload that wraps mid-chunk."""
+    shp, c, rope, ring, orc = (page_layer[k] for k in ("shape", "cache", "rope", "ring", "orc"))
+    W, N = shp.window, shp.n_new
+    start = K.kvr_ring_logical_start(ring, W)
+    lanes = K.kv_rope_query_lanes(K.rope_table_rows(rope, ring.pos_next - N, N))
+    for p in range(shp.passes):
+        _say(f"rows in load order, page pass {p}")
+        q = inputs.torch_queries(shp, 8, p, 0, "cpu")
+        rows = _page_rows(N, shp.n_heads, seed=10 + p)
+        ref = oracle.attention(orc, start, ring.n_valid, _f32(q), ring.pos_next - N, rows=rows)
+        for n_splits in ((0, 1) if p == 0 else (0,)):
+            out = K.attn_fp8_window_lanes(c, 0, start, ring.n_valid, q.cuda(), lanes, n_splits=n_splits)
+            torch.cuda.synchronize()
+            got = _f32(out)
+            mx, mean = assert_attention(np.stack([got[i, h] for i, h in rows]), ref, f"lanes pass {p}")
+            _say(f"  splits={n_splits} max-abs {mx:.4g} mean-abs {mean:.4g}")
+    run = SmallRun(inputs.TINY_WRAP)
+    for step in range(9):
+        k, v = inputs.np_chunk(inputs.TINY_WRAP, step)
+        run.step(k, v)
+        n = run.ring.n_valid
+        st = K.kvr_ring_logical_start(run.ring, 100)
+        q = inputs.np_queries(inputs.TINY_WRAP, step, 0)
+        qpos = run.ring.pos_next - 16
+        lanes = K.kv_rope_query_lanes(K.rope_table_rows(run.rope, qpos, 16))
+        out = K.attn_fp8_window_lanes(run.cache, 0, st, n, torch.from_numpy(q).cuda(), lanes, n_splits=1 + step % 2)
+        torch.cuda.synchronize()
+        assert_attention(_f32(out), oracle.attention(run.orc, st, n, q, qpos), f"lanes small step {step}")
