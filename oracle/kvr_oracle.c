@@ -36,6 +36,7 @@
  * header of each function for its pin.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -84,8 +85,21 @@ uint8_t orc_e4m3_encode(float v)
 /* ------------------------------------------------------------------------ */
 /* Row quantisation (per token, per head)            [AI-cache] [NC-cache]  */
 /* Pins: absmax element encodes to +-448 exactly; dequantisation error is  */
-/* within half an E4M3 ulp; zero rows give scale 0 and zero codes.         */
+/* within half an E4M3 ulp; zero rows give scale 0 and zero codes; rows    */
+/* whose absmax is far below 1 (down to the smallest fp32 denormal) keep   */
+/* those properties and decode to finite values.                           */
+/*                                                                          */
+/* The code of element d is the E4M3 rounding of y_d * (448 / a).  The     */
+/* fp32 inverse 448 / a overflows once a < 448 / FLT_MAX (about 1.3e-36),  */
+/* so for a < 2^-64 both a and the row are first multiplied by 2^64, which */
+/* is exact; the product y_d 2^64 * fl(448 / (a 2^64)) is then the same    */
+/* real number as y_d * fl(448 / a) wherever that inverse is finite, so    */
+/* every such row keeps its bits, and the rows where it is not get the     */
+/* codes the definition asks for instead of NaN.                            */
 /* ------------------------------------------------------------------------ */
+#define ORC_TINY_ROW 0x1p-64f
+#define ORC_TINY_LIFT 0x1p64f
+
 void orc_quant_row(const float *y, int D, uint8_t *codes, float *scale)
 {
     float a = 0.0f;
@@ -99,9 +113,10 @@ void orc_quant_row(const float *y, int D, uint8_t *codes, float *scale)
         return;
     }
     *scale = a / 448.0f;
-    float inv = 448.0f / a;
+    float lift = a < ORC_TINY_ROW ? ORC_TINY_LIFT : 1.0f;
+    float inv = 448.0f / (a * lift);
     for (int d = 0; d < D; ++d) {
-        float t = y[d] * inv;
+        float t = (y[d] * lift) * inv;
         codes[d] = orc_e4m3_encode(t);
     }
 }
@@ -591,6 +606,20 @@ void orc_rope3d_cs_n(const int64_t *coords, int64_t n, int D, const int32_t npai
         for (int i = 0; i < D / 2; ++i)
             orc_rope3d_cs(coords + 3 * r, i, npairs, base, &cs[(r * (D / 2) + i) * 2],
                           &cs[(r * (D / 2) + i) * 2 + 1]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Thread count of the OpenMP loops above (the CPU-baseline timing runs the */
+/* oracle on all host cores and on one).                                    */
+/* ------------------------------------------------------------------------ */
+void orc_set_threads(int n)
+{
+    if (n > 0) omp_set_num_threads(n);
+}
+
+int orc_max_threads(void)
+{
+    return omp_get_max_threads();
 }
 
 /* ------------------------------------------------------------------------ */

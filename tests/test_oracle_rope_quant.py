@@ -115,3 +115,56 @@ def test_quant_sign_of_zero_and_tiny():
     y[0, 1] = -1e-9          # rounds to a negative zero code
     codes, s = oracle.quant_rows(y)
     assert codes[0, 0] == 0x7E and codes[0, 1] == 0x80 and codes[0, 2] == 0x00
+
+
+def _tiny_rows(rng, D=64):
+    """Rows whose absmax runs over every power of two from the smallest fp32
+    denormal (2^-149) to 2^-40, each also one fp32 step above and below."""
+    heads = []
+    for j in range(-149, -39):
+        b = np.float32(2.0 ** j)
+        heads += [b, np.nextafter(b, np.float32(np.inf)), np.nextafter(b, np.float32(0))]
+    heads = np.array([h for h in heads if h > 0], np.float32)
+    n = heads.size
+    y = (rng.uniform(-1, 1, (n, D)) * heads[:, None].astype(np.float64)).astype(np.float32)
+    y[:, 0] = np.where(rng.random(n) < 0.5, heads, -heads)
+    y = np.where(np.abs(y) <= np.abs(y[:, :1]), y, y[:, :1]).astype(np.float32)
+    return y
+
+
+def test_quant_tiny_rows_codes_finite_and_exact():
+    """Down to the smallest fp32 denormal: no NaN codes, the absmax element
+    encodes to +-448, and every code is within half an E4M3 ulp of the real
+    value y * 448 / absmax (formed here in fp64)."""
+    y = _tiny_rows(np.random.default_rng(6))
+    codes, scales = oracle.quant_rows(y)
+    assert not np.any((codes & 0x7F) == 0x7F), "NaN code"
+    a = np.abs(y).max(axis=1).astype(np.float64)
+    am = np.abs(y).argmax(axis=1)
+    assert np.all((codes[np.arange(len(y)), am] & 0x7F) == 0x7E)
+    t = y.astype(np.float64) * (448.0 / a[:, None])
+    dec = oracle.e4m3_decode(codes)
+    assert np.all(np.isfinite(dec))
+    assert np.all(np.abs(dec - t) <= _half_ulp(t) * (1 + 1e-6) + 1e-5)
+    # the scale is a / 448 in fp32 (tiny rows give denormal or zero scales)
+    assert np.array_equal(scales, (y_abs := np.abs(y).max(axis=1)) / np.float32(448.0))
+    assert np.all(np.isfinite(oracle.dequant_rows(codes, scales)))
+
+
+def test_quant_codes_invariant_under_power_of_two_scaling():
+    """y / absmax does not change when a row is multiplied by an exact power of
+    two, so neither do its codes: tiny rows (where the fp32 inverse 448 / absmax
+    would overflow) get the codes of the same row lifted into the normal range,
+    and ordinary rows keep theirs under 2^-40 .. 2^40."""
+    rng = np.random.default_rng(7)
+    y = _tiny_rows(rng)
+    lifted = (y.astype(np.float64) * 2.0 ** 100).astype(np.float32)
+    assert np.array_equal(lifted.astype(np.float64) * 2.0 ** -100, y.astype(np.float64))   # exact
+    c0, _ = oracle.quant_rows(y)
+    c1, _ = oracle.quant_rows(lifted)
+    assert np.array_equal(c0, c1)
+    z = (rng.standard_normal((500, 128)) * rng.uniform(0.01, 100, (500, 1))).astype(np.float32)
+    cz, _ = oracle.quant_rows(z)
+    for k in (-40, -13, 5, 40):
+        zk = (z.astype(np.float64) * 2.0 ** k).astype(np.float32)
+        assert np.array_equal(oracle.quant_rows(zk)[0], cz), k
