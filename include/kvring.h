@@ -86,13 +86,14 @@ typedef struct {
 /* Device table of fp32 (cos, sin) pairs of the rotary angles of a range of
  * positions: cs[(p - pos0) * head_dim/2 + i] = (cos, sin)(p * theta_i) with
  * theta_i = base^(-2i/head_dim), the angle formed in fp64 and cos/sin
- * evaluated in fp64 then rounded to fp32.  Filled by kv_rope_table_fill. */
+ * evaluated in fp64 then rounded to fp32.  Filled by kv_rope_table_fill (the
+ * base is that call's argument; the entry points reading a table only read
+ * its rows). */
 typedef struct {
     const float *cs;    /* device, [n_pos][head_dim/2][2] */
     int64_t      pos0;  /* first position held */
     int32_t      n_pos; /* number of positions held */
     int32_t      head_dim;
-    double       base;  /* rotary base, 10000 for the workloads here */
 } kvr_rope_table;
 
 /* ---- (a1) ring bookkeeping: pure host integer code, no GPU ----------------
@@ -122,7 +123,9 @@ int32_t kv_rope_table_fill(float *cs, int64_t pos0, int32_t n_pos, int32_t head_
  * tokens j < n_new: K row (j, h) is rotated at position before->pos_next + j
  * (pairs (x[2i], x[2i+1]) by angle p * theta_i, fp32, no FMA), then K and V
  * rows are quantised (a = row absmax; scale = a / 448; code = E4M3 RNE of
- * y * (448 / a); a == 0 gives scale 0 and zero codes) and stored at slot
+ * y * (448 / a); a == 0 gives scale 0 and zero codes; when a < 2^-64 the
+ * inverse and the products are formed from a and y times 2^64, exact, since
+ * 448 / a alone can overflow fp32) and stored at slot
  * (before->head + j) mod window.  The ring itself is not modified: call
  * kvr_ring_after_write afterwards.
  *   k_new, v_new : device, per layer [n_new][n_heads][head_dim] of `dtype`,
@@ -163,6 +166,7 @@ int32_t kv_delta_rebase(const kvr_cache *cache, const kvr_ring *ring, int32_t la
  * with one power-of-two scale per query row; the softmax weights and the
  * dequantised V rows go into bf16 matrix products; accumulation is fp32 with
  * an online softmax.
+ *   softmax_scale: > 0, or 0 for the default 1/sqrt(head_dim).
  *   q       : device [n_q][n_heads][head_dim] of `dtype`, 16-byte aligned.
  *   out     : device bf16 [n_q][n_heads][head_dim] (uint16 storage).
  *   n_splits: key-range splits per (head, query block); 0 picks one for the
@@ -171,7 +175,10 @@ int32_t kv_delta_rebase(const kvr_cache *cache, const kvr_ring *ring, int32_t la
  *   ws      : device workspace of attn_fp8_window_workspace_bytes(...) bytes
  *             (may be NULL when that is 0), 256-byte aligned.
  * Errors: KVR_EINVAL (null, n_valid not in [1, window], slot_start out of
- * range, rope_base <= 1, workspace too small), KVR_EALIGN, KVR_EUNSUPPORTED. */
+ * range, rope_base <= 1, softmax_scale negative or not finite, workspace too
+ * small), KVR_EALIGN, KVR_EUNSUPPORTED.
+ * Range: the fp32 accumulators hold sums of up to window weights below 2^16
+ * times the dequantised V values, so |V| must stay below about 2^99. */
 size_t  attn_fp8_window_workspace_bytes(const kvr_cache *cache, int32_t n_q, int32_t n_valid,
                                         int32_t n_splits);
 int32_t attn_fp8_window(const kvr_cache *cache, int32_t layer, int32_t slot_start,

@@ -787,12 +787,31 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     // tile buffers, all consumed), rows of 2*D bytes whose 8-byte units are
     // XOR-swizzled by an even function of the row, then out to HBM in whole
     // 16-byte chunks:
-    // bf16 outputs when there is one split, fp16 partials plus (max, sum) else.
+    // bf16 outputs when there is one split, fp16 partials plus (max, sum,
+    // exponent) else.  A partial row whose largest element reaches 2^15 is
+    // stored times 2^-e (e the power of two that brings it below 2^15; fp16
+    // holds values below 65504), and e goes beside it for the merge; every
+    // other row has e = 0 and is stored as is.
     const float lsum = lsum0 + lsum1;
     const float ltot = lsum + __shfl_xor(lsum, 32);
     const float f = ltot > 0.0f ? 1.0f / ltot : 0.0f;
     const bool to_out = a.n_splits == 1;
     uint8_t *ob = tiles + wave * L::OUT_WAVE;
+    int ex = 0;
+    float post = 1.0f;
+    if (!to_out) {
+        float om = 0.0f;
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) om = fmaxf(om, fabsf(o[d][r]));
+        om *= f;
+        om = fmaxf(om, __shfl_xor(om, 32));
+        if (om >= 32768.0f) {                             // exponent of om, minus 14
+            ex = (int)((__float_as_uint(om) >> 23) & 0xFF) - 127 - 14;
+            post = __uint_as_float((uint32_t)(127 - ex) << 23);
+        }
+    }
     // the format is uniform: one straight-line pass per format
     auto stage = [&](auto BF) {
 #pragma unroll
@@ -800,8 +819,14 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int u = 8 * d + 2 * q + g;          // 8-byte unit of d = 4u .. 4u+3
-                const float x0 = o[d][4 * q] * f, x1 = o[d][4 * q + 1] * f;
-                const float x2 = o[d][4 * q + 2] * f, x3 = o[d][4 * q + 3] * f;
+                float x0 = o[d][4 * q] * f, x1 = o[d][4 * q + 1] * f;
+                float x2 = o[d][4 * q + 2] * f, x3 = o[d][4 * q + 3] * f;
+                if constexpr (!decltype(BF)::value) {      // exact: a power of two
+                    x0 *= post;
+                    x1 *= post;
+                    x2 *= post;
+                    x3 *= post;
+                }
                 uint32_t w0, w1;
                 if constexpr (decltype(BF)::value) {      // round to nearest even
                     w0 = pack_bf16(x0, x1);
@@ -818,8 +843,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     else stage(std::false_type{});
     if (!to_out && g == 0 && q_ok) {
         const int64_t row = ((int64_t)split * a.n_q + qi) * a.n_heads + head;
-        a.part_ml[2 * row] = kShift - cofs;             // running max, log2 units
-        a.part_ml[2 * row + 1] = ltot;
+        // running max (log2 units), denominator, exponent of the stored row
+        *reinterpret_cast<f32x4 *>(a.part_ml + 4 * row) = f32x4{kShift - cofs, ltot, (float)ex, 0.0f};
     }
     // the rows were written by other lanes of this wave: wait for the LDS
     // writes and keep the compiler from moving the reads above them
@@ -839,8 +864,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
 }
 
 // Merge the split partials of (query, head) rows in split order: each split
-// s holds a normalised row o_s (fp16) with its running max m_s (log2 units)
-// and denominator l_s; out = sum_s w_s o_s / sum_s w_s, w_s = l_s 2^(m_s - M).
+// s holds a normalised row o_s, stored in fp16 as o_s 2^-e_s, with its running
+// max m_s (log2 units), denominator l_s and e_s;
+// out = sum_s w_s o_s / sum_s w_s, w_s = l_s 2^(m_s - M).
 // D/8 lanes per row, eight elements per lane.
 template <int D>
 __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
@@ -850,7 +876,7 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
     const int64_t qh = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
     if (qh >= rows) return;
     const int e = 8 * (threadIdx.x % LPR);
-    const float2 *ml = reinterpret_cast<const float2 *>(a.part_ml);
+    const f32x4 *ml = reinterpret_cast<const f32x4 *>(a.part_ml);
     float l = 0.0f;
     float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
     // up to kCombineBatch splits are loaded in one go (max, sum and the row part
@@ -860,7 +886,7 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
     float m = -INFINITY;
     for (int s0 = 0; s0 < a.n_splits; s0 += kCombineBatch) {
         const int nb = min(kCombineBatch, a.n_splits - s0);
-        float2 mls[kCombineBatch];
+        f32x4 mls[kCombineBatch];
         u32x4 v[kCombineBatch];
 #pragma unroll
         for (int i = 0; i < kCombineBatch; ++i) {
@@ -871,7 +897,7 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
         float mb = m;
 #pragma unroll
         for (int i = 0; i < kCombineBatch; ++i)
-            if (i < nb) mb = fmaxf(mb, mls[i].x);
+            if (i < nb) mb = fmaxf(mb, mls[i][0]);
         if (mb > m) {                                  // rescale what is merged so far
             const float r = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - mb);
             l *= r;
@@ -882,14 +908,15 @@ __global__ void __launch_bounds__(256) combine_kernel(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < kCombineBatch; ++i) {
             if (i >= nb) break;
-            const float wgt = mls[i].y > 0.0f ? mls[i].y * __builtin_amdgcn_exp2f(mls[i].x - m) : 0.0f;
+            const float wgt = mls[i][1] > 0.0f ? mls[i][1] * __builtin_amdgcn_exp2f(mls[i][0] - m) : 0.0f;
             l += wgt;
+            const float wrow = __builtin_ldexpf(wgt, (int)mls[i][2]);   // the row's 2^e_s (exact)
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const uint32_t word = v[i][k];           // (bit_cast of a vector element
                 const h2 x = __builtin_bit_cast(h2, word);   //  reference is not reliable)
-                acc[2 * k] += wgt * (float)x[0];
-                acc[2 * k + 1] += wgt * (float)x[1];
+                acc[2 * k] += wrow * (float)x[0];
+                acc[2 * k + 1] += wrow * (float)x[1];
             }
         }
     }
@@ -946,7 +973,7 @@ size_t attn_workspace_bytes(int n_heads, int head_dim, int n_q, int n_splits) {
     if (n_splits <= 1) return 0;
     const size_t rows = (size_t)n_splits * n_q * n_heads;
     const size_t o_bytes = (rows * head_dim * sizeof(uint16_t) + 255) / 256 * 256;
-    return o_bytes + rows * 2 * sizeof(float);
+    return o_bytes + rows * 4 * sizeof(float);
 }
 
 template <int D>

@@ -73,7 +73,7 @@ struct AttnArgs {
     int32_t q_cs_lanes;               // 1: q_cs is in the lane layout of launch_query_lanes
     uint16_t *out;                    // [n_q][H][D] bf16
     uint16_t *part_o;                 // [splits][n_q][H][D] fp16, normalised rows
-    float *part_ml;                   // [splits][n_q][H][2]
+    float *part_ml;                   // [splits][n_q][H][4]: running max, sum, row exponent, 0
     int32_t n_heads, window, slot_start, n_valid, n_q, dtype;   // n_valid: prefix + ring keys
     int32_t prefix, cap;              // key i < prefix: slot i; else prefix + (slot_start + i - prefix) mod cap
     int32_t n_splits, tiles_per_split;

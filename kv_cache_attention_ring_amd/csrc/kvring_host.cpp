@@ -286,9 +286,12 @@ void set_partials(kvr::AttnArgs &a, void *ws, int32_t n_heads, int32_t D, int32_
 }
 
 // Validation and kernel arguments shared by attn_fp8_window and its two parts.
+// rope_base: the rotary base of the position form (the kernel forms the
+// queries' angles from it); NULL for the row and lane forms, which take the
+// queries' (cos, sin) from q_cs instead.
 int32_t attn_setup(kvr::AttnArgs &a, const kvr_cache *cache, int32_t layer, int32_t slot_start,
                    int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
-                   int64_t q_pos_start, float softmax_scale, double rope_base, uint16_t *out,
+                   int64_t q_pos_start, float softmax_scale, const double *rope_base, uint16_t *out,
                    int32_t n_splits, void *ws, size_t ws_bytes, const float *q_cs = nullptr,
                    bool q_cs_lanes = false) {
     if (int32_t e = check_cache(cache)) return e;
@@ -304,9 +307,12 @@ int32_t attn_setup(kvr::AttnArgs &a, const kvr_cache *cache, int32_t layer, int3
     if (n_q < 1 || n_q >= kMaxExtent) return fail(KVR_EINVAL, "n_q %d out of range", n_q);
     if (!q || !out) return fail(KVR_EINVAL, "q/out is NULL");
     if (!aligned16(q) || !aligned16(out)) return fail(KVR_EALIGN, "q/out not 16-byte aligned");
+    if (softmax_scale == 0.0f) softmax_scale = (float)(1.0 / sqrt((double)D));   // the default 1/sqrt(D)
     if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale))
-        return fail(KVR_EINVAL, "softmax_scale must be positive and finite");
-    if (!(rope_base > 1.0) || !isfinite(rope_base)) return fail(KVR_EINVAL, "rotary base must be > 1");
+        return fail(KVR_EINVAL, "softmax_scale must be 0 (default) or positive and finite");
+    if (rope_base && (!(*rope_base > 1.0) || !isfinite(*rope_base)))
+        return fail(KVR_EINVAL, "rotary base must be > 1");
+    if (!rope_base && !q_cs) return fail(KVR_EINVAL, "query rotary rows pointer is NULL");
     if (n_splits < 0) return fail(KVR_EINVAL, "n_splits %d < 0", n_splits);
     int32_t tps;
     n_splits = effective_splits(cache->n_heads, n_q, n_keys, n_splits, &tps);
@@ -322,10 +328,12 @@ int32_t attn_setup(kvr::AttnArgs &a, const kvr_cache *cache, int32_t layer, int3
     a.k_scales = cache->k_scales + lay;
     a.v_scales = cache->v_scales + lay;
     a.q = q;
-    a.rev = make_theta(D, rope_base);
-    for (int i = 0; i < D / 2; ++i) a.rev.t[i] *= 0.15915494309189535;   // 1 / (2 pi)
-    a.rev_step = pow(rope_base, -32.0 / (double)D);
-    a.q_pos0 = q_pos_start;
+    if (rope_base) {
+        a.rev = make_theta(D, *rope_base);
+        for (int i = 0; i < D / 2; ++i) a.rev.t[i] *= 0.15915494309189535;   // 1 / (2 pi)
+        a.rev_step = pow(*rope_base, -32.0 / (double)D);
+        a.q_pos0 = q_pos_start;
+    }
     a.out = out;
     a.n_heads = cache->n_heads;
     a.window = cache->window;
@@ -380,7 +388,7 @@ int32_t attn_fp8_window(const kvr_cache *cache, int32_t layer, int32_t slot_star
                         void *stream) {
     kvr::AttnArgs a;
     if (int32_t e = attn_setup(a, cache, layer, slot_start, n_valid, q, dtype, n_q, q_pos_start,
-                               softmax_scale, rope_base, out, n_splits, ws, ws_bytes))
+                               softmax_scale, &rope_base, out, n_splits, ws, ws_bytes))
         return e;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (int32_t e = launch_status(kvr::launch_attention_main(a, cache->head_dim, s), "attention"))
@@ -395,7 +403,7 @@ int32_t attn_fp8_window_partial(const kvr_cache *cache, int32_t layer, int32_t s
                                 void *stream) {
     kvr::AttnArgs a;
     if (int32_t e = attn_setup(a, cache, layer, slot_start, n_valid, q, dtype, n_q, q_pos_start,
-                               softmax_scale, rope_base, out, n_splits, ws, ws_bytes))
+                               softmax_scale, &rope_base, out, n_splits, ws, ws_bytes))
         return e;
     return launch_status(kvr::launch_attention_main(a, cache->head_dim, static_cast<hipStream_t>(stream)),
                          "attention");
@@ -464,7 +472,6 @@ int32_t kv_write_rope_quant_rows(const kvr_cache *cache, const kvr_ring *before,
     t.pos0 = before ? before->pos_next : 0;
     t.n_pos = n_new;
     t.head_dim = cache->head_dim;
-    t.base = 10000.0;
     return kv_write_rope_quant(cache, before, layer0, n_layers, k_new, v_new, dtype, layer_stride_elems,
                                n_new, &t, stream);
 }
@@ -554,10 +561,9 @@ int32_t attn_fp8_window_rows(const kvr_cache *cache, int32_t layer, int32_t slot
                              int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
                              const float *q_cs_rows, float softmax_scale, uint16_t *out,
                              int32_t n_splits, void *ws, size_t ws_bytes, void *stream) {
-    if (!q_cs_rows) return fail(KVR_EINVAL, "query rotary rows pointer is NULL");
     kvr::AttnArgs a;
     if (int32_t e = attn_setup(a, cache, layer, slot_start, n_valid, q, dtype, n_q, 0, softmax_scale,
-                               10000.0, out, n_splits, ws, ws_bytes, q_cs_rows))
+                               nullptr, out, n_splits, ws, ws_bytes, q_cs_rows))
         return e;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (int32_t e = launch_status(kvr::launch_attention_main(a, cache->head_dim, s), "attention"))
@@ -583,10 +589,9 @@ int32_t attn_fp8_window_lanes_partial(const kvr_cache *cache, int32_t layer, int
                                       int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
                                       const float *q_lanes, float softmax_scale, uint16_t *out,
                                       int32_t n_splits, void *ws, size_t ws_bytes, void *stream) {
-    if (!q_lanes) return fail(KVR_EINVAL, "query lanes pointer is NULL");
     kvr::AttnArgs a;
     if (int32_t e = attn_setup(a, cache, layer, slot_start, n_valid, q, dtype, n_q, 0, softmax_scale,
-                               10000.0, out, n_splits, ws, ws_bytes, q_lanes, true))
+                               nullptr, out, n_splits, ws, ws_bytes, q_lanes, true))
         return e;
     return launch_status(kvr::launch_attention_main(a, cache->head_dim, static_cast<hipStream_t>(stream)),
                          "attention");
@@ -596,10 +601,9 @@ int32_t attn_fp8_window_lanes(const kvr_cache *cache, int32_t layer, int32_t slo
                               int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
                               const float *q_lanes, float softmax_scale, uint16_t *out,
                               int32_t n_splits, void *ws, size_t ws_bytes, void *stream) {
-    if (!q_lanes) return fail(KVR_EINVAL, "query lanes pointer is NULL");
     kvr::AttnArgs a;
     if (int32_t e = attn_setup(a, cache, layer, slot_start, n_valid, q, dtype, n_q, 0, softmax_scale,
-                               10000.0, out, n_splits, ws, ws_bytes, q_lanes, true))
+                               nullptr, out, n_splits, ws, ws_bytes, q_lanes, true))
         return e;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (int32_t e = launch_status(kvr::launch_attention_main(a, cache->head_dim, s), "attention"))

@@ -94,10 +94,18 @@ __device__ __forceinline__ void rotate_pairs(float (&x)[EPT], const float *cs) {
     }
 }
 
+// Rows whose absmax lies below 2^-64 are lifted by 2^64 (exact) before the
+// inverse is formed: 448 / a itself overflows fp32 once a < 448 / FLT_MAX, and
+// y 2^64 * fl(448 / (a 2^64)) is the same real number as y * fl(448 / a)
+// wherever that inverse is finite, so no other row changes.
+constexpr float kTinyRow = 0x1p-64f;
+constexpr float kTinyLift = 0x1p64f;
+
 // Row quantisation: absmax over the 8 lanes of the row, scale = a / 448,
-// codes = E4M3_RNE(y * (448 / a)).  Writes EPT codes and (lane 0) the scale.
+// codes = E4M3_RNE(y * (448 / a)).  Writes EPT codes and (lane 0) the scale;
+// y is lifted in place for tiny rows.
 template <int EPT>
-__device__ __forceinline__ void quantize_store(const float (&y)[EPT], uint8_t *codes_dst,
+__device__ __forceinline__ void quantize_store(float (&y)[EPT], uint8_t *codes_dst,
                                                float *scale_dst, bool lane0) {
     float a = 0.0f;
 #pragma unroll
@@ -113,7 +121,14 @@ __device__ __forceinline__ void quantize_store(const float (&y)[EPT], uint8_t *c
         for (int k = 0; k < EPT / 4; ++k) w[k] = 0u;
     } else {
         scale = a / 448.0f;
-        const float inv = 448.0f / a;
+        float inv;
+        if (a < kTinyRow) {                 // rare: the row is lifted first
+#pragma unroll
+            for (int e = 0; e < EPT; ++e) y[e] = y[e] * kTinyLift;
+            inv = 448.0f / (a * kTinyLift);
+        } else {
+            inv = 448.0f / a;
+        }
 #pragma unroll
         for (int k = 0; k < EPT / 4; ++k) {
             const float t0 = y[4 * k] * inv, t1 = y[4 * k + 1] * inv;

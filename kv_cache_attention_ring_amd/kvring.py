@@ -9,7 +9,6 @@ missing this module raises at load time; there is no fallback path.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 import torch
@@ -48,7 +47,7 @@ class kvr_cache(ctypes.Structure):
 
 class kvr_rope_table(ctypes.Structure):
     _fields_ = [("cs", ctypes.c_void_p), ("pos0", ctypes.c_int64), ("n_pos", ctypes.c_int32),
-                ("head_dim", ctypes.c_int32), ("base", ctypes.c_double)]
+                ("head_dim", ctypes.c_int32)]
 
 
 _lib = None
@@ -179,7 +178,7 @@ class RopeTable:
         kv_rope_table_fill(self.cs, self.pos0, self.n_pos, head_dim, self.base, stream)
 
     def desc(self) -> kvr_rope_table:
-        return kvr_rope_table(self.cs.data_ptr(), self.pos0, self.n_pos, self.head_dim, self.base)
+        return kvr_rope_table(self.cs.data_ptr(), self.pos0, self.n_pos, self.head_dim)
 
 
 # ---------------------------------------------------------------------------
@@ -397,17 +396,25 @@ def _attn_args(cache: KVCache, layer: int, slot_start: int, n_valid: int, q: tor
     n_q = q.shape[0]
     if q.dim() != 3 or q.shape[1:] != (cache.n_heads, cache.head_dim):
         raise KVRError(KVR_EINVAL, f"q shape {tuple(q.shape)} does not match the cache")
+    # tensors allocated here are used by kernels on `stream`: when that is not
+    # the current stream, the caching allocator is told so (record_stream), or
+    # it could hand their memory to a new tensor while those kernels still run
+    side = stream is not None and stream != torch.cuda.current_stream(q.device)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+        if side:
+            out.record_stream(stream)
     if out.dtype != torch.bfloat16 or out.shape != q.shape:
         raise KVRError(KVR_EINVAL, "out must be bf16 with q's shape")
     need = attn_fp8_window_workspace_bytes(cache, n_q, n_valid, n_splits)
     if need and ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if side:
+            ws.record_stream(stream)
     ws_ptr = _dev(ws, "ws") if ws is not None else None
     ws_len = ws.numel() * ws.element_size() if ws is not None else 0
     if softmax_scale is None:
-        softmax_scale = 1.0 / math.sqrt(cache.head_dim)
+        softmax_scale = 0.0                      # the library's default, 1/sqrt(head_dim)
     c = cache.desc()
     args = (ctypes.byref(c), layer, slot_start, n_valid, _dev(q, "q"), _dtype_code(q), n_q,
             int(q_pos_start), float(softmax_scale), float(rope_base), _dev(out, "out"), int(n_splits),

@@ -96,7 +96,7 @@ def _cache(D=128, W=5788, L=1, H=12, base=FAKE):
 
 
 def _table(pos0=0, n=10000, D=128, base=FAKE + 0x4000000):
-    return K.kvr_rope_table(base, pos0, n, D, 10000.0)
+    return K.kvr_rope_table(base, pos0, n, D)
 
 
 def _write(cache, ring, n_new, table, layer0=0, n_layers=1, k=FAKE + 0x5000000, v=FAKE + 0x6000000,
@@ -153,7 +153,9 @@ def test_attention_validation():
     assert _attn(c, 5788, n_q=0) == K.KVR_EINVAL
     assert _attn(c, 5788, q=FAKE + 2) == K.KVR_EALIGN
     assert _attn(c, 5788, out=0) == K.KVR_EINVAL
-    assert _attn(c, 5788, scale=0.0) == K.KVR_EINVAL
+    assert _attn(c, 5788, scale=-0.088) == K.KVR_EINVAL
+    assert _attn(c, 5788, scale=float("inf")) == K.KVR_EINVAL
+    assert _attn(c, 5788, scale=float("nan")) == K.KVR_EINVAL
     assert _attn(c, 5788, layer=1) == K.KVR_EINVAL
     assert _attn(c, 5788, base=1.0) == K.KVR_EINVAL
     # more than one split needs a workspace of the advertised size
@@ -195,8 +197,9 @@ def test_attention_parts_validation():
 
 
 def _ws_bytes(rows, D):
-    # fp16 normalised partial rows (padded to 256 bytes) + fp32 (max, sum) per row
-    return (rows * D * 2 + 255) // 256 * 256 + rows * 2 * 4
+    # fp16 normalised partial rows (padded to 256 bytes) + fp32 (max, sum,
+    # row exponent, unused) per row
+    return (rows * D * 2 + 255) // 256 * 256 + rows * 4 * 4
 
 
 def test_workspace_sizes_and_split_clamping():

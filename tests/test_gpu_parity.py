@@ -97,6 +97,121 @@ def test_row_magnitudes_through_write():
     assert np.array_equal(got_c, want_c), np.argwhere(got_c != want_c)[:5]
 
 
+def _tiny_head_rows(lo, hi, D, rng):
+    heads = []
+    for j in range(lo, hi):
+        b = np.float32(2.0 ** j)
+        heads += [b, np.nextafter(b, np.float32(np.inf)), np.nextafter(b, np.float32(0))]
+    heads = np.array([h for h in heads if h > 0], np.float32)
+    n = heads.size
+    v = (rng.uniform(-1, 1, (n, D)) * heads[:, None].astype(np.float64)).astype(np.float32)
+    v[:, 0] = np.where(rng.random(n) < 0.5, heads, -heads)
+    return np.where(np.abs(v) <= np.abs(v[:, :1]), v, v[:, :1]).astype(np.float32)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_tiny_rows_through_write_and_rebase(dtype):
+    """Rows whose absmax runs down to the smallest denormal of the input type
+    (fp32 2^-149, bf16 2^-133), where the fp32 inverse 448 / absmax overflows:
+    codes and scales bit-exact against the oracle, no NaN code, finite decoded
+    values; the same rows as K at position 0 (identity rotation) through the
+    rebase by +-1 (dequantise, rotate, re-quantise) against the oracle too."""
+    lo = -149 if dtype == torch.float32 else -133
+    _say(f"tiny rows {dtype}")
+    D = 128
+    v32 = _tiny_head_rows(lo, -59, D, np.random.default_rng(23))
+    vt = torch.from_numpy(v32).to(dtype)
+    v = _f32(vt)                                          # the values the kernel sees
+    n = v.shape[0]
+    cache = K.KVCache(1, 1, D, n)
+    rope = K.RopeTable(-4, n + 8, D)
+    # every row as token 0 of its own one-token chunk: K at position 0
+    for i in range(n):
+        ring = K.kvr_ring(i, i, 0)
+        K.kv_write_rope_quant(cache, ring, 0, vt[i:i + 1].view(1, 1, D).cuda(), vt[i:i + 1].view(1, 1, D).cuda(),
+                              rope)
+    torch.cuda.synchronize()
+    # K goes through the rotation at position 0 (cos 1, sin 0: the values stay,
+    # but a -0 element can come out as +0), V does not
+    want = {"k": oracle.quant_rows(oracle.rope_rows(v, 0)), "v": oracle.quant_rows(v)}
+    for name in ("k", "v"):
+        want_c, want_s = want[name]
+        got_c = _np(getattr(cache, f"{name}_codes"))[0, 0]
+        got_s = _np(getattr(cache, f"{name}_scales"))[0, 0]
+        assert not np.any((got_c & 0x7F) == 0x7F), f"{name}: NaN code"
+        assert np.array_equal(got_c, want_c), (name, np.argwhere(got_c != want_c)[:5])
+        assert np.array_equal(got_s.view(np.uint32), want_s.view(np.uint32)), name
+        assert np.isfinite(oracle.dequant_rows(got_c, got_s)).all()
+    orc = oracle.LayerCache(1, D, n)
+    orc.k_codes[0], orc.k_scales[0] = want["k"]
+    ring = K.kvr_ring(0, n, 1)
+    for delta in (1, -1):
+        K.kv_delta_rebase(cache, ring, 0, 1, delta)
+        oracle.rebase(orc, 0, n, delta)
+        torch.cuda.synchronize()
+        got_c = _np(cache.k_codes)[0, 0]
+        assert not np.any((got_c & 0x7F) == 0x7F), f"rebase {delta}: NaN code"
+        assert_codes(got_c, orc.k_codes[0], f"tiny rebase {delta}")
+        assert_scales(_np(cache.k_scales)[0, 0], orc.k_scales[0], f"tiny rebase {delta}")
+
+
+def test_large_values_through_split_partials():
+    """V rows near 1e6 (fp32 inputs): outputs of that size overflow an fp16
+    partial row unless it carries its own power-of-two exponent; one split,
+    several and the default all match the oracle (compared at the data's
+    scale: attention is linear in V) and each other within bf16 rounding."""
+    shp = inputs.Shape("test", 1, 3, 128, 1100, 600)
+    run = SmallRun(shp, dtype=torch.float32)
+    for step in range(2):
+        k, v = inputs.np_chunk(shp, step)
+        run.step(k, v * 1e6)
+    q = inputs.np_queries(shp, 1, 0)
+    outs = {}
+    for splits in (1, 4, 0):
+        _say(f"large values, splits={splits}")
+        got, ref = run.attention(q, n_splits=splits, naive_too=False)
+        assert np.isfinite(got).all(), f"splits={splits}: non-finite output"
+        assert np.abs(ref).max() > 65504.0                   # past the fp16 range
+        assert_attention(got / 1e6, ref / 1e6, f"large values, splits {splits}")
+        outs[splits] = got
+    # against the single-split rows, relative to each row's largest element
+    row_max = np.abs(outs[1]).max(axis=-1, keepdims=True)
+    for splits in (4, 0):
+        d = np.abs(outs[splits] - outs[1]) / row_max
+        assert d.max() <= 2.0 ** -7, (splits, d.max())
+
+
+def test_call_on_a_side_stream_without_its_context():
+    """attn_fp8_window on an explicit stream that is not the current one, with
+    the binding allocating the output and the workspace: same bits as the call
+    on the current stream."""
+    shp = inputs.Shape("test", 1, 3, 128, 1100, 600)
+    run = SmallRun(shp, dtype=torch.bfloat16)
+    for step in range(2):
+        k, v = inputs.np_chunk(shp, step)
+        run.step(k, v)
+    q = torch.from_numpy(inputs.np_queries(shp, 1, 2)).to(torch.bfloat16).cuda()
+    W = shp.window
+    start = K.kvr_ring_logical_start(run.ring, W)
+    want = K.attn_fp8_window(run.cache, 0, start, run.ring.n_valid, q, run.ring.pos_next - 600, run.rope.base,
+                             n_splits=4)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for i in range(3):
+        _say(f"side stream call {i}")
+        outs.append(K.attn_fp8_window(run.cache, 0, start, run.ring.n_valid, q, run.ring.pos_next - 600,
+                                      run.rope.base, n_splits=4, stream=side))
+        # work on the current stream that allocates while the side stream runs
+        junk = torch.full((1 << 20,), 3.0, device="cuda")
+        del junk
+    side.synchronize()
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o, want)
+
+
 def test_e4m3_conversion_sweep_through_write():
     """V rows whose absmax is 448 are encoded without scaling (448/448 = 1)."""
     _say("e4m3 sweep")
@@ -147,7 +262,26 @@ class SmallRun:
         self.lks = torch.zeros((H, W), dtype=torch.float32, device="cuda")
         self.lvs = torch.zeros((H, W), dtype=torch.float32, device="cuda")
         self.orc = oracle.LayerCache(H, D, W)
+        # the oracle's own bookkeeping, independent of the library's ring: the
+        # number of tokens written and the sum of the position resets
         self.total = 0
+        self.shift = 0
+
+    # reference window state from the token count alone (the oracle's t mod W
+    # slot rule): valid keys, oldest slot, next position
+    def ref_n_valid(self):
+        return min(self.total, self.s.window)
+
+    def ref_start(self):
+        return oracle.slot_of_token(self.total - self.ref_n_valid(), self.s.window)
+
+    def ref_pos_next(self):
+        return self.total - self.shift
+
+    def check_ring(self):
+        """The library's ring state equals the reference bookkeeping."""
+        assert (self.ring.n_valid, K.kvr_ring_logical_start(self.ring, self.s.window), self.ring.pos_next) == \
+            (self.ref_n_valid(), self.ref_start(), self.ref_pos_next()), self.ring
 
     def step(self, k, v):
         """k, v: fp32 numpy [N][H][D]."""
@@ -161,9 +295,10 @@ class SmallRun:
                        dst_k, dst_v, self.lc, self.lv, self.lks, self.lvs)
         self.ping = 1 - self.ping
         K.kv_write_rope_quant(self.cache, self.ring, 0, kd, vd, self.rope)
-        oracle.write(self.orc, self.total, self.ring.pos_next, kf, vf)
+        oracle.write(self.orc, self.total, self.ref_pos_next(), kf, vf)
         K.kvr_ring_after_write(self.ring, s.window, k.shape[0])
         self.total += k.shape[0]
+        self.check_ring()
 
     def write_pass(self, k, v, before, total_before):
         """Write a chunk again from the step-start ring state `before` (the
@@ -172,13 +307,14 @@ class SmallRun:
         kd = torch.from_numpy(k).to(self.dtype).cuda()
         vd = torch.from_numpy(v).to(self.dtype).cuda()
         K.kv_write_rope_quant(self.cache, before, 0, kd, vd, self.rope)
-        oracle.write(self.orc, total_before, before.pos_next, _f32(kd), _f32(vd))
+        oracle.write(self.orc, total_before, total_before - self.shift, _f32(kd), _f32(vd))
 
     def rebase(self, delta):
-        start = K.kvr_ring_logical_start(self.ring, self.s.window)
         K.kv_delta_rebase(self.cache, self.ring, 0, 1, delta)
-        oracle.rebase(self.orc, start, self.ring.n_valid, delta)
+        oracle.rebase(self.orc, self.ref_start(), self.ref_n_valid(), delta)
         K.kvr_ring_after_rebase(self.ring, delta)
+        self.shift += delta
+        self.check_ring()
 
     def check_cache(self, what, naive_too=True):
         torch.cuda.synchronize()
@@ -188,8 +324,8 @@ class SmallRun:
             assert_scales(_np(getattr(self.cache, f"{name}_scales"))[0],
                           getattr(self.orc, f"{name}_scales"), f"{what} ring {name} scales")
         if naive_too:
-            W, n = self.s.window, self.ring.n_valid
-            start = K.kvr_ring_logical_start(self.ring, W)
+            W, n = self.s.window, self.ref_n_valid()
+            start = self.ref_start()
             for ring_t, lin_t in ((self.cache.k_codes, self.lc), (self.cache.v_codes, self.lv),
                                   (self.cache.k_scales, self.lks), (self.cache.v_scales, self.lvs)):
                 r = logical_rows(_np(ring_t)[0], start, n, W)
@@ -202,22 +338,22 @@ class SmallRun:
         W = self.s.window
         qd = torch.from_numpy(q).to(self.dtype).cuda()
         n_q = q.shape[0]
-        qpos = self.ring.pos_next - n_q
-        start = K.kvr_ring_logical_start(self.ring, W)
-        out = K.attn_fp8_window(self.cache, 0, start, self.ring.n_valid, qd, qpos, self.rope.base,
-                                n_splits=n_splits, ws=ws)
+        # the library call takes its arguments from the library's ring; the
+        # oracle below from the reference bookkeeping
+        out = K.attn_fp8_window(self.cache, 0, K.kvr_ring_logical_start(self.ring, W), self.ring.n_valid, qd,
+                                self.ring.pos_next - n_q, self.rope.base, n_splits=n_splits, ws=ws)
         if naive_too:
             lin_cache = K.KVCache(1, self.s.n_heads, self.s.head_dim, W)
             lin_cache.k_codes[0].copy_(self.lc)
             lin_cache.v_codes[0].copy_(self.lv)
             lin_cache.k_scales[0].copy_(self.lks)
             lin_cache.v_scales[0].copy_(self.lvs)
-            out_lin = K.attn_fp8_window(lin_cache, 0, 0, self.ring.n_valid, qd, qpos, self.rope.base,
-                                        n_splits=n_splits, ws=ws)
+            out_lin = K.attn_fp8_window(lin_cache, 0, 0, self.ring.n_valid, qd, self.ring.pos_next - n_q,
+                                        self.rope.base, n_splits=n_splits, ws=ws)
             torch.cuda.synchronize()
             assert torch.equal(out, out_lin), "ring and naive attention differ"
         torch.cuda.synchronize()
-        ref = oracle.attention(self.orc, start, self.ring.n_valid, _f32(qd), qpos)
+        ref = oracle.attention(self.orc, self.ref_start(), self.ref_n_valid(), _f32(qd), self.ref_pos_next() - n_q)
         return _f32(out), ref
 
 
@@ -264,11 +400,10 @@ def test_edge_cases_small():
     for n_q in (1, 3, 16):
         _say(f"edge n_q={n_q}")
         q = inputs.np_queries(shp, 0, 0)[:n_q].copy()
-        qpos = run.ring.pos_next - n_q
-        out = K.attn_fp8_window(run.cache, 0, 0, run.ring.n_valid, torch.from_numpy(q).cuda(), qpos,
-                                run.rope.base)
+        out = K.attn_fp8_window(run.cache, 0, 0, run.ring.n_valid, torch.from_numpy(q).cuda(),
+                                run.ring.pos_next - n_q, run.rope.base)
         torch.cuda.synchronize()
-        assert_attention(_f32(out), oracle.attention(run.orc, 0, run.ring.n_valid, q, qpos),
+        assert_attention(_f32(out), oracle.attention(run.orc, 0, run.ref_n_valid(), q, run.ref_pos_next() - n_q),
                          f"n_q={n_q}")
     # a single valid key: the output is that key's dequantised value row
     _say("edge n_valid=1")
@@ -295,13 +430,13 @@ def test_lazy_rescale_when_scores_grow():
     t = rng.standard_normal((H, D)).astype(np.float32)
     t *= 12.0 / np.linalg.norm(t, axis=1, keepdims=True)          # |t| = 12 per head
     for c in range(4):
-        pos = run.ring.pos_next + np.arange(N)
+        pos = run.ref_pos_next() + np.arange(N)
         k_rot = (-t[None] if c == 0 else 0.0 * t[None]) + rng.standard_normal((N, H, D)).astype(np.float32) * (
             0.3 if c == 0 else 1.0)
         k = oracle.rope_rows(k_rot, -pos[:, None])                # stored rotated: k_rot
         v = rng.standard_normal((N, H, D)).astype(np.float32)
         run.step(np.ascontiguousarray(k), v)
-    q_pos = run.ring.pos_next - N + np.arange(N)
+    q_pos = run.ref_pos_next() - N + np.arange(N)
     q = oracle.rope_rows(t[None] + 0.3 * rng.standard_normal((N, H, D)).astype(np.float32), -q_pos[:, None])
     q = np.ascontiguousarray(q)
     for n_splits in (1, 2):
@@ -335,6 +470,7 @@ def test_write_on_every_pass():
         total_before = run.total
         after = K.kvr_ring(before.head, before.n_valid, before.pos_next)
         K.kvr_ring_after_write(after, W, N)
+        run.total = total_before + N                   # the oracle's count after this step's write
         for p in range(shp.passes):
             _say(f"write every pass: step {step} pass {p}")
             k, v = inputs.np_chunk(shp, step, pss=p)
@@ -343,7 +479,6 @@ def test_write_on_every_pass():
             run.check_cache(f"step {step} pass {p}", naive_too=False)
             got, ref = run.attention(inputs.np_queries(shp, step, p), naive_too=False)
             assert_attention(got, ref, f"write every pass: step {step} pass {p}")
-        run.total = total_before + N
 
 
 def test_split_merge_shares_one_workspace():
@@ -416,11 +551,16 @@ def page_layer():
         _say(f"page write step {step}")
         k, v = inputs.torch_chunk(shp, step, 0, "cpu")
         K.kv_write_rope_quant(cache, ring, 0, k[0].cuda(), v[0].cuda(), rope)
-        oracle.write(orc, total, ring.pos_next, _f32(k[0]), _f32(v[0]))
+        oracle.write(orc, total, total, _f32(k[0]), _f32(v[0]))
         K.kvr_ring_after_write(ring, W, N)
         total += N
     torch.cuda.synchronize()
-    return dict(shape=shp, cache=cache, rope=rope, ring=ring, orc=orc)
+    # the oracle's window from the token count alone: the last W tokens, the
+    # oldest at slot (total - W) mod W; queries at the last chunk's positions
+    ref = dict(n_valid=min(total, W), start=oracle.slot_of_token(total - min(total, W), W), q_pos=total - N)
+    assert (ring.n_valid, K.kvr_ring_logical_start(ring, W), ring.pos_next - N) == \
+        (ref["n_valid"], ref["start"], ref["q_pos"])
+    return dict(shape=shp, cache=cache, rope=rope, ring=ring, orc=orc, ref=ref)
 
 
 def test_page_write_parity(page_layer):
@@ -438,23 +578,30 @@ def _page_rows(n_q, H, seed=0, per_head=40):
     return [(int(i), h) for h in range(H) for i in qs]
 
 
+def _all_rows(n_q, H):
+    return [(i, h) for i in range(n_q) for h in range(H)]
+
+
 def test_page_attention_parity(page_layer):
-    shp, c, rope, ring, orc = (page_layer[k] for k in ("shape", "cache", "rope", "ring", "orc"))
+    """Production layer, 4 passes: every one of the 757 x 12 output rows of
+    pass 0 (default and single split), sampled rows of every head on the
+    other passes; the oracle's window and positions come from the token count."""
+    shp, c, rope, ring, orc, r = (page_layer[k] for k in ("shape", "cache", "rope", "ring", "orc", "ref"))
     W = shp.window
     start = K.kvr_ring_logical_start(ring, W)
     for p in range(shp.passes):
         _say(f"page attention pass {p}")
         q = inputs.torch_queries(shp, 8, p, 0, "cpu")
         qd = q.cuda()
-        rows = _page_rows(shp.n_new, shp.n_heads, seed=p)
-        ref = oracle.attention(orc, start, ring.n_valid, _f32(q), ring.pos_next - shp.n_new, rows=rows)
+        rows = _all_rows(shp.n_new, shp.n_heads) if p == 0 else _page_rows(shp.n_new, shp.n_heads, seed=p)
+        ref = oracle.attention(orc, r["start"], r["n_valid"], _f32(q), r["q_pos"], rows=rows)
         for n_splits in ((0, 1) if p == 0 else (0,)):
             out = K.attn_fp8_window(c, 0, start, ring.n_valid, qd, ring.pos_next - shp.n_new, rope.base,
                                     n_splits=n_splits)
             torch.cuda.synchronize()
             got = _f32(out)
             g = np.stack([got[i, h] for i, h in rows])
-            mx, mean = assert_attention(g, ref, f"page pass {p} splits {n_splits}")
+            mx, mean = assert_attention(g, ref, f"page pass {p} splits {n_splits} ({len(rows)} rows)")
             _say(f"  splits={n_splits} max-abs {mx:.4g} mean-abs {mean:.4g}")
             assert np.isfinite(got).all()
         if p == 0:
@@ -466,16 +613,15 @@ def test_page_attention_parity(page_layer):
 
 
 def test_page_rebase_parity(page_layer):
-    shp, c, ring, orc = (page_layer[k] for k in ("shape", "cache", "ring", "orc"))
+    shp, c, ring, orc, r = (page_layer[k] for k in ("shape", "cache", "ring", "orc", "ref"))
     delta = inputs.rebase_delta()
     _say(f"page rebase delta={delta}")
     c2 = K.KVCache(1, shp.n_heads, shp.head_dim, shp.window)
     for n in ("k_codes", "v_codes", "k_scales", "v_scales"):
         getattr(c2, n).copy_(getattr(c, n))
     o2 = orc.copy()
-    start = K.kvr_ring_logical_start(ring, shp.window)
     K.kv_delta_rebase(c2, ring, 0, 1, delta)
-    oracle.rebase(o2, start, ring.n_valid, delta)
+    oracle.rebase(o2, r["start"], r["n_valid"], delta)
     torch.cuda.synchronize()
     assert_codes(_np(c2.k_codes)[0], o2.k_codes, "rebase k")
     assert_scales(_np(c2.k_scales)[0], o2.k_scales, "rebase k")
@@ -558,7 +704,7 @@ def test_extreme_sizes():
     qd = torch.from_numpy(q).to(torch.bfloat16).cuda()
     start = K.kvr_ring_logical_start(run.ring, 200)
     rows = [(i, h) for i in (0, 1, 255, 256, 1023, 1024, 2047, 2999) for h in range(2)]
-    ref = oracle.attention(run.orc, start, 200, _f32(qd), 0, rows=rows)
+    ref = oracle.attention(run.orc, run.ref_start(), 200, _f32(qd), 0, rows=rows)
     for splits in (1, 0, 4):
         _say(f"extreme: n_q={n_q} splits={splits}")
         out = K.attn_fp8_window(run.cache, 0, start, 200, qd, 0, run.rope.base, n_splits=splits)
@@ -587,9 +733,13 @@ def test_full_step_parity_layers_0_and_59():
         k, v = inputs.torch_chunk(shp, step, 0, "cuda", n_layers=L)
         K.kv_write_rope_quant(cache, ring, 0, k, v, rope)
         for layer, orc in orcs.items():
-            oracle.write(orc, total, ring.pos_next, _f32(k[layer]), _f32(v[layer]))
+            oracle.write(orc, total, total, _f32(k[layer]), _f32(v[layer]))
         K.kvr_ring_after_write(ring, W, N)
         total += N
+        # the oracle's window from the step count: the last W of the step * N tokens
+        n_ref = min(total, W)
+        start_ref = oracle.slot_of_token(total - n_ref, W)
+        assert (ring.n_valid, K.kvr_ring_logical_start(ring, W), ring.pos_next) == (n_ref, start_ref, total)
         if step not in (1, 42):
             continue
         start = K.kvr_ring_logical_start(ring, W)
@@ -602,18 +752,20 @@ def test_full_step_parity_layers_0_and_59():
                 out = K.attn_fp8_window(cache, layer, start, ring.n_valid, q, ring.pos_next - N, rope.base)
                 torch.cuda.synchronize()
                 got = _f32(out)
-                ref = oracle.attention(orcs[layer], start, ring.n_valid, _f32(q), ring.pos_next - N, rows=rows)
-                assert_attention(np.stack([got[i, h] for i, h in rows]), ref, f"step {step} pass {p} layer {layer}")
+                # every row of pass 0 of layer 59 at the last step; sampled rows otherwise
+                rr = _all_rows(N, H) if (step == 42 and p == 0 and layer == 59) else rows
+                ref = oracle.attention(orcs[layer], start_ref, n_ref, _f32(q), total - N, rows=rr)
+                assert_attention(np.stack([got[i, h] for i, h in rr]), ref,
+                                 f"step {step} pass {p} layer {layer} ({len(rr)} rows)")
     for layer, orc in orcs.items():
         assert_codes(_np(cache.k_codes[layer]), orc.k_codes, f"layer {layer} k after 42 steps")
         assert_scales(_np(cache.v_scales[layer]), orc.v_scales, f"layer {layer} v after 42 steps")
     delta = inputs.rebase_delta()
     _say(f"full-step rebase of 60 layers by {delta}")
-    start = K.kvr_ring_logical_start(ring, W)
     K.kv_delta_rebase(cache, ring, 0, L, delta)
     torch.cuda.synchronize()
     for layer, orc in orcs.items():
-        oracle.rebase(orc, start, ring.n_valid, delta)
+        oracle.rebase(orc, start_ref, n_ref, delta)
         assert_codes(_np(cache.k_codes[layer]), orc.k_codes, f"layer {layer} rebase")
         assert_scales(_np(cache.k_scales[layer]), orc.k_scales, f"layer {layer} rebase")
 
@@ -622,16 +774,19 @@ def test_graph_replay_matches_eager():
     """A step (the write of a chunk that wraps mid-chunk, four attention calls
     with one and two splits) captured as a graph: every replay, with other
     eager work and synchronisations between replays, gives the eager outputs
-    and cache bit for bit."""
+    and cache bit for bit, and those match the oracle."""
     shp = inputs.TINY_WRAP
     H, D, W, N = shp.n_heads, shp.head_dim, shp.window, shp.n_new
     cache = K.KVCache(1, H, D, W)
     rope = K.RopeTable(-256, 4096, D)
     ring = K.kvr_ring_init()
+    orc = oracle.LayerCache(H, D, W)
     for step in range(6):                              # 96 tokens: the 7th chunk wraps
         k, v = inputs.np_chunk(shp, step)
         K.kv_write_rope_quant(cache, ring, 0, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), rope)
         K.kvr_ring_after_write(ring, W, N)
+        oracle.write(orc, step * N, step * N, k, v)
+    oracle.write(orc, 6 * N, 6 * N, *inputs.np_chunk(shp, 6))
     k, v = (torch.from_numpy(a).cuda() for a in inputs.np_chunk(shp, 6))
     qs = [torch.from_numpy(inputs.np_queries(shp, 6, p)).cuda() for p in range(4)]
     after = ring.copy()
@@ -651,6 +806,13 @@ def test_graph_replay_matches_eager():
     step()
     torch.cuda.synchronize()
     want = [o.clone() for o in outs] + [cache.k_codes.clone(), cache.k_scales.clone()]
+    # the eager step (and so every replay) against the oracle: 7 * 16 = 112
+    # tokens written, the window the last 100, the queries at 96 .. 111
+    assert_codes(_np(cache.k_codes)[0], orc.k_codes, "graph step k")
+    assert_scales(_np(cache.k_scales)[0], orc.k_scales, "graph step k")
+    for p in range(4):
+        ref = oracle.attention(orc, oracle.slot_of_token(112 - W, W), W, _np(qs[p]), 6 * N)
+        assert_attention(_f32(outs[p]), ref, f"graph step pass {p}")
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -686,15 +848,15 @@ def test_position_rows_in_load_order(page_layer):
     (kv_rope_query_lanes + attn_fp8_window_lanes, what the benchmark's step
     uses), against the oracle: production layer, all 4 passes, default and
     single split; and the small W = 100 workload that wraps mid-chunk."""
-    shp, c, rope, ring, orc = (page_layer[k] for k in ("shape", "cache", "rope", "ring", "orc"))
+    shp, c, rope, ring, orc, r = (page_layer[k] for k in ("shape", "cache", "rope", "ring", "orc", "ref"))
     W, N = shp.window, shp.n_new
     start = K.kvr_ring_logical_start(ring, W)
     lanes = K.kv_rope_query_lanes(K.rope_table_rows(rope, ring.pos_next - N, N))
     for p in range(shp.passes):
         _say(f"rows in load order, page pass {p}")
         q = inputs.torch_queries(shp, 8, p, 0, "cpu")
-        rows = _page_rows(N, shp.n_heads, seed=10 + p)
-        ref = oracle.attention(orc, start, ring.n_valid, _f32(q), ring.pos_next - N, rows=rows)
+        rows = _all_rows(N, shp.n_heads) if p == 0 else _page_rows(N, shp.n_heads, seed=10 + p)
+        ref = oracle.attention(orc, r["start"], r["n_valid"], _f32(q), r["q_pos"], rows=rows)
         for n_splits in ((0, 1) if p == 0 else (0,)):
             out = K.attn_fp8_window_lanes(c, 0, start, ring.n_valid, q.cuda(), lanes, n_splits=n_splits)
             torch.cuda.synchronize()
@@ -705,11 +867,10 @@ def test_position_rows_in_load_order(page_layer):
     for step in range(9):
         k, v = inputs.np_chunk(inputs.TINY_WRAP, step)
         run.step(k, v)
-        n = run.ring.n_valid
-        st = K.kvr_ring_logical_start(run.ring, 100)
         q = inputs.np_queries(inputs.TINY_WRAP, step, 0)
-        qpos = run.ring.pos_next - 16
-        lanes = K.kv_rope_query_lanes(K.rope_table_rows(run.rope, qpos, 16))
-        out = K.attn_fp8_window_lanes(run.cache, 0, st, n, torch.from_numpy(q).cuda(), lanes, n_splits=1 + step % 2)
+        lanes = K.kv_rope_query_lanes(K.rope_table_rows(run.rope, run.ring.pos_next - 16, 16))
+        out = K.attn_fp8_window_lanes(run.cache, 0, K.kvr_ring_logical_start(run.ring, 100), run.ring.n_valid,
+                                      torch.from_numpy(q).cuda(), lanes, n_splits=1 + step % 2)
         torch.cuda.synchronize()
-        assert_attention(_f32(out), oracle.attention(run.orc, st, n, q, qpos), f"lanes small step {step}")
+        assert_attention(_f32(out), oracle.attention(run.orc, run.ref_start(), run.ref_n_valid(), q,
+                                                     run.ref_pos_next() - 16), f"lanes small step {step}")
