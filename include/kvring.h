@@ -200,6 +200,30 @@ int32_t attn_fp8_window_partial(const kvr_cache *cache, int32_t layer, int32_t s
 int32_t attn_fp8_window_merge(const kvr_cache *cache, int32_t n_q, int32_t n_valid, int32_t n_splits,
                               uint16_t *out, void *ws, size_t ws_bytes, void *stream);
 
+/* ---- allocation-free attention -------------------------------------------
+ * For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid allocation): attn_fp8_window
+ * without the caller's workspace.  The split partials go to a scratch array
+ * of KVR_NOALLOC_SCRATCH_BYTES that the library holds in device memory on
+ * every GPU it runs on, until the process ends; its device address on a GPU
+ * is looked up once, on the first call there.  This entry point calls no
+ * allocator (no hipMalloc, no allocating library routine).  Nothing in the
+ * scratch needs clearing between calls: every partial row the merge reads is
+ * written earlier in the same call.  All calls on one GPU share that GPU's
+ * scratch, so calls that overlap on one GPU (on two streams, or from two
+ * threads without ordering) race: issue them on one stream.  This is the one
+ * exception to "no global mutable state" above.
+ * Arguments, results and errors as attn_fp8_window, less ws and ws_bytes;
+ * also KVR_EINVAL when the call's partials (attn_fp8_window_workspace_bytes
+ * for the same shape and split count) exceed KVR_NOALLOC_SCRATCH_BYTES (the
+ * production shape, 12 heads x 757 queries in 7 splits, needs 17.3 MB), and
+ * KVR_ELAUNCH when the scratch address cannot be obtained. */
+#define KVR_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int32_t attn_fp8_window_noalloc(const kvr_cache *cache, int32_t layer, int32_t slot_start,
+                                int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
+                                int64_t q_pos_start, float softmax_scale, double rope_base,
+                                uint16_t *out, int32_t n_splits, void *stream);
+
 /* ---- (a5) naive per-call upkeep (the original implementation) ------------
  * [WC] [AI-cache] [NC-cache].  Shift the linear, un-rotated window: the new
  * window is src rows [drop, n_valid_before) followed by the n_new new rows,

@@ -13,6 +13,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kvr_internal.h"
 #include "kvring.h"
 
@@ -415,6 +417,80 @@ int32_t attn_fp8_window_merge(const kvr_cache *cache, int32_t n_q, int32_t n_val
     if (int32_t e = merge_setup(a, cache, n_q, n_valid, n_splits, out, ws, ws_bytes)) return e;
     return launch_status(kvr::launch_attention_merge(a, cache->head_dim, static_cast<hipStream_t>(stream)),
                          "attention merge");
+}
+
+// ---- allocation-free attention ------------------------------------------------
+// The split partials of attn_fp8_window_noalloc live in `scratch`, a device
+// array of the library's own (each GPU the library runs on holds one copy
+// until the process ends).  In host code `scratch` names a host-side stand-in,
+// not device memory: its device address on a GPU comes from
+// hipGetSymbolAddress with that GPU current, taken once per GPU on the first
+// call there and kept in g_scratch; only that address is ever passed on.
+namespace {
+
+__device__ __align__(256) uint8_t scratch[KVR_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];          // device address of `scratch` per GPU, once known
+
+// Device address of the scratch array on the GPU `stream` runs on.
+int32_t scratch_address(hipStream_t stream, void **out) {
+    int dev = -1;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(KVR_ELAUNCH, "device of the stream: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(KVR_EUNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        int cur = -1;
+        if ((e = hipGetDevice(&cur)) != hipSuccess)
+            return fail(KVR_ELAUNCH, "current device: %s", hipGetErrorString(e));
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            return fail(KVR_ELAUNCH, "select device %d: %s", dev, hipGetErrorString(e));
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess && e2 != hipSuccess)
+                return fail(KVR_ELAUNCH, "restore device %d: %s", cur, hipGetErrorString(e2));
+        }
+        if (e != hipSuccess || !p)
+            return fail(KVR_ELAUNCH, "scratch address on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return KVR_OK;
+}
+
+}  // namespace
+
+int32_t attn_fp8_window_noalloc(const kvr_cache *cache, int32_t layer, int32_t slot_start,
+                                int32_t n_valid, const void *q, kvr_dtype dtype, int32_t n_q,
+                                int64_t q_pos_start, float softmax_scale, double rope_base,
+                                uint16_t *out, int32_t n_splits, void *stream) {
+    // the partials this call needs (0 for one split, or for arguments that
+    // attn_setup rejects below)
+    const size_t need = attn_fp8_window_workspace_bytes(cache, n_q, n_valid, n_splits);
+    if (need > KVR_NOALLOC_SCRATCH_BYTES)
+        return fail(KVR_EINVAL, "split partials of %zu bytes exceed the %zu-byte scratch", need,
+                    (size_t)KVR_NOALLOC_SCRATCH_BYTES);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    // every argument is validated as attn_fp8_window validates it, with an
+    // aligned stand-in for the workspace, before the device is touched; the
+    // partials then point into the scratch
+    kvr::AttnArgs a;
+    void *const stand_in = need > 0 ? reinterpret_cast<void *>(uintptr_t{256}) : nullptr;
+    if (int32_t e = attn_setup(a, cache, layer, slot_start, n_valid, q, dtype, n_q, q_pos_start,
+                               softmax_scale, &rope_base, out, n_splits, stand_in, need))
+        return e;
+    if (need > 0) {
+        void *ws = nullptr;
+        if (int32_t e = scratch_address(s, &ws)) return e;
+        set_partials(a, ws, cache->n_heads, cache->head_dim, n_q, a.n_splits);
+    }
+    if (int32_t e = launch_status(kvr::launch_attention_main(a, cache->head_dim, s), "attention"))
+        return e;
+    return launch_status(kvr::launch_attention_merge(a, cache->head_dim, s), "attention merge");
 }
 
 // ---- 3-D (frame, row, column) rotary encoding -------------------------------

@@ -71,6 +71,8 @@ _SIGS = {
     "attn_fp8_window_partial": (_I32, [ctypes.POINTER(kvr_cache), _I32, _I32, _I32, _P, _I32, _I32, _I64,
                                        _F32, _F64, _P, _I32, _P, _SZ, _P]),
     "attn_fp8_window_merge": (_I32, [ctypes.POINTER(kvr_cache), _I32, _I32, _I32, _P, _P, _SZ, _P]),
+    "attn_fp8_window_noalloc": (_I32, [ctypes.POINTER(kvr_cache), _I32, _I32, _I32, _P, _I32, _I32, _I64,
+                                       _F32, _F64, _P, _I32, _P]),
     "naive_upkeep": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32,
                             ctypes.POINTER(kvr_rope_table), _P, _P, _P, _P, _P, _P, _P]),
     "kv_rope3d_table_fill": (_I32, [_P, _P, _I32, _I32, ctypes.POINTER(_I32), _F64, _P]),
@@ -453,6 +455,32 @@ def attn_fp8_window_merge(cache: KVCache, n_q: int, n_valid: int, out: torch.Ten
     ws_len = ws.numel() * ws.element_size() if ws is not None else 0
     _check(lib().attn_fp8_window_merge(ctypes.byref(c), n_q, n_valid, int(n_splits), _dev(out, "out"),
                                        ws_ptr, ws_len, _stream(stream)))
+    return out
+
+
+#: bytes of the library's per-GPU scratch array for attn_fp8_window_noalloc
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def attn_fp8_window_noalloc(cache: KVCache, layer: int, slot_start: int, n_valid: int, q: torch.Tensor,
+                            q_pos_start: int, rope_base: float = 10000.0, out: torch.Tensor | None = None,
+                            n_splits: int = 0, softmax_scale: float | None = None, stream=None) -> torch.Tensor:
+    """attn_fp8_window with the split partials in the library's own scratch
+    array (the C entry point allocates nothing; pass `out` to allocate nothing
+    here either)."""
+    n_q = q.shape[0]
+    if q.dim() != 3 or q.shape[1:] != (cache.n_heads, cache.head_dim):
+        raise KVRError(KVR_EINVAL, f"q shape {tuple(q.shape)} does not match the cache")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+        if stream is not None and stream != torch.cuda.current_stream(q.device):
+            out.record_stream(stream)
+    if out.dtype != torch.bfloat16 or out.shape != q.shape:
+        raise KVRError(KVR_EINVAL, "out must be bf16 with q's shape")
+    c = cache.desc()
+    _check(lib().attn_fp8_window_noalloc(ctypes.byref(c), layer, slot_start, n_valid, _dev(q, "q"), _dtype_code(q),
+                                         n_q, int(q_pos_start), float(softmax_scale or 0.0), float(rope_base),
+                                         _dev(out, "out"), int(n_splits), _stream(stream)))
     return out
 
 

@@ -196,6 +196,33 @@ def test_attention_parts_validation():
     assert merge(splits=1) == K.KVR_OK
 
 
+@no_gpu
+def test_noalloc_validation():
+    """The allocation-free call validates like attn_fp8_window, and rejects a
+    call whose split partials would not fit the library's scratch, on the host
+    (no device is touched for any of these)."""
+    c = _cache()
+    lib = K.lib()
+    call = lambda **kw: lib.attn_fp8_window_noalloc(
+        ctypes.byref(kw.get("cache", c)), 0, kw.get("start", 0), kw.get("n_valid", 5788),
+        kw.get("q", FAKE + 0x7000000), K.KVR_BF16, kw.get("n_q", 757), 0, 0.088, kw.get("base", 10000.0),
+        kw.get("out", FAKE + 0x8000000), kw.get("splits", 0), None)
+    assert call(n_valid=0) == K.KVR_EINVAL
+    assert call(start=5788) == K.KVR_EINVAL
+    assert call(q=FAKE + 2) == K.KVR_EALIGN
+    assert call(base=0.5) == K.KVR_EINVAL
+    assert call(cache=_cache(D=96)) == K.KVR_EUNSUPPORTED
+    # 5000 queries x 12 heads in 7 splits: partials beyond 32 MiB (the default
+    # split count for that many queries is 1, which needs no scratch)
+    big = lib.attn_fp8_window_workspace_bytes(ctypes.byref(c), 5000, 5788, 7)
+    assert big > K.NOALLOC_SCRATCH_BYTES
+    assert lib.attn_fp8_window_workspace_bytes(ctypes.byref(c), 5000, 5788, 0) == 0
+    assert call(n_q=5000, splits=7) == K.KVR_EINVAL
+    assert "scratch" in K.kvr_last_error()
+    # the production call fits
+    assert lib.attn_fp8_window_workspace_bytes(ctypes.byref(c), 757, 5788, 0) <= K.NOALLOC_SCRATCH_BYTES
+
+
 def _ws_bytes(rows, D):
     # fp16 normalised partial rows (padded to 256 bytes) + fp32 (max, sum,
     # row exponent, unused) per row
