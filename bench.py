@@ -739,6 +739,7 @@ def cpu_baseline(K, inputs, shp, cache, qpool, ring, chunks, torch):
     L, H, D, W, N, P = shp.n_layers, shp.n_heads, shp.head_dim, shp.window, shp.n_new, shp.passes
     cores = len(os.sched_getaffinity(0))
     os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    oracle.set_threads(int(os.environ["OMP_NUM_THREADS"]))
     lc = oracle.LayerCache(H, D, W)
     lc.k_codes[:] = cache.k_codes[0].cpu().numpy()
     lc.v_codes[:] = cache.v_codes[0].cpu().numpy()
@@ -765,16 +766,39 @@ def cpu_baseline(K, inputs, shp, cache, qpool, ring, chunks, torch):
     oracle.naive(lin_k, lin_v, kn, vn, W, ring.pos_next)
     t_naive = time.perf_counter() - t
     ms = (P * L * t_attn + L * t_write) * 1e3
-    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
-    log(f"oracle: attention call {t_attn:.2f} s, layer write {t_write * 1e3:.1f} ms -> {ms:.0f} ms/step; "
-        f"layer rebase {t_rebase * 1e3:.1f} ms, naive call {t_naive * 1e3:.1f} ms")
-    return {"value": round(ms, 1), "unit": "ms/step", "cores": min(threads, cores), "kind": "oracle",
+    threads = oracle.max_threads()
+    log(f"oracle ({threads} threads): attention call {t_attn:.2f} s, layer write {t_write * 1e3:.1f} ms -> "
+        f"{ms:.0f} ms/step; layer rebase {t_rebase * 1e3:.1f} ms, naive call {t_naive * 1e3:.1f} ms")
+    # the same oracle on one thread: a sixteenth of the call's (query, head)
+    # rows (every 16th row) and one layer's write, scaled to a step
+    one = {}
+    oracle.set_threads(1)
+    try:
+        rows = [(i, h) for i in range(N) for h in range(H)][::16]
+        t = time.perf_counter()
+        oracle.attention(lc, start, ring.n_valid, q, ring.pos_next - N, rows=rows)
+        t_rows = time.perf_counter() - t
+        t = time.perf_counter()
+        oracle.write(lc.copy(), 0, ring.pos_next, kn, vn)
+        t_write1 = time.perf_counter() - t
+        t_attn1 = t_rows * (N * H) / len(rows)
+        ms1 = (P * L * t_attn1 + L * t_write1) * 1e3
+        one = {"value": round(ms1, 1), "unit": "ms/step", "cores": 1,
+               "sample": f"{len(rows)} of the call's {N * H} (query, head) rows (every 16th) and one layer's "
+                         "write on one thread, scaled to the whole call, x240 calls and x60 layers (extrapolated)",
+               "attention_call_s": round(t_attn1, 2), "layer_write_ms": round(t_write1 * 1e3, 2)}
+        log(f"oracle (1 thread): {len(rows)} rows in {t_rows:.2f} s -> attention call {t_attn1:.1f} s, "
+            f"layer write {t_write1 * 1e3:.1f} ms -> {ms1:.0f} ms/step")
+    finally:
+        oracle.set_threads(threads)
+    return {"value": round(ms, 1), "unit": "ms/step", "cores": threads, "kind": "oracle",
             "sample": "one full attention call (757 queries x 12 heads x 5788 keys, fp64) and one "
                       "layer's write, timed on the host, scaled x240 calls and x60 layers "
                       "(extrapolated); also one layer's rebase (x60) and one naive rebuild (x240)",
             "attention_call_s": round(t_attn, 3), "layer_write_ms": round(t_write * 1e3, 2),
             "rebase_ms_extrapolated": round(L * t_rebase * 1e3, 1),
-            "naive_upkeep_ms_per_step_extrapolated": round(P * L * t_naive * 1e3, 1)}
+            "naive_upkeep_ms_per_step_extrapolated": round(P * L * t_naive * 1e3, 1),
+            "single_thread": one}
 
 
 if __name__ == "__main__":

@@ -105,8 +105,19 @@ def lib():
                                            ctypes.c_int, ctypes.c_int, _c_i32p, ctypes.c_int32,
                                            _c_f32p, _c_i64p, _c_i32p, ctypes.c_double,
                                            ctypes.c_double, _c_i32p, ctypes.c_int, _c_f64p]
+        L.orc_set_threads.argtypes = [ctypes.c_int]
+        L.orc_max_threads.restype = ctypes.c_int
         _lib = L
     return _lib
+
+
+def set_threads(n: int) -> None:
+    """Thread count of the oracle's OpenMP loops (for the CPU-baseline timing)."""
+    lib().orc_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(lib().orc_max_threads())
 
 
 def _p(a: np.ndarray, ct):
