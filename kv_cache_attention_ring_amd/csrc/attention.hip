@@ -387,6 +387,32 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int k = 0; k < P; ++k)
         issue_tile<D, PREFIX>(a, kh, vh, scales_h, min(t0 + k, t1 - 1), tiles + k * L::BUF, wave);
+
+    // position form: the rotation depends on the query's position only, so its
+    // (cos, sin) are formed while Q and the first tiles are in flight.  Pair i
+    // of the lane's slice h has frequency index 32h + 16g + i; the angle
+    // (position times theta_i / 2pi, in revolutions) is formed in fp64 and its
+    // fractional part, in [0, 1), goes to the hardware sine and cosine.  theta
+    // for the g = 1 half is theta_{32h+i} * base^(-32/D) (exact to an ulp of
+    // fp64).
+    constexpr int PC = QTAB ? 1 : QV / 2;
+    float pcos[PC], psin[PC];
+    if constexpr (!QTAB) {
+        const double pos = (double)(a.q_pos0 + qi);
+        const double gmul = g ? a.rev_step : 1.0;
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const double r = pos * (a.rev.t[32 * h + i] * gmul);
+                const float fr = (float)__builtin_amdgcn_fract(r);
+                pcos[16 * h + i] = __builtin_amdgcn_cosf(fr);
+                psin[16 * h + i] = __builtin_amdgcn_sinf(fr);
+            }
+        // keep them ahead of the wait below
+#pragma unroll
+        for (int j = 0; j < PC; ++j) asm volatile("" : "+v"(pcos[j]), "+v"(psin[j]));
+    }
     qwait<P * ops_per_tile<D>()>(qraw);
     if constexpr (QTAB) {
         // issued before the tiles, so the wait above covered them too; order
@@ -408,37 +434,24 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
             }
         }
 
-    // rotate: pair i of the lane's slice h has frequency index 32h + 16g + i; the
-    // angle (position times theta_i / 2pi, revolutions) is formed in fp64 and
-    // reduced to [-1/2, 1/2] before the hardware sine and cosine.  theta for
-    // the g = 1 half is theta_{32h+i} * base^(-32/D) (exact to an ulp of fp64).
-    if constexpr (QTAB) {
+    // rotate (rotation rows, or the (cos, sin) formed above)
 #pragma unroll
-        for (int h = 0; h < NH; ++h)
+    for (int h = 0; h < NH; ++h)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < 16; ++i) {
+            float cc, ss;
+            if constexpr (QTAB) {
                 const u32x4 w = csraw[8 * h + i / 2];
-                const float cc = __uint_as_float(w[2 * (i % 2)]), ss = __uint_as_float(w[2 * (i % 2) + 1]);
-                const float x0 = qv[32 * h + 2 * i], x1 = qv[32 * h + 2 * i + 1];
-                qv[32 * h + 2 * i] = x0 * cc - x1 * ss;
-                qv[32 * h + 2 * i + 1] = x0 * ss + x1 * cc;
+                cc = __uint_as_float(w[2 * (i % 2)]);
+                ss = __uint_as_float(w[2 * (i % 2) + 1]);
+            } else {
+                cc = pcos[16 * h + i];
+                ss = psin[16 * h + i];
             }
-    } else {
-        const double pos = (double)(a.q_pos0 + qi);
-        const double gmul = g ? a.rev_step : 1.0;
-#pragma unroll
-        for (int h = 0; h < NH; ++h)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const double rv = a.rev.t[32 * h + i] * gmul;
-                const double r = pos * rv;
-                const float fr = (float)(r - __builtin_rint(r));
-                const float cc = __builtin_amdgcn_cosf(fr), ss = __builtin_amdgcn_sinf(fr);
-                const float x0 = qv[32 * h + 2 * i], x1 = qv[32 * h + 2 * i + 1];
-                qv[32 * h + 2 * i] = x0 * cc - x1 * ss;
-                qv[32 * h + 2 * i + 1] = x0 * ss + x1 * cc;
-            }
-    }
+            const float x0 = qv[32 * h + 2 * i], x1 = qv[32 * h + 2 * i + 1];
+            qv[32 * h + 2 * i] = x0 * cc - x1 * ss;
+            qv[32 * h + 2 * i + 1] = x0 * ss + x1 * cc;
+        }
     // scores in log2 units: softmax_scale * log2(e) (c2) times a per-query
     // power-of-two scale 2^-qk (lanes l and l ^ 32 hold the two halves of one
     // query) multiplies q, so the scaled query has absmax in (224, 448]; the
