@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=20261105, help="base seed of the synthetic inputs")
     ap.add_argument("--pos-steps", type=int, default=10,
                     help="timed steps with the position form of the attention call (0 = skip)")
+    ap.add_argument("--fused-steps", type=int, default=10,
+                    help="steps with each layer's chunk written by its first attention call (0 = skip)")
     ap.add_argument("--graph-steps", type=int, default=10,
                     help="replays of one whole step captured as a graph (0 = skip)")
     ap.add_argument("--rope3d-steps", type=int, default=10,
@@ -199,7 +201,7 @@ def main():
     shp = inputs.PAGE_STEP
     L, H, D, W, N, P = shp.n_layers, shp.n_heads, shp.head_dim, shp.window, shp.n_new, shp.passes
     pre = 8
-    total_steps = (pre + args.warmup + args.steps + args.pos_steps + 3 +
+    total_steps = (pre + args.warmup + args.steps + args.pos_steps + args.fused_steps + 4 +
                    (args.every_pass_steps + 1 if args.every_pass_steps > 0 else 0))
     pos_lo = -inputs.DELTA_MAX - 8 * N
     rope = K.RopeTable(pos_lo, total_steps * N - pos_lo, D, device=dev)
@@ -285,6 +287,44 @@ def main():
         torch.cuda.synchronize()
         pos_ms = p0.elapsed_time(p1) / args.pos_steps
         log(f"position form: {pos_ms:.4f} ms/step")
+
+    # ---- the chunk's write fused into each layer's first call -----------------
+    # attn_fp8_window_write: the pass-0 call of layer l writes layer l's chunk
+    # and attends over the window holding it (one launch pair, no separate
+    # write); the other passes are the position-form calls.  Compared with the
+    # position-form step above (same query form, one 60-layer write launch).
+    fused = None
+    if args.fused_steps > 0:
+        wsf = torch.zeros(max(K.attn_fp8_window_write_workspace_bytes(cache, ring, N, args.splits), 256),
+                          dtype=torch.uint8, device=dev)
+
+        def step_fused(step_idx):
+            k, v = chunks[step_idx % pool]
+            before = ring.copy()
+            K.kvr_ring_after_write(ring, W, N)
+            start = K.kvr_ring_logical_start(ring, W)
+            for p in range(P):
+                for layer in range(L):
+                    if p == 0:
+                        K.attn_fp8_window_write(cache, before, layer, k[layer], v[layer], qpool[layer], rope,
+                                                rope.base, out=outs[layer], n_splits=args.splits, ws=wsf)
+                    else:
+                        attend_pos(layer, p, start)
+
+        step_fused(sidx)                         # untimed: first use of the fused kernels
+        sidx += 1
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record()
+        for _ in range(args.fused_steps):
+            step_fused(sidx)
+            sidx += 1
+        f1.record()
+        torch.cuda.synchronize()
+        ctl = wsf[-K.FUSED_SYNC_BYTES:].view(torch.int32)[:3].tolist()
+        fused = {"ms_per_step": round(f0.elapsed_time(f1) / args.fused_steps, 5), "steps": args.fused_steps,
+                 "control_block_after": ctl}
+        log(f"write fused into each layer's first call: {fused['ms_per_step']:.4f} ms/step "
+            f"(control block {ctl})")
 
     # ---- the chunk written on every denoise pass ------------------------------
     # each pass brings new K/V rows for the step's chunk: they are written to
@@ -655,6 +695,7 @@ def main():
             "rebase_delta": delta,
         },
         "position_form": None if pos_ms is None else {"ms_per_step": round(pos_ms, 5), "steps": args.pos_steps},
+        "fused_write": fused,
         "naive": naive,
         "write_every_pass": every_pass,
         "graph": graph,

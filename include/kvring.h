@@ -200,6 +200,50 @@ int32_t attn_fp8_window_partial(const kvr_cache *cache, int32_t layer, int32_t s
 int32_t attn_fp8_window_merge(const kvr_cache *cache, int32_t n_q, int32_t n_valid, int32_t n_splits,
                               uint16_t *out, void *ws, size_t ws_bytes, void *stream);
 
+/* ---- the chunk's write fused into the call that first reads it -----------
+ * [AI-cache] [NC-cache]: every call of a step reads a window whose newest
+ * n_new rows are the step's chunk, rotated and quantised when written.  One
+ * call that writes the chunk of `layer` and attends over the window holding
+ * it, with the chunk's tokens as the queries (the step's first call of the
+ * layer):
+ *   - the write is kv_write_rope_quant of this one layer with state `before`
+ *     (K row j rotated at position before->pos_next + j, stored at ring slot
+ *     (before->head + j) mod capacity), the same bits;
+ *   - the attention is attn_fp8_window over the window after that write
+ *     (slot_start = kvr_ring_logical_start and n_valid of `before` advanced by
+ *     n_new), query i at position before->pos_next + i, the same bits.
+ * The ring is not modified: call kvr_ring_after_write afterwards.
+ * The new keys are the last n_new in logical order.  When some key splits
+ * hold old keys only, it is one launch: the workgroups of those splits store
+ * the chunk's rows, complete and write back the stores and count themselves
+ * done in the control block; the workgroups whose keys include new rows load
+ * and prepare their queries meanwhile and wait for that count (a bounded
+ * wait) before loading keys.  When every split holds new keys (one split, or
+ * a chunk that is most of the window) the write kernel and then the plain
+ * attention call are launched instead, with the same results.
+ *   k_new, v_new, q : device [n_new][n_heads][head_dim] of `dtype`, 16-byte aligned.
+ *   rope      : device table covering positions pos_next .. pos_next+n_new-1
+ *               (the K rows' rotation); rope_base: the queries' rotary base.
+ *   ws        : device workspace of attn_fp8_window_write_workspace_bytes(...)
+ *               bytes, 256-byte aligned.  Its last 256 bytes are the control
+ *               block, uint32 words: [0] writers done, [1] waiting workgroups
+ *               through, [2] waits that gave up, [3] a poll limit (0: the
+ *               library's, 2^18 polls of about a microsecond each).  Words 0..2 must be zero before the
+ *               first call with this workspace (allocate it zeroed); every call
+ *               leaves words 0 and 1 zero.  A wait that gives up adds one to
+ *               word 2 and turns that workgroup's output rows into NaN; the
+ *               control block must then be zeroed again.  Calls sharing a
+ *               workspace must be ordered (one stream).
+ * Errors: those of kv_write_rope_quant (one layer) and of attn_fp8_window
+ * (also KVR_EINVAL for a workspace smaller than the query's result). */
+size_t  attn_fp8_window_write_workspace_bytes(const kvr_cache *cache, const kvr_ring *before,
+                                              int32_t n_new, int32_t n_splits);
+int32_t attn_fp8_window_write(const kvr_cache *cache, const kvr_ring *before, int32_t layer,
+                              const void *k_new, const void *v_new, const void *q, kvr_dtype dtype,
+                              int32_t n_new, const kvr_rope_table *rope, float softmax_scale,
+                              double rope_base, uint16_t *out, int32_t n_splits, void *ws,
+                              size_t ws_bytes, void *stream);
+
 /* ---- allocation-free attention -------------------------------------------
  * For callers that cannot allocate device memory (code under graph capture,
  * tight serving loops, harnesses that forbid allocation): attn_fp8_window

@@ -52,12 +52,27 @@
 // 2^16 and the fp32 sums cannot overflow).  Splits of one (head, query block)
 // are merged by a second kernel in split order, so a call is deterministic and
 // a linear window gives the same bits as the ring.
+//
+// Fused form (the chunk's write carried by the call that first reads it,
+// [AI-cache]: every call's window holds the chunk's new rows).  The new keys
+// are the last n_new in logical order, so only the splits from s_new on hold
+// any.  The workgroups of the other splits write the chunk's rows after
+// issuing their first tiles (the upkeep kernels' row arithmetic, rowquant.h,
+// with stores that write through to memory), wait for the stores to complete
+// and count themselves done; the workgroups that read new keys load and
+// prepare Q meanwhile, wait for the count, invalidate their stale cache lines
+// and only then stream their tiles.  Writers come first in block order, so on
+// every XCD they are dispatched before any waiting workgroup, and the wait is
+// bounded.  Measured at the production shape this is slower than the separate
+// write launch plus the plain call: the waiting workgroups are released ~15 us
+// into the launch, the writers' own start is delayed too.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
 #include <type_traits>
 
 #include "kvr_internal.h"
+#include "rowquant.h"
 
 namespace kvr {
 namespace {
@@ -288,12 +303,106 @@ __device__ __forceinline__ void wait_tiles(int later) {
     else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * OPT) : "memory");
 }
 
+// Rank of block b among the blocks [lo, lo + n) ordered by (XCD, block), the
+// XCD of a block being b % 8: the blocks of one XCD get consecutive ranks
+// (with lo = 0 and n = the grid, the numbering of the plain form).
+__device__ __forceinline__ int xcd_rank(int b, int lo, int n) {
+    const int x = b % 8;
+    auto upto = [](int m, int y) { return m > y ? (m - 1 - y) / 8 + 1 : 0; };   // blocks < m on XCD y
+    int r = 0;
+    for (int y = 0; y < x; ++y) r += upto(lo + n, y) - upto(lo, y);
+    return r + upto(b, x) - upto(lo, x);
+}
+
+// Fused form, writer workgroup w: the chunk's rows, each written exactly as
+// the write kernel writes it (rowquant.h) but with stores that write through
+// to memory, since workgroups on other XCDs read them in this launch.  Rows
+// are numbered (K/V, token, head) in the inputs' order; writer w takes rows
+// 64 (w + i n_writers) + g, one row per 8-lane group g, the loads of two rows
+// in flight together.
+template <int D, bool BF16>
+__device__ __forceinline__ void fused_write(const AttnArgs &a, int w) {
+    constexpr int EPT = D / rowq::kRowLanes;
+    constexpr int kGroups = kThreads / rowq::kRowLanes;
+    constexpr int kRows = 2;                               // rows per group with loads in flight together
+    const int lane8 = threadIdx.x % rowq::kRowLanes;
+    const int per_kv = a.w_n_new * a.n_heads, rows = 2 * per_kv;
+    const int step = a.n_writers * kGroups;
+    for (int r0 = w * kGroups + (int)threadIdx.x / rowq::kRowLanes; r0 < rows; r0 += kRows * step) {
+        rowq::RawChunk<EPT, BF16> raw[kRows];
+        float4 csv[kRows][EPT / 4];
+        int rem[kRows];
+        bool is_v[kRows];
+#pragma unroll
+        for (int u = 0; u < kRows; ++u) {
+            const int r = min(r0 + u * step, rows - 1);
+            is_v[u] = r >= per_kv;
+            rem[u] = is_v[u] ? r - per_kv : r;             // token * n_heads + head
+            raw[u].load(is_v[u] ? a.w_v : a.w_k, (int64_t)rem[u] * D + lane8 * EPT);
+            const int j = rem[u] / a.n_heads;
+            const float4 *t = reinterpret_cast<const float4 *>(a.w_cs + (int64_t)j * D + lane8 * EPT);
+#pragma unroll
+            for (int v = 0; v < EPT / 4; ++v) csv[u][v] = is_v[u] ? float4{} : t[v];
+        }
+#pragma unroll
+        for (int u = 0; u < kRows; ++u) {
+            if (r0 + u * step >= rows) break;
+            const int j = rem[u] / a.n_heads, h = rem[u] - j * a.n_heads;
+            float x[EPT];
+            raw[u].to_f32(x);
+            if (!is_v[u]) rowq::rotate_pairs<EPT>(x, reinterpret_cast<const float *>(csv[u]));
+            int slot = a.w_head + j;
+            if (slot >= a.cap) slot -= a.cap;
+            const int64_t row = (int64_t)h * a.window + a.prefix + slot;
+            rowq::quantize_store<EPT, true>(x, (is_v[u] ? a.w_v_codes : a.w_k_codes) + row * D + lane8 * EPT,
+                                            (is_v[u] ? a.w_v_scales : a.w_k_scales) + row, lane8 == 0);
+        }
+    }
+}
+
+// Fused form, workgroups that read new keys: wait until every writer has
+// counted itself done (sync[0] == n_writers), at most sync[3] polls (when
+// nonzero; else kFusedSpinLimit); the last of these workgroups through clears
+// sync[0] and sync[1] for the next call.  A wait that gives up adds one to
+// sync[2] and returns true: the workgroup's results are then made NaN.
+__device__ __forceinline__ bool wait_for_writers(const AttnArgs &a, uint8_t *smem) {
+    uint32_t *flag = reinterpret_cast<uint32_t *>(smem);
+    if (threadIdx.x == 0) {
+        uint32_t *sync = a.sync;
+        const uint32_t lim = __hip_atomic_load(sync + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t limit = lim ? lim : kFusedSpinLimit;
+        uint32_t polls = 0, gave_up = 0;
+        while (__hip_atomic_load(sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)a.n_writers) {
+            if (++polls >= limit) {
+                gave_up = 1;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if (gave_up) __hip_atomic_fetch_add(sync + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t n_wait = gridDim.x - (uint32_t)a.n_writers;
+        if (__hip_atomic_fetch_add(sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_wait - 1) {
+            __hip_atomic_store(sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        *flag = gave_up;
+        // the rewritten slots may sit stale in this CU's and this XCD's
+        // caches: one invalidation, ahead of the barrier after which the
+        // workgroup's loads start
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(*flag) != 0;
+}
+
 // QTAB: the queries' rotation comes from (cos, sin) rows, one per query
 // (a.q_cs, [n_q][D/2][2] fp32: the 3-D form, where the angle of a pair is its
 // own axis coordinate times its frequency), instead of position times frequency.
 // PREFIX: keys start with the cache's fixed prefix rows (see slot_of).
-template <int D, bool BF16, bool QTAB, bool PREFIX>
+// FUSE: the fused form (the chunk's write; position form only).
+template <int D, bool BF16, bool QTAB, bool PREFIX, bool FUSE = false>
 __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
+    static_assert(!(FUSE && QTAB), "the fused form takes query positions");
     using L = Lds<D>;
     constexpr int CH = L::CH;
     constexpr int NH = D / 64;          // 64-wide d slices of the QK^T contraction
@@ -311,13 +420,26 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     // straddle two XCDs).
     const int n_qb = (a.n_q + kQB - 1) / kQB;
     int unit, qb;
-    {
+    bool writer = false, bad = false;
+    if constexpr (!FUSE) {
         const int b = blockIdx.x, G = gridDim.x;
         const int xcd = b % 8, k = b / 8;
         const int per = G / 8, extra = G % 8;             // XCDs below `extra` hold per + 1
         const int slot = xcd * per + min(xcd, extra) + k;
         unit = slot / n_qb;
         qb = slot % n_qb;
+    } else {
+        // blocks [0, n_writers) take the (head, split < s_new, query block)
+        // units, the others those of the splits from s_new on, each range
+        // numbered XCD by XCD as above
+        const int b = blockIdx.x, nw = a.n_writers;
+        writer = b < nw;
+        const int lo = writer ? 0 : nw, n = writer ? nw : (int)gridDim.x - nw;
+        const int slot = xcd_rank(b, lo, n);
+        const int s0 = writer ? 0 : a.s_new, ns = writer ? a.s_new : a.n_splits - a.s_new;
+        const int h = slot / (ns * n_qb), r = slot % (ns * n_qb);
+        unit = h * a.n_splits + s0 + r / n_qb;
+        qb = r % n_qb;
     }
     const int head = unit / a.n_splits;
     const int split = unit % a.n_splits;
@@ -384,9 +506,14 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     // start streaming the first P tiles (and their scales); always P of them,
     // so the compiler can count them in its wait for Q (a split shorter than
     // P tiles reloads its last tile into the spare buffers)
+    if (!FUSE || writer) {
 #pragma unroll
-    for (int k = 0; k < P; ++k)
-        issue_tile<D, PREFIX>(a, kh, vh, scales_h, min(t0 + k, t1 - 1), tiles + k * L::BUF, wave);
+        for (int k = 0; k < P; ++k)
+            issue_tile<D, PREFIX>(a, kh, vh, scales_h, min(t0 + k, t1 - 1), tiles + k * L::BUF, wave);
+    }
+    if constexpr (FUSE) {
+        if (writer) fused_write<D, BF16>(a, (int)blockIdx.x);
+    }
 
     // position form: the rotation depends on the query's position only, so its
     // (cos, sin) are formed while Q and the first tiles are in flight.  Pair i
@@ -412,6 +539,21 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
         // keep them ahead of the wait below
 #pragma unroll
         for (int j = 0; j < PC; ++j) asm volatile("" : "+v"(pcos[j]), "+v"(psin[j]));
+    }
+    if constexpr (FUSE) {
+        if (writer) {
+            // the chunk's rows went to memory through the caches: once every
+            // lane's stores are acknowledged, the workgroup counts itself done
+            // (no write-back of this XCD's L2 is needed for them)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (tid == 0) __hip_atomic_fetch_add(a.sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            bad = wait_for_writers(a, smem);
+#pragma unroll
+            for (int k = 0; k < P; ++k)
+                issue_tile<D, PREFIX>(a, kh, vh, scales_h, min(t0 + k, t1 - 1), tiles + k * L::BUF, wave);
+        }
     }
     qwait<P * ops_per_tile<D>()>(qraw);
     if constexpr (QTAB) {
@@ -807,7 +949,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     // other row has e = 0 and is stored as is.
     const float lsum = lsum0 + lsum1;
     const float ltot = lsum + __shfl_xor(lsum, 32);
-    const float f = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+    float f = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+    if constexpr (FUSE) {
+        if (bad) f = __builtin_nanf("");                 // the wait for the writers gave up
+    }
     const bool to_out = a.n_splits == 1;
     uint8_t *ob = tiles + wave * L::OUT_WAVE;
     int ex = 0;
@@ -972,6 +1117,8 @@ hipError_t launch_query_lanes(const float *cs_rows, int n_q, int head_dim, float
     return hipGetLastError();
 }
 
+int attn_query_blocks(int n_q) { return (n_q + kQB - 1) / kQB; }
+
 int attn_default_splits(int n_heads, int n_q, int n_valid) {
     const int n_qb = (n_q + kQB - 1) / kQB;
     const int tiles = (n_valid + kKT - 1) / kKT;
@@ -996,6 +1143,12 @@ static void launch_merge_d(const AttnArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(combine_kernel<D>, dim3((rows + RPB - 1) / RPB), dim3(256), 0, s, a);
 }
 
+template <int D, bool BF16>
+static void launch_fused_d(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
+    if (a.prefix > 0) hipLaunchKernelGGL((attn_kernel<D, BF16, false, true, true>), grid, block, Lds<D>::TOTAL, s, a);
+    else hipLaunchKernelGGL((attn_kernel<D, BF16, false, false, true>), grid, block, Lds<D>::TOTAL, s, a);
+}
+
 template <int D, bool BF16, bool QTAB>
 static void launch_main_d(const AttnArgs &a, dim3 grid, dim3 block, hipStream_t s) {
     if (a.prefix > 0) hipLaunchKernelGGL((attn_kernel<D, BF16, QTAB, true>), grid, block, Lds<D>::TOTAL, s, a);
@@ -1014,6 +1167,15 @@ hipError_t launch_attention_main(const AttnArgs &a, int head_dim, hipStream_t s)
         if (tab) bf16 ? launch_main_d<64, true, true>(a, grid, block, s) : launch_main_d<64, false, true>(a, grid, block, s);
         else bf16 ? launch_main_d<64, true, false>(a, grid, block, s) : launch_main_d<64, false, false>(a, grid, block, s);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_attention_fused(const AttnArgs &a, int head_dim, hipStream_t s) {
+    const int n_qb = (a.n_q + kQB - 1) / kQB;
+    const dim3 grid(n_qb * a.n_heads * a.n_splits), block(kThreads);
+    const bool bf16 = a.dtype == KVR_BF16;
+    if (head_dim == 128) bf16 ? launch_fused_d<128, true>(a, grid, block, s) : launch_fused_d<128, false>(a, grid, block, s);
+    else bf16 ? launch_fused_d<64, true>(a, grid, block, s) : launch_fused_d<64, false>(a, grid, block, s);
     return hipGetLastError();
 }
 

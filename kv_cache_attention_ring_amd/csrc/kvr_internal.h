@@ -78,8 +78,20 @@ struct AttnArgs {
     int32_t prefix, cap;              // key i < prefix: slot i; else prefix + (slot_start + i - prefix) mod cap
     int32_t n_splits, tiles_per_split;
     float softmax_scale;
+    // The chunk's write carried by the attention launch (fused form only):
+    // writer workgroups (those of splits below s_new, whose keys are all old)
+    // store the n_new new rows of this layer, then count themselves done in
+    // sync[0]; the other workgroups wait for that count before loading tiles.
+    const void *w_k, *w_v;            // [n_new][H][D] of `dtype`
+    const float *w_cs;                // rotary table row of the chunk's first position (pair-major)
+    uint8_t *w_k_codes, *w_v_codes;   // this layer's codes and scales (written)
+    float *w_k_scales, *w_v_scales;
+    int32_t w_head, w_n_new;          // ring slot of new token 0, tokens in the chunk
+    int32_t n_writers, s_new;         // writer workgroups; first split holding a new key
+    uint32_t *sync;                   // control block: writers done, waiters through, timeouts, spin limit
 };
 int attn_default_splits(int n_heads, int n_q, int n_valid);
+int attn_query_blocks(int n_q);      // query blocks (workgroups per head and split)
 // (cos, sin) rows [n_q][D/2][2] rearranged so that the attention kernel's load
 // c of lane l of wave w of query block b reads 16 bytes at
 // ((b * 8 + w) * (D / 8) + c) * 64 + l (units of 16 bytes)
@@ -88,6 +100,9 @@ hipError_t launch_query_lanes(const float *cs_rows, int n_q, int head_dim, float
 size_t attn_workspace_bytes(int n_heads, int head_dim, int n_q, int n_splits);
 // the attention kernel (output rows when n_splits == 1, split partials else)
 hipError_t launch_attention_main(const AttnArgs &a, int head_dim, hipStream_t s);
+// the same kernel carrying the chunk's write (a.n_writers > 0, position form)
+hipError_t launch_attention_fused(const AttnArgs &a, int head_dim, hipStream_t s);
+constexpr uint32_t kFusedSpinLimit = 1u << 18;   // polls (each ~1 us: an atomic round trip and a short sleep) before a wait gives up
 // the merge of the split partials into the output rows (nothing for one split)
 hipError_t launch_attention_merge(const AttnArgs &a, int head_dim, hipStream_t s);
 

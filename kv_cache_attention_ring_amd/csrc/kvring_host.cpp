@@ -419,6 +419,102 @@ int32_t attn_fp8_window_merge(const kvr_cache *cache, int32_t n_q, int32_t n_val
                          "attention merge");
 }
 
+// ---- the chunk's write fused into the call that first reads it -------------
+// [AI-cache] [NC-cache]: every call reads a window whose newest n_new rows are
+// the chunk; the step's first call of a layer writes them on the way.
+namespace {
+
+constexpr size_t kSyncBytes = 256;     // control block after the partials
+
+size_t fused_sync_offset(size_t partial_bytes) { return (partial_bytes + 255) / 256 * 256; }
+
+}  // namespace
+
+size_t attn_fp8_window_write_workspace_bytes(const kvr_cache *cache, const kvr_ring *before,
+                                             int32_t n_new, int32_t n_splits) {
+    if (!cache || !before || n_new < 1 || n_splits < 0) return 0;
+    const int32_t W = cache->window - cache->n_prefix;
+    if (W < 1 || n_new > W || before->n_valid < 0 || before->n_valid > W) return 0;
+    const int32_t n_valid = before->n_valid + n_new < W ? before->n_valid + n_new : W;
+    return fused_sync_offset(attn_fp8_window_workspace_bytes(cache, n_new, n_valid, n_splits)) + kSyncBytes;
+}
+
+int32_t attn_fp8_window_write(const kvr_cache *cache, const kvr_ring *before, int32_t layer,
+                              const void *k_new, const void *v_new, const void *q, kvr_dtype dtype,
+                              int32_t n_new, const kvr_rope_table *rope, float softmax_scale,
+                              double rope_base, uint16_t *out, int32_t n_splits, void *ws,
+                              size_t ws_bytes, void *stream) {
+    // the write's arguments, validated as kv_write_rope_quant validates them
+    if (int32_t e = check_cache(cache)) return e;
+    const int32_t W = ring_cap(cache), D = cache->head_dim;
+    if (int32_t e = check_ring(before, W)) return e;
+    if (int32_t e = check_dtype(dtype)) return e;
+    if (!k_new || !v_new) return fail(KVR_EINVAL, "k_new/v_new is NULL");
+    if (!aligned16(k_new) || !aligned16(v_new)) return fail(KVR_EALIGN, "k_new/v_new not 16-byte aligned");
+    if (n_new < 1 || n_new > W) return fail(KVR_EINVAL, "n_new %d not in [1,%d]", n_new, W);
+    if (layer < 0 || layer >= cache->n_layers)
+        return fail(KVR_EINVAL, "layer %d outside cache of %d", layer, cache->n_layers);
+    const float *cs;
+    if (int32_t e = table_rows(rope, D, before->pos_next, n_new, &cs)) return e;
+    // the window after the write, and the chunk's tokens as the queries
+    kvr_ring after = *before;
+    if (int32_t e = kvr_ring_after_write(&after, W, n_new)) return e;
+    const int32_t slot_start = kvr_ring_logical_start(&after, W);
+    const size_t part = attn_fp8_window_workspace_bytes(cache, n_new, after.n_valid, n_splits);
+    const size_t need = fused_sync_offset(part) + kSyncBytes;
+    if (!ws) return fail(KVR_EINVAL, "workspace of %zu bytes required", need);
+    if (ws_bytes < need) return fail(KVR_EINVAL, "workspace %zu < %zu bytes", ws_bytes, need);
+    kvr::AttnArgs a;
+    if (int32_t e = attn_setup(a, cache, layer, slot_start, after.n_valid, q, dtype, n_new,
+                               before->pos_next, softmax_scale, &rope_base, out, n_splits, ws, ws_bytes))
+        return e;
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+        return fail(KVR_EALIGN, "workspace must be 256-byte aligned");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    // splits below s_new hold old keys only (the new keys are the last n_new
+    // in logical order); their workgroups write the chunk
+    const int32_t first_new = a.n_valid - n_new;
+    const int32_t s_new = first_new / (a.tiles_per_split * 64);
+    const int64_t lay = (int64_t)layer * cache->n_heads * cache->window;
+    if (s_new == 0) {
+        // every split reads new keys: the write kernel, then the plain call
+        kvr::WriteArgs w{};
+        w.k_codes = cache->k_codes;
+        w.v_codes = cache->v_codes;
+        w.k_scales = cache->k_scales;
+        w.v_scales = cache->v_scales;
+        w.k_new = k_new;
+        w.v_new = v_new;
+        w.cs = cs;
+        w.n_heads = cache->n_heads;
+        w.window = cache->window;
+        w.prefix = cache->n_prefix;
+        w.cap = W;
+        w.head = before->head;
+        w.n_new = n_new;
+        w.layer0 = layer;
+        w.n_layers = 1;
+        w.dtype = dtype;
+        if (int32_t e = launch_status(kvr::launch_write(w, D, s), "write")) return e;
+        if (int32_t e = launch_status(kvr::launch_attention_main(a, D, s), "attention")) return e;
+        return launch_status(kvr::launch_attention_merge(a, D, s), "attention merge");
+    }
+    a.w_k = k_new;
+    a.w_v = v_new;
+    a.w_cs = cs;
+    a.w_k_codes = cache->k_codes + lay * D;
+    a.w_v_codes = cache->v_codes + lay * D;
+    a.w_k_scales = cache->k_scales + lay;
+    a.w_v_scales = cache->v_scales + lay;
+    a.w_head = before->head;
+    a.w_n_new = n_new;
+    a.s_new = s_new;
+    a.n_writers = cache->n_heads * s_new * kvr::attn_query_blocks(n_new);
+    a.sync = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + fused_sync_offset(part));
+    if (int32_t e = launch_status(kvr::launch_attention_fused(a, D, s), "fused write and attention")) return e;
+    return launch_status(kvr::launch_attention_merge(a, D, s), "attention merge");
+}
+
 // ---- allocation-free attention ------------------------------------------------
 // The split partials of attn_fp8_window_noalloc live in `scratch`, a device
 // array of the library's own (each GPU the library runs on holds one copy

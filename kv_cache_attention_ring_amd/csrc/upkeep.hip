@@ -9,147 +9,28 @@
 //   [WC]       wechild.cn news item 1943 (original per-call upkeep).
 //
 // Every row of head_dim elements is handled by 8 consecutive lanes, each lane
-// owning head_dim/8 contiguous elements (16-byte loads and stores); the row
-// absmax is a 3-step butterfly across those 8 lanes.  Decoding a stored row
-// is the exact E4M3 value times the fp32 row scale (one fp32 product).  The arithmetic order
-// of one element is fixed (rotation: x0*c - x1*s, x0*s + x1*c, each product
-// and sum rounded to fp32; quantisation: y * (448 / absmax) rounded to fp32,
-// then E4M3 round-to-nearest-even via v_cvt_pk_fp8_f32), and this file is
-// built with -ffp-contract=off so no FMA merges those roundings.  The write,
-// rebase and naive kernels share these device helpers, so the ring cache and
-// the naive linear window are bit-identical.
+// owning head_dim/8 contiguous elements; the row arithmetic (rotation of the
+// interleaved pairs, row quantisation) is rowquant.h's, shared by the write,
+// rebase and naive kernels here and by the write the attention kernel can
+// carry, so the ring cache and the naive linear window are bit-identical.
+// Decoding a stored row is the exact E4M3 value times the fp32 row scale (one
+// fp32 product).  This file is also built with -ffp-contract=off, so no FMA
+// merges the roundings of the rebase's dequantisation either.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
 #include "kvr_internal.h"
+#include "rowquant.h"
 
 #pragma clang fp contract(off)
 
 namespace kvr {
 namespace {
 
-typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+using namespace rowq;
 
-constexpr int kRowLanes = 8;          // lanes per row
 constexpr int kBlock = 256;           // threads per workgroup
 constexpr int kRowsPerIter = kBlock / kRowLanes;
-
-__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
-    return __uint_as_float(bits16 << 16);
-}
-
-// A lane's chunk of EPT elements in its storage type, as 16-byte vectors.
-template <int EPT, bool BF16>
-struct RawChunk {
-    static constexpr int kVecs = EPT * (BF16 ? 2 : 4) / 16;
-    uint4 v[kVecs];
-
-    __device__ __forceinline__ void load(const void *base, int64_t elem_off) {
-        const uint4 *p = reinterpret_cast<const uint4 *>(
-            reinterpret_cast<const char *>(base) + elem_off * (BF16 ? 2 : 4));
-#pragma unroll
-        for (int k = 0; k < kVecs; ++k) v[k] = p[k];
-    }
-    __device__ __forceinline__ void store(void *base, int64_t elem_off) const {
-        uint4 *p = reinterpret_cast<uint4 *>(reinterpret_cast<char *>(base) +
-                                             elem_off * (BF16 ? 2 : 4));
-        // (used by the naive rebuild for the shifted window, which the next
-        // call reads from HBM again: nontemporal)
-#pragma unroll
-        for (int k = 0; k < kVecs; ++k)
-            __builtin_nontemporal_store(u32x4v{v[k].x, v[k].y, v[k].z, v[k].w}, reinterpret_cast<u32x4v *>(p + k));
-    }
-    __device__ __forceinline__ void to_f32(float (&x)[EPT]) const {
-#pragma unroll
-        for (int k = 0; k < kVecs; ++k) {
-            const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-            if constexpr (BF16) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    x[8 * k + 2 * q] = bf16_to_f32(w[q] & 0xFFFFu);
-                    x[8 * k + 2 * q + 1] = bf16_to_f32(w[q] >> 16);
-                }
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) x[4 * k + q] = __uint_as_float(w[q]);
-            }
-        }
-    }
-};
-
-// y = R(angle) x on the EPT/2 interleaved pairs; cs holds (cos, sin) per pair.
-template <int EPT>
-__device__ __forceinline__ void rotate_pairs(float (&x)[EPT], const float *cs) {
-#pragma unroll
-    for (int i = 0; i < EPT / 2; ++i) {
-        const float c = cs[2 * i], s = cs[2 * i + 1];
-        const float x0 = x[2 * i], x1 = x[2 * i + 1];
-        const float a = x0 * c;
-        const float b = x1 * s;
-        const float e = x0 * s;
-        const float f = x1 * c;
-        x[2 * i] = a - b;
-        x[2 * i + 1] = e + f;
-    }
-}
-
-// Rows whose absmax lies below 2^-64 are lifted by 2^64 (exact) before the
-// inverse is formed: 448 / a itself overflows fp32 once a < 448 / FLT_MAX, and
-// y 2^64 * fl(448 / (a 2^64)) is the same real number as y * fl(448 / a)
-// wherever that inverse is finite, so no other row changes.
-constexpr float kTinyRow = 0x1p-64f;
-constexpr float kTinyLift = 0x1p64f;
-
-// Row quantisation: absmax over the 8 lanes of the row, scale = a / 448,
-// codes = E4M3_RNE(y * (448 / a)).  Writes EPT codes and (lane 0) the scale;
-// y is lifted in place for tiny rows.
-template <int EPT>
-__device__ __forceinline__ void quantize_store(float (&y)[EPT], uint8_t *codes_dst,
-                                               float *scale_dst, bool lane0) {
-    float a = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) a = fmaxf(a, fabsf(y[e]));
-    a = fmaxf(a, __shfl_xor(a, 1, kRowLanes));
-    a = fmaxf(a, __shfl_xor(a, 2, kRowLanes));
-    a = fmaxf(a, __shfl_xor(a, 4, kRowLanes));
-    uint32_t w[EPT / 4];
-    float scale;
-    if (a == 0.0f) {
-        scale = 0.0f;
-#pragma unroll
-        for (int k = 0; k < EPT / 4; ++k) w[k] = 0u;
-    } else {
-        scale = a / 448.0f;
-        float inv;
-        if (a < kTinyRow) {                 // rare: the row is lifted first
-#pragma unroll
-            for (int e = 0; e < EPT; ++e) y[e] = y[e] * kTinyLift;
-            inv = 448.0f / (a * kTinyLift);
-        } else {
-            inv = 448.0f / a;
-        }
-#pragma unroll
-        for (int k = 0; k < EPT / 4; ++k) {
-            const float t0 = y[4 * k] * inv, t1 = y[4 * k + 1] * inv;
-            const float t2 = y[4 * k + 2] * inv, t3 = y[4 * k + 3] * inv;
-            int pk = __builtin_amdgcn_cvt_pk_fp8_f32(t0, t1, 0, false);
-            pk = __builtin_amdgcn_cvt_pk_fp8_f32(t2, t3, pk, true);
-            w[k] = (uint32_t)pk;
-        }
-    }
-    // the codes are written once and not read again by this launch, a whole
-    // 128-byte row per 8 lanes: nontemporal stores.  The 4-byte scales of
-    // consecutive rows come from different waves: ordinary stores, so they
-    // merge into whole lines in L2 before going to HBM (nontemporal scale
-    // stores measured ~5% slower for the write and the rebase)
-    if constexpr (EPT == 16) {
-        __builtin_nontemporal_store(u32x4v{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4v *>(codes_dst));
-    } else {
-        __builtin_nontemporal_store(u32x2v{w[0], w[1]}, reinterpret_cast<u32x2v *>(codes_dst));
-    }
-    if (lane0) *scale_dst = scale;
-}
 
 // ---------------------------------------------------------------------------
 // Rotary table: cs[p][i] = (cos, sin)(p * theta_i), fp64 angle and trig.

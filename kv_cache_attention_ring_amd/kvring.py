@@ -71,6 +71,11 @@ _SIGS = {
     "attn_fp8_window_partial": (_I32, [ctypes.POINTER(kvr_cache), _I32, _I32, _I32, _P, _I32, _I32, _I64,
                                        _F32, _F64, _P, _I32, _P, _SZ, _P]),
     "attn_fp8_window_merge": (_I32, [ctypes.POINTER(kvr_cache), _I32, _I32, _I32, _P, _P, _SZ, _P]),
+    "attn_fp8_window_write_workspace_bytes": (_SZ, [ctypes.POINTER(kvr_cache), ctypes.POINTER(kvr_ring),
+                                                     _I32, _I32]),
+    "attn_fp8_window_write": (_I32, [ctypes.POINTER(kvr_cache), ctypes.POINTER(kvr_ring), _I32, _P, _P, _P,
+                                     _I32, _I32, ctypes.POINTER(kvr_rope_table), _F32, _F64, _P, _I32, _P,
+                                     _SZ, _P]),
     "attn_fp8_window_noalloc": (_I32, [ctypes.POINTER(kvr_cache), _I32, _I32, _I32, _P, _I32, _I32, _I64,
                                        _F32, _F64, _P, _I32, _P]),
     "naive_upkeep": (_I32, [_P, _P, _P, _P, _I32, _I32, _I32, _I64, _I32, _I32, _I32,
@@ -455,6 +460,51 @@ def attn_fp8_window_merge(cache: KVCache, n_q: int, n_valid: int, out: torch.Ten
     ws_len = ws.numel() * ws.element_size() if ws is not None else 0
     _check(lib().attn_fp8_window_merge(ctypes.byref(c), n_q, n_valid, int(n_splits), _dev(out, "out"),
                                        ws_ptr, ws_len, _stream(stream)))
+    return out
+
+
+def attn_fp8_window_write_workspace_bytes(cache: KVCache, before: kvr_ring, n_new: int,
+                                          n_splits: int = 0) -> int:
+    c = cache.desc()
+    return int(lib().attn_fp8_window_write_workspace_bytes(ctypes.byref(c), ctypes.byref(before), n_new,
+                                                            n_splits))
+
+
+#: size of the control block at the end of a fused-write workspace (uint32 words: writers done,
+#: waiting workgroups through, waits that gave up, poll limit)
+FUSED_SYNC_BYTES = 256
+
+
+def attn_fp8_window_write(cache: KVCache, before: kvr_ring, layer: int, k_new: torch.Tensor,
+                          v_new: torch.Tensor, q: torch.Tensor, rope: RopeTable, rope_base: float = 10000.0,
+                          out: torch.Tensor | None = None, n_splits: int = 0, ws: torch.Tensor | None = None,
+                          softmax_scale: float | None = None, stream=None) -> torch.Tensor:
+    """Write the chunk k_new/v_new ([N][H][D]) of `layer` at ring state `before`
+    and attend with q ([N][H][D], the chunk's tokens) over the window holding
+    it -> out [N][H][D] bf16.  ws: zeroed before its first use (a workspace
+    allocated here is)."""
+    n_layers, n_new, _ = _new_rows(cache, k_new, v_new)
+    if n_layers != 1 or q.shape != k_new.shape or q.dtype != k_new.dtype:
+        raise KVRError(KVR_EINVAL, "k_new, v_new and q must be one layer's [N][H][D] of one dtype")
+    side = stream is not None and stream != torch.cuda.current_stream(q.device)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+        if side:
+            out.record_stream(stream)
+    if out.dtype != torch.bfloat16 or out.shape != q.shape:
+        raise KVRError(KVR_EINVAL, "out must be bf16 with q's shape")
+    if ws is None:
+        ws = torch.zeros(attn_fp8_window_write_workspace_bytes(cache, before, n_new, n_splits),
+                         dtype=torch.uint8, device=q.device)
+        if side:
+            ws.record_stream(stream)
+    c = cache.desc()
+    t = rope.desc()
+    _check(lib().attn_fp8_window_write(ctypes.byref(c), ctypes.byref(before), layer, _dev(k_new, "k_new"),
+                                       _dev(v_new, "v_new"), _dev(q, "q"), _dtype_code(q), n_new, ctypes.byref(t),
+                                       float(softmax_scale or 0.0), float(rope_base), _dev(out, "out"),
+                                       int(n_splits), _dev(ws, "ws"), ws.numel() * ws.element_size(),
+                                       _stream(stream)))
     return out
 
 

@@ -223,6 +223,56 @@ def test_noalloc_validation():
     assert lib.attn_fp8_window_workspace_bytes(ctypes.byref(c), 757, 5788, 0) <= K.NOALLOC_SCRATCH_BYTES
 
 
+def _fused(cache, ring, n_new, table, layer=0, k=FAKE + 0x5000000, v=FAKE + 0x6000000, q=FAKE + 0x7000000,
+           out=FAKE + 0x8000000, dtype=K.KVR_BF16, base=10000.0, splits=0, ws=FAKE + 0x9000000, ws_bytes=None):
+    lib = K.lib()
+    if ws_bytes is None:
+        ws_bytes = lib.attn_fp8_window_write_workspace_bytes(ctypes.byref(cache), ctypes.byref(ring), n_new, splits)
+    return lib.attn_fp8_window_write(ctypes.byref(cache), ctypes.byref(ring), layer, k, v, q, dtype, n_new,
+                                     ctypes.byref(table), 0.0, base, out, splits, ws, ws_bytes, None)
+
+
+@no_gpu
+def test_fused_write_validation():
+    """The fused write + attention call validates the write's and the call's
+    arguments on the host before anything is launched."""
+    c, t, r = _cache(), _table(), K.kvr_ring_init()
+    full = K.kvr_ring(5299, 5299, 5299)          # before the 8th chunk: it wraps
+    assert _fused(_cache(D=96), r, 757, t) == K.KVR_EUNSUPPORTED
+    assert _fused(c, r, 0, t) == K.KVR_EINVAL
+    assert _fused(c, r, 5789, t) == K.KVR_EINVAL
+    assert _fused(c, r, 757, t, layer=1) == K.KVR_EINVAL
+    assert _fused(c, r, 757, t, layer=-1) == K.KVR_EINVAL
+    assert _fused(c, r, 757, t, k=FAKE + 8) == K.KVR_EALIGN
+    assert _fused(c, r, 757, t, v=0) == K.KVR_EINVAL
+    assert _fused(c, r, 757, t, q=0) == K.KVR_EINVAL
+    assert _fused(c, r, 757, t, q=FAKE + 8) == K.KVR_EALIGN
+    assert _fused(c, r, 757, t, out=FAKE + 8) == K.KVR_EALIGN
+    assert _fused(c, r, 757, t, dtype=7) == K.KVR_EUNSUPPORTED
+    assert _fused(c, K.kvr_ring(5788, 0, 0), 757, t) == K.KVR_EINVAL
+    assert _fused(c, K.kvr_ring(0, 0, 9500), 757, t) == K.KVR_EINVAL
+    assert "rotary table" in K.kvr_last_error()
+    assert _fused(c, full, 757, t, ws=0) == K.KVR_EINVAL
+    assert _fused(c, full, 757, t, ws_bytes=1024) == K.KVR_EINVAL
+    assert _fused(c, full, 757, t, ws=FAKE + 0x9000000 + 16) == K.KVR_EALIGN
+    assert _fused(c, full, 757, t, base=0.5) == K.KVR_EINVAL
+    assert _fused(c, full, 757, t, splits=-1) == K.KVR_EINVAL
+
+
+def test_fused_write_workspace_sizes():
+    c = _cache()
+    lib = K.lib()
+    full = K.kvr_ring(5299, 5299, 5299)
+    size = lambda ring, n, s=0: lib.attn_fp8_window_write_workspace_bytes(ctypes.byref(c), ctypes.byref(ring), n, s)
+    # the call's partials over the window after the write, then a 256-byte control block
+    part = lib.attn_fp8_window_workspace_bytes(ctypes.byref(c), 757, 5788, 0)
+    assert part > 0 and size(full, 757) == (part + 255) // 256 * 256 + 256
+    assert size(full, 757, 1) == 256                     # one split: no partials
+    first = lib.attn_fp8_window_workspace_bytes(ctypes.byref(c), 757, 757, 0)
+    assert size(K.kvr_ring_init(), 757) == (first + 255) // 256 * 256 + 256
+    assert size(full, 0) == 0 and size(full, 5789) == 0 and size(K.kvr_ring(0, 5789, 0), 757) == 0
+
+
 def _ws_bytes(rows, D):
     # fp16 normalised partial rows (padded to 256 bytes) + fp32 (max, sum,
     # row exponent, unused) per row
