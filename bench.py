@@ -468,7 +468,6 @@ def main():
         w_ms.append(e[0].elapsed_time(e[1]))
         a_ms += [e[j].elapsed_time(e[j + 1]) for j in range(2, len(e), 2)]
     write_in_step_ms = sum(w_ms) / len(w_ms)
-    attn_in_step_ms = sum(a_ms) / n_meas
     # the write kernel's own rate: launches back to back between two events (a write
     # without the ring bookkeeping stores rows in the same slots each time); each
     # launch takes the next chunk of the pool (8 x 280 MB of bf16 rows), so its
@@ -689,13 +688,14 @@ def main():
             "attention_call_us_p90_single": round(pct(a_sorted, 90) * 1e3, 3),
             "upkeep_share_of_step": round(write_ms / ms_step, 4),
             # each figure above comes from its own loop of launches back to back,
-            # so they are rates, not parts of one step; the parts of a step are
-            # the event pairs inside two measured steps (in_step)
+            # so they are rates, not parts of one step (240 back-to-back calls
+            # alone, below, need not add up with the write to ms_per_step); the
+            # step's own split is step_split
             "attention_ms_per_step_back_to_back": round(attn_ms * P * L, 4),
-            "in_step": {"write_ms": round(write_in_step_ms, 4), "attention_calls_ms": round(attn_in_step_ms, 4),
-                        "sum_ms": round(write_in_step_ms + attn_in_step_ms, 4),
-                        "note": "event pairs around the write and around each of the 240 calls of two "
-                                "steps (the query rows' rearrangement, one small launch, is between them)"},
+            "step_split": {"write_ms": round(write_in_step_ms, 4),
+                           "attention_ms": round(ms_step - write_in_step_ms, 4),
+                           "note": "write_ms: one event pair around the write inside a step; attention_ms: "
+                                   "the step time minus it (the 240 calls and the query rows' rearrangement)"},
             "rebase_ms": round(reb_ms, 4),
             "rebase_GBps": round(reb_gbs, 1),
             "rebase_frac_hbm": round(reb_gbs / HBM_PEAK_GBS, 4),
