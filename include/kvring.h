@@ -224,9 +224,13 @@ int32_t attn_fp8_window_merge(const kvr_cache *cache, int32_t n_q, int32_t n_val
  *   k_new, v_new, q : device [n_new][n_heads][head_dim] of `dtype`, 16-byte aligned.
  *   rope      : device table covering positions pos_next .. pos_next+n_new-1
  *               (the K rows' rotation); rope_base: the queries' rotary base.
- *   ws        : device workspace of attn_fp8_window_write_workspace_bytes(...)
- *               bytes, 256-byte aligned.  Its last 256 bytes are the control
- *               block, uint32 words: [0] writers done, [1] waiting workgroups
+ *   ws        : device workspace of at least
+ *               attn_fp8_window_write_workspace_bytes(...) bytes, 256-byte
+ *               aligned.  Its control block is the 256 bytes at offset
+ *               ws_bytes - 256 rounded down to a multiple of 64 (the last 256
+ *               bytes when ws_bytes is a multiple of 64), whatever the call's
+ *               shape, so a workspace reused by calls of several shapes keeps
+ *               it in one place; uint32 words: [0] writers done, [1] waiting workgroups
  *               through, [2] waits that gave up, [3] a poll limit (0: the
  *               library's, 2^18 polls of about a microsecond each).  Words 0..2 must be zero before the
  *               first call with this workspace (allocate it zeroed); every call

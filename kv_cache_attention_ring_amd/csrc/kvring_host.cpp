@@ -510,7 +510,10 @@ int32_t attn_fp8_window_write(const kvr_cache *cache, const kvr_ring *before, in
     a.w_n_new = n_new;
     a.s_new = s_new;
     a.n_writers = cache->n_heads * s_new * kvr::attn_query_blocks(n_new);
-    a.sync = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + fused_sync_offset(part));
+    // the control block is the workspace's last 256 bytes (64-byte aligned),
+    // wherever this call's partials end: a buffer reused by calls of other
+    // shapes keeps its counters in one place
+    a.sync = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + ((ws_bytes - kSyncBytes) & ~size_t{63}));
     if (int32_t e = launch_status(kvr::launch_attention_fused(a, D, s), "fused write and attention")) return e;
     return launch_status(kvr::launch_attention_merge(a, D, s), "attention merge");
 }

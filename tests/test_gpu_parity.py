@@ -12,6 +12,8 @@ element with the bars in tests/_parity.py.  Cases:
   * the 60-layer batched write of a full step (sampled layers), and the full-
     step configuration the benchmark times: 42 steps of 60-layer writes, all
     4 passes of layers 0 and 59 at steps 1 and 42, then the 60-layer rebase;
+  * 20 heads (more rows per write workgroup than it has row groups), chunks of
+    33 tokens wrapping mid-chunk;
   * edge cases: ring not yet full, one valid key, one query, ragged query
     counts, fp32 inputs at D 128, all-zero rows, scores that grow along the
     window past the lazy-rescale threshold, a chunk as large as the window
@@ -386,6 +388,24 @@ def test_wrap_mid_chunk():
         if step in (0, 6, 7, 15):
             got, ref = run.attention(inputs.np_queries(shp, step, 0), n_splits=0)
             assert_attention(got, ref, f"wrap step {step}")
+
+
+@pytest.mark.parametrize("D,dtype", [(64, torch.bfloat16), (128, torch.float32)])
+def test_many_heads_odd_chunks(D, dtype):
+    """20 heads: a two-token run of the write is 40 rows, more than one pass of
+    the workgroup's 32 row groups; chunks of 33 tokens (the last run holds one
+    token) wrap mid-chunk in a window of 100.  Caches (ring and naive) against
+    the oracle after every write, attention on some steps."""
+    shp = inputs.Shape("test", 1, 20, D, 100, 33)
+    run = SmallRun(shp, dtype=dtype)
+    for step in range(7):
+        _say(f"20 heads D={D} {dtype} step {step}")
+        k, v = inputs.np_chunk(shp, step)
+        run.step(k, v)
+        run.check_cache(f"20 heads step {step}")
+        if step in (0, 3, 6):
+            got, ref = run.attention(inputs.np_queries(shp, step, 0), n_splits=0)
+            assert_attention(got, ref, f"20 heads step {step}")
 
 
 def test_edge_cases_small():
