@@ -51,7 +51,7 @@ def counted_traffic(key="attn_kernel_traffic_bytes"):
 
 def pct(sorted_vals, p):
     """p-th percentile (nearest rank) of an ascending list."""
-    k = max(0, min(len(sorted_vals) - 1, int(round(p / 100.0 * len(sorted_vals) + 0.5)) - 1))
+    k = max(0, min(len(sorted_vals) - 1, math.ceil(p / 100.0 * len(sorted_vals) - 1e-9) - 1))
     return sorted_vals[k]
 
 
