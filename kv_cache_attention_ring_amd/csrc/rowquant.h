@@ -99,9 +99,12 @@ constexpr float kTinyRow = 0x1p-64f;
 constexpr float kTinyLift = 0x1p64f;
 
 // Stores that write through to memory (system-coherent: sc0 sc1), for rows
-// that workgroups on other XCDs read later in the same launch.
+// that workgroups on other XCDs read later in the same launch.  A vector
+// store of more than 8 bytes needs one wait state before a VALU instruction
+// may overwrite its data registers; the compiler inserts it for its own
+// stores but cannot see into an asm statement, so the 16-byte form carries it.
 __device__ __forceinline__ void store_wt(void *p, u32x4v v) {
-    asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1" : : "v"(p), "v"(v) : "memory");
+    asm volatile("global_store_dwordx4 %0, %1, off sc0 sc1\n\ts_nop 0" : : "v"(p), "v"(v) : "memory");
 }
 __device__ __forceinline__ void store_wt(void *p, u32x2v v) {
     asm volatile("global_store_dwordx2 %0, %1, off sc0 sc1" : : "v"(p), "v"(v) : "memory");
