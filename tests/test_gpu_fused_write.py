@@ -175,11 +175,12 @@ def test_fused_write_small(H, D, W, N, dtype, splits, steps, prefill):
         t.fused_step(s, splits)
 
 
-def test_fused_write_with_prefix():
-    t = Twin(4, 128, 600, 50, torch.bfloat16, prefix=40, steps=16)
+@pytest.mark.parametrize("D,dtype,splits", [(128, torch.bfloat16, 0), (64, torch.float32, 3)])
+def test_fused_write_with_prefix(D, dtype, splits):
+    t = Twin(4, D, 600, 50, dtype, prefix=40, steps=16)
     for s in range(14):
-        _say(f"fused with prefix step {s} (n_valid {t.ring.n_valid})")
-        t.fused_step(s, 0)
+        _say(f"fused with prefix D={D} {dtype} step {s} (n_valid {t.ring.n_valid})")
+        t.fused_step(s, splits)
 
 
 @pytest.mark.parametrize("W,N,splits", [(96, 16, 1), (96, 80, 2), (5788, 757, 1)])
