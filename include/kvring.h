@@ -214,32 +214,37 @@ int32_t attn_fp8_window_merge(const kvr_cache *cache, int32_t n_q, int32_t n_val
  *     n_new), query i at position before->pos_next + i, the same bits.
  * The ring is not modified: call kvr_ring_after_write afterwards.
  * The new keys are the last n_new in logical order.  When some key splits
- * hold old keys only, it is one launch: the workgroups of those splits store
- * the chunk's rows, complete and write back the stores and count themselves
+ * hold old keys only, it is one launch: the workgroups of those splits (the
+ * first block numbers, so dispatched first) store the chunk's rows with
+ * stores that write through to memory, wait for them and count themselves
  * done in the control block; the workgroups whose keys include new rows load
- * and prepare their queries meanwhile and wait for that count (a bounded
- * wait) before loading keys.  When every split holds new keys (one split, or
- * a chunk that is most of the window) the write kernel and then the plain
+ * and prepare their queries meanwhile, wait for that count (a bounded wait)
+ * and only then load keys.  When every split holds new keys (one split, or a
+ * chunk that is most of the window) the write kernel and then the plain
  * attention call are launched instead, with the same results.
- *   k_new, v_new, q : device [n_new][n_heads][head_dim] of `dtype`, 16-byte aligned.
+ *   k_new, v_new, q : device [n_new][n_heads][head_dim] of `dtype`, 16-byte
+ *               aligned.
  *   rope      : device table covering positions pos_next .. pos_next+n_new-1
- *               (the K rows' rotation); rope_base: the queries' rotary base.
+ *               (the K rows' rotation); rope_base: the queries' rotary base;
+ *               softmax_scale, out, n_splits: as attn_fp8_window.
  *   ws        : device workspace of at least
  *               attn_fp8_window_write_workspace_bytes(...) bytes, 256-byte
  *               aligned.  Its control block is the 256 bytes at offset
  *               ws_bytes - 256 rounded down to a multiple of 64 (the last 256
- *               bytes when ws_bytes is a multiple of 64), whatever the call's
+ *               bytes when ws_bytes is a multiple of 64) whatever the call's
  *               shape, so a workspace reused by calls of several shapes keeps
- *               it in one place; uint32 words: [0] writers done, [1] waiting workgroups
- *               through, [2] waits that gave up, [3] a poll limit (0: the
- *               library's, 2^18 polls of about a microsecond each).  Words 0..2 must be zero before the
- *               first call with this workspace (allocate it zeroed); every call
- *               leaves words 0 and 1 zero.  A wait that gives up adds one to
- *               word 2 and turns that workgroup's output rows into NaN; the
- *               control block must then be zeroed again.  Calls sharing a
- *               workspace must be ordered (one stream).
- * Errors: those of kv_write_rope_quant (one layer) and of attn_fp8_window
- * (also KVR_EINVAL for a workspace smaller than the query's result). */
+ *               it in one place.  uint32 words: [0] writers done, [1] waiting
+ *               workgroups through, [2] waits that gave up, [3] a poll limit
+ *               (0: the library's, 2^18 polls of about a microsecond each).
+ *               Words 0..2 must be zero before the first call with this
+ *               workspace (allocate it zeroed); every call leaves words 0 and
+ *               1 zero.  A wait that gives up adds one to word 2 and turns
+ *               that workgroup's output rows into NaN; the control block must
+ *               then be zeroed again.  Calls sharing a workspace must be
+ *               ordered (one stream).
+ * Errors: those of kv_write_rope_quant (one layer) and of attn_fp8_window;
+ * KVR_EINVAL for a missing or too small workspace, KVR_EALIGN for one not
+ * 256-byte aligned. */
 size_t  attn_fp8_window_write_workspace_bytes(const kvr_cache *cache, const kvr_ring *before,
                                               int32_t n_new, int32_t n_splits);
 int32_t attn_fp8_window_write(const kvr_cache *cache, const kvr_ring *before, int32_t layer,
