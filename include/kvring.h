@@ -215,13 +215,15 @@ int32_t attn_fp8_window_merge(const kvr_cache *cache, int32_t n_q, int32_t n_val
  * The ring is not modified: call kvr_ring_after_write afterwards.
  * The new keys are the last n_new in logical order.  When some key splits
  * hold old keys only, it is one launch: the workgroups of those splits (the
- * first block numbers, so dispatched first) store the chunk's rows with
+ * first block numbers) store the chunk's rows with
  * stores that write through to memory, wait for them and count themselves
  * done in the control block; the workgroups whose keys include new rows load
  * and prepare their queries meanwhile, wait for that count (a bounded wait)
  * and only then load keys.  When every split holds new keys (one split, or a
- * chunk that is most of the window) the write kernel and then the plain
- * attention call are launched instead, with the same results.
+ * chunk that is most of the window), or when the launch's workgroups could
+ * not all be resident on the GPU at once (so that a waiting workgroup could
+ * hold a writer back), the write kernel and then the plain attention call are
+ * launched instead, with the same results.
  *   k_new, v_new, q : device [n_new][n_heads][head_dim] of `dtype`, 16-byte
  *               aligned.
  *   rope      : device table covering positions pos_next .. pos_next+n_new-1

@@ -1170,6 +1170,26 @@ hipError_t launch_attention_main(const AttnArgs &a, int head_dim, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int D, bool BF16>
+static const void *fused_kernel(bool prefix) {
+    return prefix ? reinterpret_cast<const void *>(&attn_kernel<D, BF16, false, true, true>)
+                  : reinterpret_cast<const void *>(&attn_kernel<D, BF16, false, false, true>);
+}
+
+hipError_t attention_fused_resident(int head_dim, int dtype, bool prefix, int device, int *max_blocks) {
+    const bool bf16 = dtype == KVR_BF16;
+    const void *k = head_dim == 128 ? (bf16 ? fused_kernel<128, true>(prefix) : fused_kernel<128, false>(prefix))
+                                    : (bf16 ? fused_kernel<64, true>(prefix) : fused_kernel<64, false>(prefix));
+    const size_t lds = head_dim == 128 ? Lds<128>::TOTAL : Lds<64>::TOTAL;
+    int per_cu = 0, cus = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kThreads, lds);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+    if (e != hipSuccess) return e;
+    *max_blocks = per_cu * cus;
+    return hipSuccess;
+}
+
 hipError_t launch_attention_fused(const AttnArgs &a, int head_dim, hipStream_t s) {
     const int n_qb = (a.n_q + kQB - 1) / kQB;
     const dim3 grid(n_qb * a.n_heads * a.n_splits), block(kThreads);

@@ -102,6 +102,8 @@ size_t attn_workspace_bytes(int n_heads, int head_dim, int n_q, int n_splits);
 hipError_t launch_attention_main(const AttnArgs &a, int head_dim, hipStream_t s);
 // the same kernel carrying the chunk's write (a.n_writers > 0, position form)
 hipError_t launch_attention_fused(const AttnArgs &a, int head_dim, hipStream_t s);
+// how many workgroups of that kernel can be resident on `device` at once
+hipError_t attention_fused_resident(int head_dim, int dtype, bool prefix, int device, int *max_blocks);
 constexpr uint32_t kFusedSpinLimit = 1u << 18;   // polls (each ~1 us: an atomic round trip and a short sleep) before a wait gives up
 // the merge of the split partials into the output rows (nothing for one split)
 hipError_t launch_attention_merge(const AttnArgs &a, int head_dim, hipStream_t s);

@@ -476,8 +476,22 @@ int32_t attn_fp8_window_write(const kvr_cache *cache, const kvr_ring *before, in
     const int32_t first_new = a.n_valid - n_new;
     const int32_t s_new = first_new / (a.tiles_per_split * 64);
     const int64_t lay = (int64_t)layer * cache->n_heads * cache->window;
-    if (s_new == 0) {
-        // every split reads new keys: the write kernel, then the plain call
+    // the waiting workgroups need every writer to run, whatever order the
+    // hardware dispatches them in: the fused launch only when all of its
+    // workgroups fit on the GPU at once
+    bool resident = false;
+    if (s_new > 0) {
+        int dev = -1, max_blocks = 0;
+        hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+        if (e == hipSuccess)
+            e = kvr::attention_fused_resident(D, dtype, cache->n_prefix > 0, dev, &max_blocks);
+        if (e != hipSuccess) return launch_status(e, "fused write and attention: resident workgroups");
+        const int64_t grid = (int64_t)kvr::attn_query_blocks(n_new) * cache->n_heads * a.n_splits;
+        resident = grid <= max_blocks;
+    }
+    if (!resident) {
+        // every split reads new keys, or the launch would not be resident at
+        // once: the write kernel, then the plain call
         kvr::WriteArgs w{};
         w.k_codes = cache->k_codes;
         w.v_codes = cache->v_codes;

@@ -12,8 +12,9 @@ row (window, slots and positions from the oracle's own token count).  Cases:
     mid-chunk), fp32 and bf16, head_dim 64 and 128, two query blocks, a ring
     filling up over the steps, the workspace reused by every step;
   * a fixed prefix beside the ring;
-  * one split, and a chunk most of the window (every split reads new keys:
-    the write kernel and the plain call are launched instead);
+  * one split, a chunk most of the window (every split reads new keys), and a
+    launch with more workgroups than the GPU holds at once (the write kernel
+    and the plain call are launched instead);
   * the control block back at zero after every call, in one workspace reused
     by every step while the partials before it change size;
   * a poll limit of one (the bounded wait's give-up path): output rows are
@@ -165,6 +166,10 @@ def test_fused_write_production_layer():
     (3, 128, 1000, 300, torch.bfloat16, 3, 6, 0),
     (3, 64, 900, 260, torch.float32, 4, 6, 1),
     (20, 64, 300, 33, torch.bfloat16, 3, 12, 0),
+    # 64 heads: with 5 splits 320 workgroups, more than the GPU holds at once
+    # (the write kernel and the plain call instead); with 3 splits 192, fused
+    (64, 64, 300, 33, torch.bfloat16, 5, 4, 7),
+    (64, 64, 300, 33, torch.bfloat16, 3, 4, 7),
 ])
 def test_fused_write_small(H, D, W, N, dtype, splits, steps, prefill):
     t = Twin(H, D, W, N, dtype, steps=steps + prefill)
