@@ -85,9 +85,10 @@ constexpr int kRunRows = kUnroll * kRowsPerIter;
 // Two tokens per workgroup measured fastest (75.9-76.2 us for 60 layers at the
 // production shape, against 81-82 us for 32 tokens x 4 heads per workgroup:
 // the source was then read in 1 KB pieces of 3 KB token rows, three passes
-// over each region).
+// over each region); the XCD runs below took it to 72.4-74.3 us.
 // ---------------------------------------------------------------------------
 constexpr int kWriteTokens = 2;
+constexpr int kWriteRun = 16;      // token pairs per XCD run (write_kernel's numbering)
 
 template <int D, bool BF16>
 __global__ void __launch_bounds__(kBlock) write_kernel(WriteArgs a) {
@@ -95,10 +96,24 @@ __global__ void __launch_bounds__(kBlock) write_kernel(WriteArgs a) {
     constexpr int T = kWriteTokens;
     __shared__ float4 cs_lds[T * D / 4];
     const int lane8 = threadIdx.x % kRowLanes, grp = threadIdx.x / kRowLanes;
-    const int j0 = blockIdx.x * T;
+    // Workgroups are dealt round-robin over the 8 XCDs (linear block b runs
+    // on XCD b % 8).  Renumber them so that each XCD takes runs of
+    // kWriteRun consecutive blocks of the (layer, K/V, token pair) order --
+    // 32 tokens, as many slots as share a 128-byte line of row scales -- the
+    // runs of the 8 XCDs interleaved: a line of scales then leaves the L2s in
+    // at most two parts rather than in pieces from every XCD.  The last
+    // G mod (8 kWriteRun) blocks keep their own numbers.
+    const int GX = gridDim.x, G = GX * gridDim.y;
+    const int b = blockIdx.y * GX + blockIdx.x;
+    int u = b;
+    if (b < G / (8 * kWriteRun) * (8 * kWriteRun)) {
+        const int xcd = b % 8, k = b / 8;
+        u = ((k / kWriteRun) * 8 + xcd) * kWriteRun + k % kWriteRun;
+    }
+    const int j0 = (u % GX) * T;
     const int nt = min(T, a.n_new - j0);
-    const int kv = blockIdx.y % 2;
-    const int lrel = blockIdx.y / 2;
+    const int kv = (u / GX) % 2;
+    const int lrel = (u / GX) / 2;
     if (kv == 0) {
         // the run's (cos, sin) rows (pair-major, D floats per token)
         for (int i = threadIdx.x; i < T * D / 4; i += kBlock) {
