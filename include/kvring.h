@@ -133,7 +133,9 @@ int32_t kv_rope_table_fill(float *cs, int64_t pos0, int32_t n_pos, int32_t head_
  *                  16-byte aligned; layer_stride_elems a multiple of 8.
  *   rope         : device table covering positions pos_next .. pos_next+n_new-1.
  * Errors: KVR_EINVAL (null, n_new not in [1, window], layer range, table range,
- * table shape), KVR_EALIGN, KVR_EUNSUPPORTED. */
+ * table shape), KVR_EALIGN, KVR_EUNSUPPORTED (head_dim, dtype; also more than
+ * 32767 layers in one call, or n_layers * n_new of 2^31 or more: the kernel's
+ * grid). */
 int32_t kv_write_rope_quant(const kvr_cache *cache, const kvr_ring *before,
                             int32_t layer0, int32_t n_layers,
                             const void *k_new, const void *v_new, kvr_dtype dtype,

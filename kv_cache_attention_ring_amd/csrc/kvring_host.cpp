@@ -117,6 +117,16 @@ int32_t effective_splits(int32_t n_heads, int32_t n_q, int32_t n_valid, int32_t 
     return (tiles + *tps - 1) / *tps;
 }
 
+// The write kernel's grid: one workgroup per two new tokens of each (layer,
+// K/V), numbered with 32-bit block indices; the second extent is 2 n_layers.
+int32_t check_write_grid(int32_t n_layers, int32_t n_new) {
+    const int64_t gy = 2 * (int64_t)n_layers, gx = ((int64_t)n_new + 1) / 2;
+    if (gy > 65535 || gx * gy >= (int64_t{1} << 31))
+        return fail(KVR_EUNSUPPORTED, "a write of %d layers x %d tokens exceeds the kernel's grid", n_layers,
+                    n_new);
+    return KVR_OK;
+}
+
 int32_t mod_w(int64_t x, int32_t W) {
     int64_t r = x % W;
     return (int32_t)(r < 0 ? r + W : r);
@@ -196,6 +206,7 @@ int32_t kv_write_rope_quant(const kvr_cache *cache, const kvr_ring *before, int3
     if (layer0 < 0 || n_layers < 1 || layer0 + n_layers > cache->n_layers)
         return fail(KVR_EINVAL, "layers [%d,%d) outside cache of %d", layer0, layer0 + n_layers,
                     cache->n_layers);
+    if (int32_t e = check_write_grid(n_layers, n_new)) return e;
     const int64_t per_layer = (int64_t)n_new * cache->n_heads * D;
     if (n_layers > 1 && (layer_stride_elems < per_layer || layer_stride_elems % 8 != 0))
         return fail(KVR_EINVAL, "layer_stride_elems %lld must be >= %lld and a multiple of 8",
@@ -681,6 +692,7 @@ int32_t kv_write_prefix_rows(const kvr_cache *cache, int32_t slot0, int32_t laye
     if (layer0 < 0 || n_layers < 1 || layer0 + n_layers > cache->n_layers)
         return fail(KVR_EINVAL, "layers [%d,%d) outside cache of %d", layer0, layer0 + n_layers,
                     cache->n_layers);
+    if (int32_t e = check_write_grid(n_layers, n_tok)) return e;
     const int64_t per_layer = (int64_t)n_tok * cache->n_heads * D;
     if (n_layers > 1 && (layer_stride_elems < per_layer || layer_stride_elems % 8 != 0))
         return fail(KVR_EINVAL, "layer_stride_elems %lld must be >= %lld and a multiple of 8",

@@ -123,6 +123,15 @@ def test_write_validation():
     assert _write(c, r, 757, _table(D=64)) == K.KVR_EINVAL
     assert _write(_cache(L=60), r, 757, t, n_layers=60, stride=5) == K.KVR_EINVAL
     assert _write(_cache(base=FAKE + 4), r, 757, t) == K.KVR_EALIGN
+    # beyond the write kernel's grid: more than 32767 layers, or 2^31 blocks
+    assert _write(_cache(L=40000), r, 757, t, n_layers=40000, stride=757 * 12 * 128) == K.KVR_EUNSUPPORTED
+    assert "grid" in K.kvr_last_error()
+    big = _cache(W=(1 << 23), L=600)
+    assert _write(big, r, 1 << 23, t, n_layers=600, stride=(1 << 23) * 12 * 128) == K.KVR_EUNSUPPORTED
+    # 32767 layers pass the grid check (and fail later, on a position outside the table)
+    assert _write(_cache(L=32767), K.kvr_ring(0, 0, 9500), 757, t, n_layers=32767,
+                  stride=757 * 12 * 128) == K.KVR_EINVAL
+    assert "rotary table" in K.kvr_last_error()
 
 
 @no_gpu
