@@ -29,20 +29,37 @@ HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 
 
+# the sources the attention kernels are compiled from
+KERNEL_SOURCES = ("attention.hip", "rowquant.h", "kvr_internal.h")
+
+
+def kernel_code_digest(root=None):
+    """sha256 of the attention kernels' sources with comments and whitespace
+    removed: it changes with the code, not with its comments."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(root or ROOT, "kv_cache_attention_ring_amd", "csrc", name)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update((name + "\n" + " ".join(src.split()) + "\n").encode())
+    return h.hexdigest()
+
+
 def counted_traffic(key="attn_kernel_traffic_bytes"):
     """HBM bytes per launch from the committed counter summary (the attention
     kernel's by default, or `attn_call_traffic_bytes` for the whole call), or
-    None when the attention source has changed since the counters were taken."""
-    import hashlib
+    None when the kernels' code has changed since the counters were taken."""
     import re
     prof = os.path.join(ROOT, "profiles", "attn_traffic_counters.md")
-    src = os.path.join(ROOT, "kv_cache_attention_ring_amd", "csrc", "attention.hip")
     try:
         text = open(prof).read()
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        digest = kernel_code_digest()
     except OSError:
         return None
-    m = re.search(r"attention\.hip sha256: ([0-9a-f]{64})", text)
+    m = re.search(r"kernel code sha256: ([0-9a-f]{64})", text)
     t = re.search(key + r": (\d+)", text)
     if not m or not t or m.group(1) != digest:
         return None

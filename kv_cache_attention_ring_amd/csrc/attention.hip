@@ -731,14 +731,19 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) s[kb][4 * q + r] = s[kb][4 * q + r] * f[r] + cofs;
             }
-        // running max as a tree (depth 4 instead of a 16-long chain)
-        float m8[8];
+        // running max as a tree of three-input maxima (16 of them for 32
+        // values, depth 4): ten of three scores, four of three of those, then
+        // the last two with the two scores left over
+        float m10[10];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            m8[i] = fmaxf(fmaxf(s[i / 4][4 * (i % 4)], s[i / 4][4 * (i % 4) + 1]),
-                          fmaxf(s[i / 4][4 * (i % 4) + 2], s[i / 4][4 * (i % 4) + 3]));
-        float mx = fmaxf(fmaxf(fmaxf(m8[0], m8[1]), fmaxf(m8[2], m8[3])),
-                         fmaxf(fmaxf(m8[4], m8[5]), fmaxf(m8[6], m8[7])));
+        for (int i = 0; i < 10; ++i)
+            m10[i] = fmaxf(fmaxf(s[(3 * i) / 16][(3 * i) % 16], s[(3 * i + 1) / 16][(3 * i + 1) % 16]),
+                           s[(3 * i + 2) / 16][(3 * i + 2) % 16]);
+        float m4[4];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) m4[i] = fmaxf(fmaxf(m10[3 * i], m10[3 * i + 1]), m10[3 * i + 2]);
+        m4[3] = fmaxf(fmaxf(m10[9], s[1][14]), s[1][15]);
+        float mx = fmaxf(fmaxf(fmaxf(m4[0], m4[1]), m4[2]), m4[3]);
         const int lim = a.n_valid - t * kKT;              // valid keys of this tile
         if (lim < kKT) {                                  // last tile of the window
             mx = -INFINITY;
@@ -885,7 +890,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     land(-1, 0);
     land(-1, 1);
     lds_barrier();
-    half_m(t0 - 1, tiles, vt_base, no{}, yes{});       // S^T of tile t0
+    if (lead) half_m(t0 - 1, tiles, vt_base, no{}, yes{});   // S^T of tile t0 (lead group)
     {                                                  // V^T of tile t0
         v2i ut[NCV];
         f32x4 sv[NCV][2];
@@ -898,13 +903,26 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     lds_barrier();
 
     // Both groups run the same loop; the trailing group enters it one
-    // interval late (an extra barrier first), the lead group leaves it with an
-    // extra barrier, so both pass the same 2n+1 barriers.
+    // interval late (its S^T of tile t0 and an extra barrier first), the lead
+    // group leaves it with an extra barrier, so both pass the same 2n+1
+    // barriers.
     //   V(u): scores and weights of tile u, V^T of tile u+1 (buffer (u+1)%3)
     //   M(u): O^T += V^T(u) . P^T(u), S^T of tile u+1
     // V^T(u+1) is written in intervals 2u, 2u+1 and read in 2u+3, 2u+4; its
     // buffer last held V^T(u-2), read in 2u-3, 2u-2.
-    if (!lead) lds_barrier();
+    if (!lead) {
+        // the trailing group's S^T of tile t0, in the interval in which the
+        // lead group runs V(t0) (its matrix work then pairs with that VALU
+        // half-step rather than with the lead group's own S^T in the prologue)
+        __builtin_amdgcn_s_setprio(1);
+        half_m(t0 - 1, tiles, vt_base, no{}, yes{});
+        __builtin_amdgcn_s_setprio(0);
+        lds_barrier();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(fkr[kb][q]));
+    }
     int bcur = 0;                                      // tile buffer of tile t0+u
     int vcur = 0;                                      // V^T buffer of tile t0+u
     for (int u = 0; u < n; ++u) {

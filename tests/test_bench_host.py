@@ -1,5 +1,5 @@
 """Host-side logic of bench.py (no GPU): the one-GPU refusal, the traffic
-figure tied to the attention source it was counted on, the percentile rule."""
+figure tied to the kernel code it was counted on, the percentile rule."""
 import importlib.util
 import json
 import os
@@ -25,20 +25,26 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert "one GPU" in msg["error"]
 
 
-def test_traffic_counts_belong_to_the_source_they_were_taken_on(tmp_path):
+def test_traffic_counts_belong_to_the_code_they_were_taken_on(tmp_path):
     b = _bench()
-    # the committed counters match the committed attention source
+    # the committed counters match the committed kernel code
     kern = b.counted_traffic()
     call = b.counted_traffic("attn_call_traffic_bytes")
     assert kern is not None and call is not None and call > kern > 23_000_000
-    # an edited source (a copy with one byte more) voids them
     (tmp_path / "profiles").mkdir()
     shutil.copy(os.path.join(ROOT, "profiles", "attn_traffic_counters.md"), tmp_path / "profiles")
     src_dir = tmp_path / "kv_cache_attention_ring_amd" / "csrc"
     src_dir.mkdir(parents=True)
-    with open(os.path.join(ROOT, "kv_cache_attention_ring_amd", "csrc", "attention.hip"), "rb") as f:
-        (src_dir / "attention.hip").write_bytes(f.read() + b"\n")
+    for name in b.KERNEL_SOURCES[1:]:
+        shutil.copy(os.path.join(ROOT, "kv_cache_attention_ring_amd", "csrc", name), src_dir)
+    with open(os.path.join(ROOT, "kv_cache_attention_ring_amd", "csrc", "attention.hip")) as f:
+        src = f.read()
     b.ROOT = str(tmp_path)
+    # a comment or a blank line more keeps them
+    (src_dir / "attention.hip").write_text(src + "\n// a note\n/* and\n another */\n\n")
+    assert b.counted_traffic() == kern
+    # a code change voids them
+    (src_dir / "attention.hip").write_text(src + "\nstatic int one_more;\n")
     assert b.counted_traffic() is None
 
 
