@@ -1019,8 +1019,10 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     else stage(std::false_type{});
     if (!to_out && g == 0 && q_ok) {
         const int64_t row = ((int64_t)split * a.n_q + qi) * a.n_heads + head;
-        // running max (log2 units), denominator, exponent of the stored row
-        *reinterpret_cast<f32x4 *>(a.part_ml + 4 * row) = f32x4{kShift - cofs, ltot, (float)ex, 0.0f};
+        // running max (log2 units), denominator, exponent of the stored row;
+        // written through to memory like the partial rows (below)
+        const f32x4 mlv = {kShift - cofs, ltot, (float)ex, 0.0f};
+        rowq::store_wt(a.part_ml + 4 * row, __builtin_bit_cast(rowq::u32x4v, mlv));
     }
     // the rows were written by other lanes of this wave: wait for the LDS
     // writes and keep the compiler from moving the reads above them
@@ -1034,8 +1036,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
         const u32x4 v = *reinterpret_cast<const u32x4 *>(ob + r * (2 * D) + 8 * ((2 * k) ^ ((2 * r) & (D / 4 - 2))));
         uint16_t *dst = to_out ? a.out + ((int64_t)qr * a.n_heads + head) * D
                                : a.part_o + (((int64_t)split * a.n_q + qr) * a.n_heads + head) * D;
-        // written once, read by another kernel (or the caller): nontemporal
-        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst + 8 * k));
+        // written once, read by another kernel (or the caller).  Output rows:
+        // nontemporal.  Split partials: written through to memory, so that
+        // the L2s hold no dirty partial lines when the launch ends (their
+        // write-back at the end of the launch delays the merge: 0.5-0.7 us a
+        // call against nontemporal stores)
+        if (to_out) __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst + 8 * k));
+        else rowq::store_wt(dst + 8 * k, __builtin_bit_cast(rowq::u32x4v, v));
     }
 }
 
