@@ -708,6 +708,37 @@ def test_step_batched_write_60_layers():
         assert not arr[:, :, untouched].any(), n
 
 
+@pytest.mark.parametrize("L,H,D,N,dtype", [(5, 3, 64, 200, torch.float32), (3, 5, 128, 300, torch.bfloat16)])
+def test_multi_layer_write_mid_sizes(L, H, D, N, dtype):
+    """Multi-layer writes whose grids hold both workgroups renumbered into
+    per-XCD runs and the grid's last blocks left in place (5 layers x 100
+    token pairs: 896 + 104 blocks; 3 layers x 150: 896 + 4), against the
+    oracle on every layer, the chunk wrapping at the end of the ring."""
+    W = 2 * N + 37
+    shp = inputs.Shape("test", L, H, D, W, N)
+    cache = K.KVCache(L, H, D, W)
+    rope = K.RopeTable(0, 4 * N, D)
+    head = W - N // 3                                   # the chunk wraps
+    ring = K.kvr_ring(head, W, 2 * N)
+    k, v = inputs.torch_chunk(shp, 1, 0, "cpu", dtype=dtype, n_layers=L)
+    _say(f"{L}-layer write, {H} heads, D {D}, N {N}, {dtype}")
+    K.kv_write_rope_quant(cache, ring, 0, k.cuda(), v.cuda(), rope)
+    torch.cuda.synchronize()
+    slots = (head + np.arange(N)) % W
+    got = {n: _np(getattr(cache, n)) for n in ("k_codes", "v_codes", "k_scales", "v_scales")}
+    for layer in range(L):
+        orc = oracle.LayerCache(H, D, W)
+        oracle.write(orc, head, 2 * N, _f32(k[layer]), _f32(v[layer]))
+        for n in ("k", "v"):
+            assert_codes(got[f"{n}_codes"][layer][:, slots], getattr(orc, f"{n}_codes")[:, slots],
+                         f"layer {layer} {n}")
+            assert_scales(got[f"{n}_scales"][layer][:, slots], getattr(orc, f"{n}_scales")[:, slots],
+                          f"layer {layer} {n}")
+    untouched = np.setdiff1d(np.arange(W), slots)
+    for n, arr in got.items():
+        assert not arr[:, :, untouched].any(), n
+
+
 def test_extreme_sizes():
     """A chunk as large as the window (every slot rewritten in one write, twice,
     the second time wrapping from a non-zero head), and 3000 queries (12 query
