@@ -215,17 +215,18 @@ int32_t attn_fp8_window_merge(const kvr_cache *cache, int32_t n_q, int32_t n_val
  *     (slot_start = kvr_ring_logical_start and n_valid of `before` advanced by
  *     n_new), query i at position before->pos_next + i, the same bits.
  * The ring is not modified: call kvr_ring_after_write afterwards.
- * The new keys are the last n_new in logical order.  When some key splits
- * hold old keys only, it is one launch: the workgroups of those splits (the
- * first block numbers) store the chunk's rows with
- * stores that write through to memory, wait for them and count themselves
- * done in the control block; the workgroups whose keys include new rows load
- * and prepare their queries meanwhile, wait for that count (a bounded wait)
- * and only then load keys.  When every split holds new keys (one split, or a
- * chunk that is most of the window), or when the launch's workgroups could
- * not all be resident on the GPU at once (so that a waiting workgroup could
- * hold a writer back), the write kernel and then the plain attention call are
- * launched instead, with the same results.
+ * The new keys are the last n_new in logical order; the key tiles are dealt
+ * to the splits in turn (split s takes tiles s, s + S, ...), so they sit at
+ * the end of every split.  When all of the launch's workgroups can be
+ * resident on the GPU at once, it is one launch: every workgroup issues its
+ * first tiles of old keys, stores its share of the chunk's rows with stores
+ * that write through to memory, waits for them and counts itself done in the
+ * control block; a workgroup whose split holds new keys waits for every
+ * share (a bounded wait) before it loads its first tile holding new keys, and
+ * loads those past stale cached copies.  When the workgroups could not all be
+ * resident at once (a waiting workgroup could then hold a writer back), the
+ * write kernel and then the plain attention call are launched instead, with
+ * the same results.
  *   k_new, v_new, q : device [n_new][n_heads][head_dim] of `dtype`, 16-byte
  *               aligned.
  *   rope      : device table covering positions pos_next .. pos_next+n_new-1

@@ -18,8 +18,9 @@
 // cached row).  Keys are visited in logical window order (slot_start + j) mod W.
 //
 // Work decomposition.  A workgroup owns one head, a block of 256 queries and a
-// contiguous range of 64-key tiles (a "split"); each of its 8 waves (two per
-// SIMD) owns 32 queries.  Key tiles go global -> LDS with direct loads
+// "split" of the 64-key tiles: with S splits, split s takes tiles s, s + S,
+// s + 2S, ... in that order; each of its 8 waves (two per SIMD) owns 32
+// queries.  Key tiles go global -> LDS with direct loads
 // (global_load_lds, 16 bytes a lane, no VGPR staging) into five buffers, four
 // tiles in flight.  The two waves of a SIMD alternate between a VALU
 // half-step and a matrix half-step (see the main loop); two LDS-only
@@ -55,17 +56,16 @@
 //
 // Fused form (the chunk's write carried by the call that first reads it,
 // [AI-cache]: every call's window holds the chunk's new rows).  The new keys
-// are the last n_new in logical order, so only the splits from s_new on hold
-// any.  The workgroups of the other splits write the chunk's rows after
-// issuing their first tiles (the upkeep kernels' row arithmetic, rowquant.h,
-// with stores that write through to memory), wait for the stores to complete
-// and count themselves done; the workgroups that read new keys load and
-// prepare Q meanwhile, wait for the count, invalidate their stale cache lines
-// and only then stream their tiles.  Writers come first in block order, so on
-// every XCD they are dispatched before any waiting workgroup, and the wait is
-// bounded.  Measured at the production shape this is slower than the separate
-// write launch plus the plain call: the waiting workgroups are released ~15 us
-// into the launch, the writers' own start is delayed too.
+// are the last n_new in logical order, so with the tiles dealt in turn they
+// sit at the end of every split.  Every workgroup writes its share of the
+// chunk's rows after issuing its first tiles (the upkeep kernels' row
+// arithmetic, rowquant.h, with stores that write through to memory), waits
+// for its stores to complete and counts itself done; before it streams its
+// first tile holding new keys it waits (bounded) for the count to reach the
+// grid, and it streams those tiles with device-scope loads, which miss any
+// stale copy.  At the production shape that tile comes ~11 tiles into a
+// split, long after the writes, so the wait is a single poll.  The host takes
+// this form only when the whole grid can be resident at once.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -113,7 +113,8 @@ struct Lds {
     static constexpr int F_OFF = K_BYTES + V_BYTES;
     static constexpr int BUF = F_OFF + kNW * 64 * 4;
     static constexpr int TILE_OFF = 3 * VT_BYTES;
-    static constexpr int TOTAL = TILE_OFF + kNBuf * BUF;
+    static constexpr int FLAG_OFF = TILE_OFF + kNBuf * BUF;   // one word: the outcome of a wait
+    static constexpr int TOTAL = FLAG_OFF + 16;
     // after the loop the tile buffers stage the output rows (2D bytes each)
     static constexpr int OUT_WAVE = kQW * 2 * D;
     static_assert(kNW * OUT_WAVE <= kNBuf * BUF, "output staging fits the tile buffers");
@@ -257,7 +258,11 @@ __device__ __forceinline__ int slot_of(const AttnArgs &a, int idx) {
 template <int D>
 constexpr int ops_per_tile() { return D == 128 ? 3 : 2; }
 
-template <int D, bool PREFIX>
+// AUX: the loads' cache policy (kSc1: device scope, for rows written in this
+// launch by workgroups that may run on other XCDs; such a load misses in any
+// cache that may hold an older copy of the line).
+constexpr int kSc1 = 16;
+template <int D, bool PREFIX, int AUX = 0>
 __device__ __forceinline__ void issue_tile(const AttnArgs &a, const uint8_t *kh, const uint8_t *vh,
                                            const float *scales_h, int tile, uint8_t *buf, int wave) {
     using L = Lds<D>;
@@ -270,8 +275,8 @@ __device__ __forceinline__ void issue_tile(const AttnArgs &a, const uint8_t *kh,
         const uint32_t srow = (uint32_t)slot_of<PREFIX>(a, tile * kKT + row) * D;
         const uint32_t offk = srow + 16 * (pos ^ (swz_k<D>(row) & (CH - 1)));
         const uint32_t offv = srow + 16 * (pos ^ (swz_v<D>(row) & (CH - 1)));
-        __builtin_amdgcn_global_load_lds(kh + offk, (LDS_AS void *)(buf + 16 * p0), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vh + offv, (LDS_AS void *)(buf + L::K_BYTES + 16 * p0), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(kh + offk, (LDS_AS void *)(buf + 16 * p0), 16, 0, AUX);
+        __builtin_amdgcn_global_load_lds(vh + offv, (LDS_AS void *)(buf + L::K_BYTES + 16 * p0), 16, 0, AUX);
     } else {
         const bool is_k = wave < 4;
         const int p0 = 64 * (wave % 4);
@@ -280,11 +285,11 @@ __device__ __forceinline__ void issue_tile(const AttnArgs &a, const uint8_t *kh,
         const uint32_t off = (uint32_t)slot_of<PREFIX>(a, tile * kKT + row) * D +
                              16 * (pos ^ ((is_k ? swz_k<D>(row) : swz_v<D>(row)) & (CH - 1)));
         __builtin_amdgcn_global_load_lds((is_k ? kh : vh) + off,
-                                         (LDS_AS void *)(buf + (is_k ? 0 : L::K_BYTES) + 16 * p0), 16, 0, 0);
+                                         (LDS_AS void *)(buf + (is_k ? 0 : L::K_BYTES) + 16 * p0), 16, 0, AUX);
     }
     const int key = 16 * (wave % 4) + lane % 16;
     __builtin_amdgcn_global_load_lds(scales_h + slot_of<PREFIX>(a, tile * kKT + key),
-                                     (LDS_AS void *)(buf + L::F_OFF + 256 * wave), 4, 0, 0);
+                                     (LDS_AS void *)(buf + L::F_OFF + 256 * wave), 4, 0, AUX);
 }
 
 // scale slot of key k (0..63): K sk_j or V sv_j
@@ -303,23 +308,12 @@ __device__ __forceinline__ void wait_tiles(int later) {
     else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * OPT) : "memory");
 }
 
-// Rank of block b among the blocks [lo, lo + n) ordered by (XCD, block), the
-// XCD of a block being b % 8: the blocks of one XCD get consecutive ranks
-// (with lo = 0 and n = the grid, the numbering of the plain form).
-__device__ __forceinline__ int xcd_rank(int b, int lo, int n) {
-    const int x = b % 8;
-    auto upto = [](int m, int y) { return m > y ? (m - 1 - y) / 8 + 1 : 0; };   // blocks < m on XCD y
-    int r = 0;
-    for (int y = 0; y < x; ++y) r += upto(lo + n, y) - upto(lo, y);
-    return r + upto(b, x) - upto(lo, x);
-}
-
-// Fused form, writer workgroup w: the chunk's rows, each written exactly as
-// the write kernel writes it (rowquant.h) but with stores that write through
-// to memory, since workgroups on other XCDs read them in this launch.  Rows
-// are numbered (K/V, token, head) in the inputs' order; writer w takes rows
-// 64 (w + i n_writers) + g, one row per 8-lane group g, the loads of two rows
-// in flight together.
+// Fused form, workgroup w's share of the chunk: its rows, each written
+// exactly as the write kernel writes it (rowquant.h) but with stores that
+// write through to memory, since workgroups on other XCDs read them in this
+// launch.  Rows are numbered (K/V, token, head) in the inputs' order;
+// workgroup w takes rows 64 (w + i n_writers) + g, one row per 8-lane group
+// g, the loads of two rows in flight together.
 template <int D, bool BF16>
 __device__ __forceinline__ void fused_write(const AttnArgs &a, int w) {
     constexpr int EPT = D / rowq::kRowLanes;
@@ -360,13 +354,15 @@ __device__ __forceinline__ void fused_write(const AttnArgs &a, int w) {
     }
 }
 
-// Fused form, workgroups that read new keys: wait until every writer has
-// counted itself done (sync[0] == n_writers), at most sync[3] polls (when
-// nonzero; else kFusedSpinLimit); the last of these workgroups through clears
+// Fused form, before a workgroup streams its first tile holding new keys:
+// thread 0 polls until every workgroup has counted its share of the chunk
+// written (sync[0] == n_writers), at most sync[3] polls (when nonzero; else
+// kFusedSpinLimit); the last of the n_waiters workgroups through clears
 // sync[0] and sync[1] for the next call.  A wait that gives up adds one to
-// sync[2] and returns true: the workgroup's results are then made NaN.
-__device__ __forceinline__ bool wait_for_writers(const AttnArgs &a, uint8_t *smem) {
-    uint32_t *flag = reinterpret_cast<uint32_t *>(smem);
+// sync[2].  Thread 0 leaves the outcome (1: gave up) in *flag, which the
+// caller's barrier publishes to the workgroup.  No cache is invalidated: the
+// tiles that hold new keys are streamed with device-scope loads.
+__device__ __forceinline__ void poll_writers(const AttnArgs &a, uint32_t *flag) {
     if (threadIdx.x == 0) {
         uint32_t *sync = a.sync;
         const uint32_t lim = __hip_atomic_load(sync + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -380,19 +376,13 @@ __device__ __forceinline__ bool wait_for_writers(const AttnArgs &a, uint8_t *sme
             __builtin_amdgcn_s_sleep(2);
         }
         if (gave_up) __hip_atomic_fetch_add(sync + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t n_wait = gridDim.x - (uint32_t)a.n_writers;
-        if (__hip_atomic_fetch_add(sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_wait - 1) {
+        if (__hip_atomic_fetch_add(sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            (uint32_t)a.n_waiters - 1) {
             __hip_atomic_store(sync, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(sync + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         *flag = gave_up;
-        // the rewritten slots may sit stale in this CU's and this XCD's
-        // caches: one invalidation, ahead of the barrier after which the
-        // workgroup's loads start
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
-    __syncthreads();
-    return __builtin_amdgcn_readfirstlane(*flag) != 0;
 }
 
 // QTAB: the queries' rotation comes from (cos, sin) rows, one per query
@@ -419,34 +409,35 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     // from HBM once rather than once per query block (at most 7 ranges
     // straddle two XCDs).
     const int n_qb = (a.n_q + kQB - 1) / kQB;
+    bool bad = false;
     int unit, qb;
-    bool writer = false, bad = false;
-    if constexpr (!FUSE) {
+    {
         const int b = blockIdx.x, G = gridDim.x;
         const int xcd = b % 8, k = b / 8;
         const int per = G / 8, extra = G % 8;             // XCDs below `extra` hold per + 1
         const int slot = xcd * per + min(xcd, extra) + k;
         unit = slot / n_qb;
         qb = slot % n_qb;
-    } else {
-        // blocks [0, n_writers) take the (head, split < s_new, query block)
-        // units, the others those of the splits from s_new on, each range
-        // numbered XCD by XCD as above
-        const int b = blockIdx.x, nw = a.n_writers;
-        writer = b < nw;
-        const int lo = writer ? 0 : nw, n = writer ? nw : (int)gridDim.x - nw;
-        const int slot = xcd_rank(b, lo, n);
-        const int s0 = writer ? 0 : a.s_new, ns = writer ? a.s_new : a.n_splits - a.s_new;
-        const int h = slot / (ns * n_qb), r = slot % (ns * n_qb);
-        unit = h * a.n_splits + s0 + r / n_qb;
-        qb = r % n_qb;
     }
     const int head = unit / a.n_splits;
     const int split = unit % a.n_splits;
+    // The 64-key tiles are dealt to the splits in turn: split s takes tiles
+    // s, s + S, s + 2S, ... (S = n_splits), visited in that order (local
+    // index u = 0 .. n-1), so every split's keys stay in logical order and
+    // the newest keys of the window sit at the end of every split.
     const int n_tiles = (a.n_valid + kKT - 1) / kKT;
-    const int t0 = split * a.tiles_per_split;
-    const int t1 = min(n_tiles, t0 + a.tiles_per_split);
-    const int n = t1 - t0;
+    const int S = a.n_splits;
+    const int n = (n_tiles - split + S - 1) / S;
+    auto tile_at = [&](int u) { return split + min(u, n - 1) * S; };
+    // fused form: the first local tile holding a key of the chunk; n + P when
+    // none does (no wait below can match it, and every tile loads plainly)
+    int u_new = n + P;
+    if constexpr (FUSE) {
+        const int ft = a.first_new / kKT;
+        const int c = ft <= split ? 0 : (ft - split + S - 1) / S;
+        if (c < n) u_new = c;
+    }
+    uint32_t *flag = reinterpret_cast<uint32_t *>(smem + L::FLAG_OFF);
 
     const int tid = threadIdx.x, lane = tid % 64;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -483,37 +474,37 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
             for (int c = 0; c < QW / NH; ++c) qraw[(QW / NH) * h + c] = gload16(src + c);
         }
         if constexpr (QTAB) {
-            if (a.q_cs_lanes) {
-                // lane layout: load c of the wave reads 64 consecutive 16-byte
-                // words, one per lane (whole lines)
-                const u32x4 *src = reinterpret_cast<const u32x4 *>(a.q_cs) +
-                                   (int64_t)(qb * kNW + wave) * (8 * NH) * 64 + lane;
+            // word c (of 8 per slice h = c / 8) of the lane's (cos, sin):
+            //   lane layout: load c of the wave reads 64 consecutive 16-byte
+            //     words, one per lane (whole lines): lane_base + 64 c;
+            //   row layout: the (cos, sin) of the lane's pairs 32h + 16g ..
+            //     +15 of each slice h, 128 contiguous bytes per slice:
+            //     row_base + 16 (c / 8) + c % 8.
+            // One sequence of loads for both (the layout is uniform), so the
+            // loads carry no control flow.
+            const bool lanes = a.q_cs_lanes != 0;
+            const u32x4 *lane_base = reinterpret_cast<const u32x4 *>(a.q_cs) +
+                                     (int64_t)(qb * kNW + wave) * (8 * NH) * 64 + lane;
+            const u32x4 *row_base = reinterpret_cast<const u32x4 *>(a.q_cs + 2 * (qrow * (D / 2) + 16 * g));
+            const u32x4 *base = lanes ? lane_base : row_base;
 #pragma unroll
-                for (int c = 0; c < 8 * NH; ++c) csraw[c] = gload16(src + 64 * c);
-            } else {
-                // the (cos, sin) of the lane's pairs 32h + 16g .. +15 of each slice h:
-                // 128 contiguous bytes per slice
-#pragma unroll
-                for (int h = 0; h < NH; ++h) {
-                    const u32x4 *src = reinterpret_cast<const u32x4 *>(a.q_cs + 2 * (qrow * (D / 2) + 32 * h + 16 * g));
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) csraw[8 * h + c] = gload16(src + c);
-                }
-            }
+            for (int c = 0; c < 8 * NH; ++c) csraw[c] = gload16(base + (lanes ? 64 * c : 16 * (c / 8) + c % 8));
         }
     }
 
     // start streaming the first P tiles (and their scales); always P of them,
     // so the compiler can count them in its wait for Q (a split shorter than
-    // P tiles reloads its last tile into the spare buffers)
-    if (!FUSE || writer) {
+    // P tiles reloads its last tile into the spare buffers).  Fused form: the
+    // tiles before u_new now, then this workgroup's share of the chunk.
 #pragma unroll
-        for (int k = 0; k < P; ++k)
-            issue_tile<D, PREFIX>(a, kh, vh, scales_h, min(t0 + k, t1 - 1), tiles + k * L::BUF, wave);
+    for (int k = 0; k < P; ++k) {
+        if constexpr (FUSE) {
+            if (k < u_new) issue_tile<D, PREFIX>(a, kh, vh, scales_h, tile_at(k), tiles + k * L::BUF, wave);
+        } else {
+            issue_tile<D, PREFIX>(a, kh, vh, scales_h, tile_at(k), tiles + k * L::BUF, wave);
+        }
     }
-    if constexpr (FUSE) {
-        if (writer) fused_write<D, BF16>(a, (int)blockIdx.x);
-    }
+    if constexpr (FUSE) fused_write<D, BF16>(a, (int)blockIdx.x);
 
     // position form: the rotation depends on the query's position only, so its
     // (cos, sin) are formed while Q and the first tiles are in flight.  Pair i
@@ -541,18 +532,22 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
         for (int j = 0; j < PC; ++j) asm volatile("" : "+v"(pcos[j]), "+v"(psin[j]));
     }
     if constexpr (FUSE) {
-        if (writer) {
-            // the chunk's rows went to memory through the caches: once every
-            // lane's stores are acknowledged, the workgroup counts itself done
-            // (no write-back of this XCD's L2 is needed for them)
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-            if (tid == 0) __hip_atomic_fetch_add(a.sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            bad = wait_for_writers(a, smem);
+        // the chunk's rows went to memory through the caches: once every
+        // lane's stores are acknowledged, the workgroup counts itself done
+        // (no write-back of this XCD's L2 is needed for them)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) __hip_atomic_fetch_add(a.sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (u_new < P) {
+            // a tile holding new keys is among the first P: wait for every
+            // share of the chunk, then stream those tiles past stale copies
+            poll_writers(a, flag);
+            lds_barrier();
+            bad = __builtin_amdgcn_readfirstlane(*flag) != 0;
 #pragma unroll
             for (int k = 0; k < P; ++k)
-                issue_tile<D, PREFIX>(a, kh, vh, scales_h, min(t0 + k, t1 - 1), tiles + k * L::BUF, wave);
+                if (k >= u_new)
+                    issue_tile<D, PREFIX, kSc1>(a, kh, vh, scales_h, tile_at(k), tiles + k * L::BUF, wave);
         }
     }
     qwait<P * ops_per_tile<D>()>(qraw);
@@ -687,13 +682,14 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     //         operands; its share of the dequantisation of V(t+1) into V^T
     //   M(t): O^T += V^T(t) . P^T(t); S^T(t+1) = K(t+1) . Q^T; the K scales of
     //         tile t+1 for V(t+1) (they land during the barrier wait)
-    // in the order M(t0-1) V(t0) M(t0) V(t0+1) ... M(t1-1), where M(t0-1) only
-    // holds the tile-t0 parts.  Half-steps are separated by workgroup barriers,
+    // (t a local tile index) in the order M(-1) V(0) M(0) V(1) ... M(n-1),
+    // where M(-1) only holds the tile-0 parts.  Half-steps are separated by
+    // workgroup barriers,
     // and waves 4..7 run one half-step behind waves 0..3, so the two waves
     // sharing a SIMD are in different half-steps: one keeps the matrix core
     // busy while the other uses the VALU.
-    // Buffers: tile t0+k sits in tile buffer k mod kNBuf.  Each wave issues its
-    // part of tile u+P (relative to t0) after the barrier that ends its V(u),
+    // Buffers: local tile k sits in tile buffer k mod kNBuf.  Each wave issues
+    // its part of local tile u+P after the barrier that ends its V(u),
     // and lands (waits for) its part of tile u+2 at the end of V(u); the
     // barrier that follows publishes it before its first use, in V(u+1) and
     // M(u+1).  The last reader of a tile is the trailing group's V half-step,
@@ -744,7 +740,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
         for (int i = 0; i < 3; ++i) m4[i] = fmaxf(fmaxf(m10[3 * i], m10[3 * i + 1]), m10[3 * i + 2]);
         m4[3] = fmaxf(fmaxf(m10[9], s[1][14]), s[1][15]);
         float mx = fmaxf(fmaxf(fmaxf(m4[0], m4[1]), m4[2]), m4[3]);
-        const int lim = a.n_valid - t * kKT;              // valid keys of this tile
+        const int lim = a.n_valid - tile_at(t) * kKT;     // valid keys of this tile
         if (lim < kKT) {                                  // last tile of the window
             mx = -INFINITY;
 #pragma unroll
@@ -762,7 +758,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
             mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         }
-        const bool first = t == t0;
+        const bool first = t == 0;
         const bool over = mx > kShift + kTau;
         if (__any(first || over)) {
             float shift = 0.0f;                  // new cofs = cofs - shift
@@ -804,13 +800,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
         for (int i = 0; i < NCV; ++i) asm volatile("" : "+v"(ut[i]));
-        if (t + 1 < t1) convert_write(ut, sv, vt_next); // V^T of tile t+1
+        if (t + 1 < n) convert_write(ut, sv, vt_next);  // V^T of tile t+1
     };
 
     // M half-step.  PV and PREP select the parts (both in the steady state).
     auto half_m = [&](int t, const uint8_t *buf1, const uint8_t *vt, auto PV, auto PREP_) {
         constexpr bool PREP = decltype(PREP_)::value;
-        const bool PREP_on = PREP && t + 1 < t1;
+        const bool PREP_on = PREP && t + 1 < n;
         auto read_v = [&](int grp, u32x4 (&va)[ND]) {
             const int kb = grp / 2, ks = grp % 2;
 #pragma unroll
@@ -884,14 +880,14 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     // at the end of its V(u): tile u+2, whose V rows the next V half-step
     // dequantises; the barrier that follows publishes it.  The newest tile a
     // wave has issued before V(u) ends is max(P-1, min(u+P-1, n-1)).
-    auto land = [&](int u, int m) {                    // tile t0+m
+    auto land = [&](int u, int m) {                    // local tile m
         if (m < n) wait_tiles<D>(max(P - 1, min(u + P - 1, n - 1)) - m);
     };
     land(-1, 0);
     land(-1, 1);
     lds_barrier();
-    if (lead) half_m(t0 - 1, tiles, vt_base, no{}, yes{});   // S^T of tile t0 (lead group)
-    {                                                  // V^T of tile t0
+    if (lead) half_m(-1, tiles, vt_base, no{}, yes{});  // S^T of local tile 0 (lead group)
+    {                                                  // V^T of local tile 0
         v2i ut[NCV];
         f32x4 sv[NCV][2];
         convert_read(tiles, ut, sv);
@@ -903,7 +899,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     lds_barrier();
 
     // Both groups run the same loop; the trailing group enters it one
-    // interval late (its S^T of tile t0 and an extra barrier first), the lead
+    // interval late (its S^T of local tile 0 and an extra barrier first), the lead
     // group leaves it with an extra barrier, so both pass the same 2n+1
     // barriers.
     //   V(u): scores and weights of tile u, V^T of tile u+1 (buffer (u+1)%3)
@@ -911,11 +907,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     // V^T(u+1) is written in intervals 2u, 2u+1 and read in 2u+3, 2u+4; its
     // buffer last held V^T(u-2), read in 2u-3, 2u-2.
     if (!lead) {
-        // the trailing group's S^T of tile t0, in the interval in which the
-        // lead group runs V(t0) (its matrix work then pairs with that VALU
+        // the trailing group's S^T of local tile 0, in the interval in which
+        // the lead group runs V(0) (its matrix work then pairs with that VALU
         // half-step rather than with the lead group's own S^T in the prologue)
         __builtin_amdgcn_s_setprio(1);
-        half_m(t0 - 1, tiles, vt_base, no{}, yes{});
+        half_m(-1, tiles, vt_base, no{}, yes{});
         __builtin_amdgcn_s_setprio(0);
         lds_barrier();
 #pragma unroll
@@ -923,23 +919,32 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(fkr[kb][q]));
     }
-    int bcur = 0;                                      // tile buffer of tile t0+u
-    int vcur = 0;                                      // V^T buffer of tile t0+u
+    int bcur = 0;                                      // tile buffer of local tile u
+    int vcur = 0;                                      // V^T buffer of local tile u
     for (int u = 0; u < n; ++u) {
         const int bnext = bcur + 1 == kNBuf ? 0 : bcur + 1;
         const int vnext = vcur + 1 == 3 ? 0 : vcur + 1;
         uint8_t *buf = tiles + bcur * L::BUF;
         uint8_t *buf1 = tiles + bnext * L::BUF;
-        half_v(t0 + u, buf, buf1, vt_base + vnext * L::VT_BYTES);
+        half_v(u, buf, buf1, vt_base + vnext * L::VT_BYTES);
         land(u, u + 2);
+        // fused form: before the first tile holding new keys is streamed,
+        // wait for every share of the chunk (thread 0 polls; the barrier
+        // below publishes the outcome)
+        const bool wait_here = FUSE && u + P == u_new;
+        if (wait_here) poll_writers(a, flag);
         lds_barrier();
-        if (u + P < n) {                               // stream tile t0+u+P
+        if (wait_here) bad = __builtin_amdgcn_readfirstlane(*flag) != 0;
+        if (u + P < n) {                               // stream local tile u+P
             int bl = bcur + P;
             bl = bl >= kNBuf ? bl - kNBuf : bl;
-            issue_tile<D, PREFIX>(a, kh, vh, scales_h, t0 + u + P, tiles + bl * L::BUF, wave);
+            if (FUSE && u + P >= u_new)
+                issue_tile<D, PREFIX, kSc1>(a, kh, vh, scales_h, tile_at(u + P), tiles + bl * L::BUF, wave);
+            else
+                issue_tile<D, PREFIX>(a, kh, vh, scales_h, tile_at(u + P), tiles + bl * L::BUF, wave);
         }
         __builtin_amdgcn_s_setprio(1);                 // the MFMA half-step issues first
-        half_m(t0 + u, buf1, vt_base + vcur * L::VT_BYTES, yes{}, yes{});
+        half_m(u, buf1, vt_base + vcur * L::VT_BYTES, yes{}, yes{});
         __builtin_amdgcn_s_setprio(0);
         lds_barrier();
 #pragma unroll

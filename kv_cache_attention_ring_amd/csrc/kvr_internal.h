@@ -76,18 +76,19 @@ struct AttnArgs {
     float *part_ml;                   // [splits][n_q][H][4]: running max, sum, row exponent, 0
     int32_t n_heads, window, slot_start, n_valid, n_q, dtype;   // n_valid: prefix + ring keys
     int32_t prefix, cap;              // key i < prefix: slot i; else prefix + (slot_start + i - prefix) mod cap
-    int32_t n_splits, tiles_per_split;
+    int32_t n_splits;                 // key tiles dealt to the splits in turn
     float softmax_scale;
     // The chunk's write carried by the attention launch (fused form only):
-    // writer workgroups (those of splits below s_new, whose keys are all old)
-    // store the n_new new rows of this layer, then count themselves done in
-    // sync[0]; the other workgroups wait for that count before loading tiles.
+    // every workgroup stores its share of the n_new new rows of this layer,
+    // then counts itself done in sync[0]; a workgroup whose key range holds
+    // new keys waits for n_writers before streaming its first such tile.
     const void *w_k, *w_v;            // [n_new][H][D] of `dtype`
     const float *w_cs;                // rotary table row of the chunk's first position (pair-major)
     uint8_t *w_k_codes, *w_v_codes;   // this layer's codes and scales (written)
     float *w_k_scales, *w_v_scales;
     int32_t w_head, w_n_new;          // ring slot of new token 0, tokens in the chunk
-    int32_t n_writers, s_new;         // writer workgroups; first split holding a new key
+    int32_t n_writers, n_waiters;     // workgroups that write (the grid); that wait
+    int32_t first_new;                // logical index of the chunk's first key (n_valid - n_new)
     uint32_t *sync;                   // control block: writers done, waiters through, timeouts, spin limit
 };
 int attn_default_splits(int n_heads, int n_q, int n_valid);

@@ -105,8 +105,10 @@ kvr::ThetaTable make_theta(int32_t D, double base) {
 }
 
 // Number of key-range splits actually used: the requested count (0 = the
-// shape's default) clamped to the number of 64-key tiles, then reduced so
-// that no split is empty.  *tps receives the tiles per split.
+// shape's default) clamped to the number of 64-key tiles, then reduced to the
+// fewest splits whose largest share is still ceil(tiles / requested) tiles
+// (the same longest split, fewer partials to merge).  *tps receives that
+// largest share; the tiles are dealt to the splits in turn.
 int32_t effective_splits(int32_t n_heads, int32_t n_q, int32_t n_valid, int32_t requested,
                          int32_t *tps) {
     const int32_t tiles = (n_valid + 63) / 64;
@@ -357,7 +359,6 @@ int32_t attn_setup(kvr::AttnArgs &a, const kvr_cache *cache, int32_t layer, int3
     a.n_q = n_q;
     a.dtype = dtype;
     a.n_splits = n_splits;
-    a.tiles_per_split = tps;
     a.softmax_scale = softmax_scale;
     set_partials(a, ws, cache->n_heads, D, n_q, n_splits);
     return KVR_OK;
@@ -385,7 +386,6 @@ int32_t merge_setup(kvr::AttnArgs &a, const kvr_cache *cache, int32_t n_q, int32
     a.n_valid = n_valid;
     a.n_q = n_q;
     a.n_splits = n_splits;
-    a.tiles_per_split = tps;
     if (int32_t e = check_workspace(kvr::attn_workspace_bytes(cache->n_heads, D, n_q, n_splits), ws, ws_bytes))
         return e;
     set_partials(a, ws, cache->n_heads, D, n_q, n_splits);
@@ -482,27 +482,33 @@ int32_t attn_fp8_window_write(const kvr_cache *cache, const kvr_ring *before, in
     if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
         return fail(KVR_EALIGN, "workspace must be 256-byte aligned");
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    // splits below s_new hold old keys only (the new keys are the last n_new
-    // in logical order); their workgroups write the chunk
+    // every workgroup writes a share of the chunk; a workgroup whose split
+    // holds new keys (the last n_new in logical order: with the tiles dealt
+    // to the splits in turn, the end of a split) waits for all of them
     const int32_t first_new = a.n_valid - n_new;
-    const int32_t s_new = first_new / (a.tiles_per_split * 64);
     const int64_t lay = (int64_t)layer * cache->n_heads * cache->window;
+    const int32_t n_tiles = (a.n_valid + 63) / 64, S = a.n_splits;
+    int32_t splits_new = 0;                          // splits whose last tile holds a new key
+    for (int32_t sp = 0; sp < S; ++sp) {
+        const int32_t n_s = (n_tiles - sp + S - 1) / S;
+        if ((int64_t)(sp + (int64_t)(n_s - 1) * S) * 64 + 63 >= first_new) ++splits_new;
+    }
+    const int64_t grid = (int64_t)kvr::attn_query_blocks(n_new) * cache->n_heads * S;
     // the waiting workgroups need every writer to run, whatever order the
     // hardware dispatches them in: the fused launch only when all of its
     // workgroups fit on the GPU at once
     bool resident = false;
-    if (s_new > 0) {
+    {
         int dev = -1, max_blocks = 0;
         hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
         if (e == hipSuccess)
             e = kvr::attention_fused_resident(D, dtype, cache->n_prefix > 0, dev, &max_blocks);
         if (e != hipSuccess) return launch_status(e, "fused write and attention: resident workgroups");
-        const int64_t grid = (int64_t)kvr::attn_query_blocks(n_new) * cache->n_heads * a.n_splits;
         resident = grid <= max_blocks;
     }
     if (!resident) {
-        // every split reads new keys, or the launch would not be resident at
-        // once: the write kernel, then the plain call
+        // the launch would not be resident at once: the write kernel, then
+        // the plain call
         kvr::WriteArgs w{};
         w.k_codes = cache->k_codes;
         w.v_codes = cache->v_codes;
@@ -533,8 +539,9 @@ int32_t attn_fp8_window_write(const kvr_cache *cache, const kvr_ring *before, in
     a.w_v_scales = cache->v_scales + lay;
     a.w_head = before->head;
     a.w_n_new = n_new;
-    a.s_new = s_new;
-    a.n_writers = cache->n_heads * s_new * kvr::attn_query_blocks(n_new);
+    a.first_new = first_new;
+    a.n_writers = (int32_t)grid;
+    a.n_waiters = splits_new * cache->n_heads * kvr::attn_query_blocks(n_new);
     // the control block is the workspace's last 256 bytes (64-byte aligned),
     // wherever this call's partials end: a buffer reused by calls of other
     // shapes keeps its counters in one place

@@ -5,16 +5,16 @@ The fused call must store exactly the codes and scales kv_write_rope_quant
 stores and return exactly the rows attn_fp8_window returns over the window
 after that write; its outputs are also checked against the oracle on every
 row (window, slots and positions from the oracle's own token count).  Cases:
-  * the production layer (12 heads, D 128, W 5788, N 757; 7 splits: 216
-    writing and 36 waiting workgroups), two steps, the first chunk wrapping
-    past the end of the ring;
-  * small shapes with one or more writer splits: W 96 and W 100 (chunks wrap
-    mid-chunk), fp32 and bf16, head_dim 64 and 128, two query blocks, a ring
+  * the production layer (12 heads, D 128, W 5788, N 757; 7 splits, 252
+    workgroups, each writing a share and each waiting before its last tiles),
+    two steps, the first chunk wrapping past the end of the ring;
+  * small shapes: W 96 and W 100 (chunks wrap mid-chunk), fp32 and bf16, head_dim 64 and 128, two query blocks, a ring
     filling up over the steps, the workspace reused by every step;
   * a fixed prefix beside the ring;
-  * one split, a chunk most of the window (every split reads new keys), and a
-    launch with more workgroups than the GPU holds at once (the write kernel
-    and the plain call are launched instead);
+  * one split, a chunk most of the window (every tile of some splits holds new
+    keys: those wait before their first tile), and a launch with more
+    workgroups than the GPU holds at once (the write kernel and the plain call
+    are launched instead);
   * the control block back at zero after every call, in one workspace reused
     by every step while the partials before it change size;
   * a poll limit of one (the bounded wait's give-up path): output rows are
@@ -153,7 +153,7 @@ def test_fused_write_production_layer():
     for s in range(7):
         _say(f"production prefill {s}")
         t.prefill(s)
-    _say("production fused step 7 (the chunk wraps; 216 writers, 36 waiting)")
+    _say("production fused step 7 (the chunk wraps; 252 workgroups)")
     t.fused_step(7, 0)
     _say("production fused step 8")
     t.fused_step(8, 0, oracle_check=False)
@@ -189,11 +189,12 @@ def test_fused_write_with_prefix(D, dtype, splits):
 
 
 @pytest.mark.parametrize("W,N,splits", [(96, 16, 1), (96, 80, 2), (5788, 757, 1)])
-def test_fused_write_without_writer_splits(W, N, splits):
-    """Every split reads new keys: the write kernel and the plain call."""
+def test_fused_write_new_keys_everywhere(W, N, splits):
+    """One split, or a chunk that is most of the window: workgroups wait
+    before their first tile or soon after."""
     t = Twin(2 if W < 1000 else 12, 64 if W < 1000 else 128, W, N, torch.bfloat16, steps=4)
     for s in range(3):
-        _say(f"no writer splits W={W} N={N} splits={splits} step {s}")
+        _say(f"new keys in every split W={W} N={N} splits={splits} step {s}")
         t.fused_step(s, splits, oracle_check=W < 1000)
 
 
