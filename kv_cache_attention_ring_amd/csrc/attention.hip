@@ -689,12 +689,14 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     // sharing a SIMD are in different half-steps: one keeps the matrix core
     // busy while the other uses the VALU.
     // Buffers: local tile k sits in tile buffer k mod kNBuf.  Each wave issues
-    // its part of local tile u+P after the barrier that ends its V(u),
+    // its part of local tile u+P at the end of its M(u), behind the last
+    // MFMAs (so that M(u) starts with its operand reads),
     // and lands (waits for) its part of tile u+2 at the end of V(u); the
     // barrier that follows publishes it before its first use, in V(u+1) and
-    // M(u+1).  The last reader of a tile is the trailing group's V half-step,
-    // at least one interval before the buffer is reloaded.  V^T is triple
-    // buffered (below).
+    // M(u+1).  Tile u+1 is read in V(u) and M(u); its last reader, the
+    // trailing group's M(u), ends at least two intervals before the buffer is
+    // reloaded (with tile u+6, at the end of M(u+2)).  V^T is triple buffered
+    // (below).
     v16f o[ND];
 #pragma unroll
     for (int d = 0; d < ND; ++d) o[d] = v16f{};
@@ -793,9 +795,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
                                                           false);
                 }
                 // keep the weights computed in this half-step (not sunk
-                // into the matrix half-step that consumes them)
+                // into the matrix half-step that consumes them); a use, not
+                // a redefinition, so they stay in the registers they are
+                // formed in
+                asm volatile("" ::"v"(w));
                 pb[kb][ks] = __builtin_bit_cast(v8bf, w);
-                asm volatile("" : "+v"(pb[kb][ks]));
             }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
@@ -935,16 +939,16 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
         if (wait_here) poll_writers(a, flag);
         lds_barrier();
         if (wait_here) bad = __builtin_amdgcn_readfirstlane(*flag) != 0;
-        if (u + P < n) {                               // stream local tile u+P
-            int bl = bcur + P;
+        __builtin_amdgcn_s_setprio(1);                 // the MFMA half-step issues first
+        half_m(u, buf1, vt_base + vcur * L::VT_BYTES, yes{}, yes{});
+        if (u + P < n) {                               // stream local tile u+P (the barrier
+            int bl = bcur + P;                         // before M(u) ended every read of its buffer)
             bl = bl >= kNBuf ? bl - kNBuf : bl;
             if (FUSE && u + P >= u_new)
                 issue_tile<D, PREFIX, kSc1>(a, kh, vh, scales_h, tile_at(u + P), tiles + bl * L::BUF, wave);
             else
                 issue_tile<D, PREFIX>(a, kh, vh, scales_h, tile_at(u + P), tiles + bl * L::BUF, wave);
         }
-        __builtin_amdgcn_s_setprio(1);                 // the MFMA half-step issues first
-        half_m(u, buf1, vt_base + vcur * L::VT_BYTES, yes{}, yes{});
         __builtin_amdgcn_s_setprio(0);
         lds_barrier();
 #pragma unroll
