@@ -331,6 +331,10 @@ int32_t attn_setup(kvr::AttnArgs &a, const kvr_cache *cache, int32_t layer, int3
     if (n_splits < 0) return fail(KVR_EINVAL, "n_splits %d < 0", n_splits);
     int32_t tps;
     n_splits = effective_splits(cache->n_heads, n_q, n_keys, n_splits, &tps);
+    // one workgroup per (query block, head, split), numbered with 32-bit indices
+    if ((int64_t)kvr::attn_query_blocks(n_q) * cache->n_heads * n_splits >= (int64_t{1} << 31))
+        return fail(KVR_EUNSUPPORTED, "%d queries x %d heads x %d splits exceed the attention kernel's grid", n_q,
+                    cache->n_heads, n_splits);
     if (int32_t e = check_workspace(kvr::attn_workspace_bytes(cache->n_heads, D, n_q, n_splits), ws, ws_bytes))
         return e;
     if (q_cs && !aligned16(q_cs)) return fail(KVR_EALIGN, "query rotary rows not 16-byte aligned");

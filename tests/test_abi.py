@@ -173,6 +173,12 @@ def test_attention_validation():
     assert _attn(c, 5788, n_splits=4) == K.KVR_EINVAL
     assert _attn(c, 5788, n_splits=4, ws=FAKE + 0x9000000, ws_bytes=need - 4) == K.KVR_EINVAL
     assert _attn(c, 5788, n_splits=4, ws=FAKE + 0x9000010, ws_bytes=need) == K.KVR_EALIGN
+    # beyond the attention kernel's grid: 65536 query blocks x 32768 heads = 2^31 workgroups
+    assert _attn(_cache(H=1 << 15), 5788, n_q=(1 << 24) - 1) == K.KVR_EUNSUPPORTED
+    assert "grid" in K.kvr_last_error()
+    # 65536 x 16383 heads x 2 splits pass the grid check (and fail later, on the missing workspace)
+    assert _attn(_cache(H=(1 << 14) - 1), 5788, n_q=(1 << 24) - 1, n_splits=2) == K.KVR_EINVAL
+    assert "workspace" in K.kvr_last_error()
     assert _attn(_cache(D=256), 5788) == K.KVR_EUNSUPPORTED
 
 
