@@ -295,7 +295,9 @@ int32_t attn_fp8_window_noalloc(const kvr_cache *cache, int32_t layer, int32_t s
  *                          src and dst must not overlap (ping-pong buffers).
  *   k_new, v_new         : device [n_new][n_heads][head_dim] of `dtype`.
  *   rope                 : table covering the n_after positions.
- * Errors: KVR_EINVAL, KVR_EALIGN, KVR_EUNSUPPORTED. */
+ * No output (lin_*_dst, codes, scales) may overlap an input or another
+ * output; the inputs may alias each other.
+ * Errors: KVR_EINVAL (also overlapping buffers), KVR_EALIGN, KVR_EUNSUPPORTED. */
 int32_t naive_upkeep(const void *lin_k_src, const void *lin_v_src,
                      const void *k_new, const void *v_new, kvr_dtype dtype, int32_t n_new,
                      int32_t n_valid_before, int64_t pos_next_before,

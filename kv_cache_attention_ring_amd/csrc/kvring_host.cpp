@@ -843,14 +843,33 @@ int32_t naive_upkeep(const void *lin_k_src, const void *lin_v_src, const void *k
         if (!p) return fail(KVR_EINVAL, "naive_upkeep: NULL buffer");
         if (!aligned16(p)) return fail(KVR_EALIGN, "naive_upkeep: buffer not 16-byte aligned");
     }
+    // no output may overlap an input or another output (the inputs are only read)
     const size_t esz = dtype == KVR_BF16 ? 2 : 4;
     const size_t win_bytes = (size_t)n_heads * window * head_dim * esz;
-    auto overlap = [&](const void *a, const void *b) {
-        const char *x = static_cast<const char *>(a), *y = static_cast<const char *>(b);
-        return x < y + win_bytes && y < x + win_bytes;
+    const size_t new_bytes = (size_t)n_new * n_heads * head_dim * esz;
+    const size_t code_bytes = (size_t)n_heads * window * head_dim, scale_bytes = (size_t)n_heads * window * 4;
+    struct Span {
+        const void *p;
+        size_t n;
+        const char *name;
     };
-    if (overlap(lin_k_src, lin_k_dst) || overlap(lin_v_src, lin_v_dst))
-        return fail(KVR_EINVAL, "naive_upkeep: src and dst windows overlap");
+    const Span ins[] = {{lin_k_src, win_bytes, "lin_k_src"}, {lin_v_src, win_bytes, "lin_v_src"},
+                        {k_new, new_bytes, "k_new"}, {v_new, new_bytes, "v_new"}};
+    const Span outs[] = {{lin_k_dst, win_bytes, "lin_k_dst"}, {lin_v_dst, win_bytes, "lin_v_dst"},
+                         {k_codes, code_bytes, "k_codes"},     {v_codes, code_bytes, "v_codes"},
+                         {k_scales, scale_bytes, "k_scales"},  {v_scales, scale_bytes, "v_scales"}};
+    auto overlap = [](const Span &a, const Span &b) {
+        const char *x = static_cast<const char *>(a.p), *y = static_cast<const char *>(b.p);
+        return x < y + b.n && y < x + a.n;
+    };
+    for (size_t i = 0; i < sizeof outs / sizeof outs[0]; ++i) {
+        for (const Span &in : ins)
+            if (overlap(outs[i], in))
+                return fail(KVR_EINVAL, "naive_upkeep: %s overlaps the input %s", outs[i].name, in.name);
+        for (size_t j = i + 1; j < sizeof outs / sizeof outs[0]; ++j)
+            if (overlap(outs[i], outs[j]))
+                return fail(KVR_EINVAL, "naive_upkeep: outputs %s and %s overlap", outs[i].name, outs[j].name);
+    }
     const int32_t n_after = n_valid_before + n_new < window ? n_valid_before + n_new : window;
     const int32_t drop = n_valid_before + n_new - n_after;
     const float *cs;

@@ -310,7 +310,7 @@ def test_workspace_sizes_and_split_clamping():
 def test_naive_validation():
     lib = K.lib()
     t = _table()
-    p = [FAKE + i * 0x1000000 for i in range(10)]
+    p = [FAKE + i * 0x2000000 for i in range(10)]     # 32 MiB apart: a window is 17.8 MB
 
     def call(n_new=757, n_valid=5788, H=12, D=128, W=5788, ptrs=p, dtype=K.KVR_BF16, table=t, pos=0):
         return lib.naive_upkeep(ptrs[0], ptrs[1], ptrs[2], ptrs[3], dtype, n_new, n_valid, pos, H, D,
@@ -322,6 +322,19 @@ def test_naive_validation():
     bad = list(p)
     bad[4] = p[0] + 256            # dst overlaps src
     assert call(ptrs=bad) == K.KVR_EINVAL
+    # across K and V, into the inputs' new rows, and between two outputs
+    for i, j, name in ((5, 0, "lin_v_dst overlaps the input lin_k_src"),
+                       (6, 3, "k_codes overlaps the input v_new"),
+                       (9, 8, "outputs k_scales and v_scales overlap")):
+        bad = list(p)
+        bad[i] = p[j] + 4096
+        assert call(ptrs=bad) == K.KVR_EINVAL
+        assert name in K.kvr_last_error(), K.kvr_last_error()
+    # the inputs may alias each other (both windows read from one buffer)
+    alias = list(p)
+    alias[1] = p[0]
+    assert call(ptrs=alias, pos=9500) == K.KVR_EINVAL      # gets as far as the table check
+    assert "rotary table" in K.kvr_last_error()
     bad = list(p)
     bad[6] = p[6] + 1
     assert call(ptrs=bad) == K.KVR_EALIGN
