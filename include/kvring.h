@@ -178,7 +178,7 @@ int32_t kv_delta_rebase(const kvr_cache *cache, const kvr_ring *ring, int32_t la
  *             (may be NULL when that is 0), 256-byte aligned.
  * Errors: KVR_EINVAL (null, n_valid not in [1, window], slot_start out of
  * range, rope_base <= 1, softmax_scale negative or not finite, workspace too
- * small), KVR_EALIGN, KVR_EUNSUPPORTED (head_dim or dtype, or more than
+ * small, out overlapping q, the query rotary rows or the workspace), KVR_EALIGN, KVR_EUNSUPPORTED (head_dim or dtype, or more than
  * 2^31 - 1 workgroups: ceil(n_q / 256) x n_heads x splits).
  * Range: the fp32 accumulators hold sums of up to window weights below 2^16
  * times the dequantised V values, so |V| must stay below about 2^99. */

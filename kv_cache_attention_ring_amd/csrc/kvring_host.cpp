@@ -338,6 +338,24 @@ int32_t attn_setup(kvr::AttnArgs &a, const kvr_cache *cache, int32_t layer, int3
     if (int32_t e = check_workspace(kvr::attn_workspace_bytes(cache->n_heads, D, n_q, n_splits), ws, ws_bytes))
         return e;
     if (q_cs && !aligned16(q_cs)) return fail(KVR_EALIGN, "query rotary rows not 16-byte aligned");
+    {
+        // out is written while other workgroups still read q, the rotary rows
+        // and the partials: it may overlap none of them
+        const size_t rows = (size_t)n_q * cache->n_heads;
+        const char *o = reinterpret_cast<const char *>(out);
+        const size_t ob = rows * D * 2;
+        auto overlaps = [&](const void *p, size_t n) {
+            const char *x = static_cast<const char *>(p);
+            return p && n && o < x + n && x < o + ob;
+        };
+        if (overlaps(q, rows * D * (dtype == KVR_BF16 ? 2 : 4))) return fail(KVR_EINVAL, "out overlaps q");
+        // the position form has no rows; the row form [n_q][D/2][2] fp32, the lane form
+        // its padded load order
+        const size_t cs_bytes = !q_cs ? 0 : q_cs_lanes ? kvr::query_lanes_bytes(n_q, D) : (size_t)n_q * D * 4;
+        if (overlaps(q_cs, cs_bytes)) return fail(KVR_EINVAL, "out overlaps the query rotary rows");
+        if (overlaps(ws, kvr::attn_workspace_bytes(cache->n_heads, D, n_q, n_splits)))
+            return fail(KVR_EINVAL, "out overlaps the workspace");
+    }
     a = kvr::AttnArgs{};
     a.q_cs = q_cs;
     a.q_cs_lanes = q_cs_lanes ? 1 : 0;
@@ -485,6 +503,12 @@ int32_t attn_fp8_window_write(const kvr_cache *cache, const kvr_ring *before, in
         return e;
     if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
         return fail(KVR_EALIGN, "workspace must be 256-byte aligned");
+    {
+        // nor the control block at the workspace's end (the partials are checked above)
+        const char *o = reinterpret_cast<const char *>(out), *w = static_cast<const char *>(ws);
+        if (o < w + ws_bytes && w < o + (size_t)n_new * cache->n_heads * D * 2)
+            return fail(KVR_EINVAL, "out overlaps the workspace");
+    }
     const hipStream_t s = static_cast<hipStream_t>(stream);
     // every workgroup writes a share of the chunk; a workgroup whose split
     // holds new keys (the last n_new in logical order: with the tiles dealt

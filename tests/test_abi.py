@@ -173,6 +173,15 @@ def test_attention_validation():
     assert _attn(c, 5788, n_splits=4) == K.KVR_EINVAL
     assert _attn(c, 5788, n_splits=4, ws=FAKE + 0x9000000, ws_bytes=need - 4) == K.KVR_EINVAL
     assert _attn(c, 5788, n_splits=4, ws=FAKE + 0x9000010, ws_bytes=need) == K.KVR_EALIGN
+    # out may not overlap q, the workspace or the rotary rows
+    assert _attn(c, 5788, out=FAKE + 0x7000000 + 4096) == K.KVR_EINVAL
+    assert "out overlaps q" in K.kvr_last_error()
+    assert _attn(c, 5788, n_splits=4, ws=FAKE + 0x8000000 - 4096, ws_bytes=need) == K.KVR_EINVAL
+    assert "out overlaps the workspace" in K.kvr_last_error()
+    rows = K.lib().attn_fp8_window_rows
+    assert rows(ctypes.byref(c), 0, 0, 5788, FAKE + 0x7000000, K.KVR_BF16, 757, FAKE + 0x8000000 + 256, 0.088,
+                FAKE + 0x8000000, 1, None, 0, None) == K.KVR_EINVAL
+    assert "rotary rows" in K.kvr_last_error()
     # beyond the attention kernel's grid: 65536 query blocks x 32768 heads = 2^31 workgroups
     assert _attn(_cache(H=1 << 15), 5788, n_q=(1 << 24) - 1) == K.KVR_EUNSUPPORTED
     assert "grid" in K.kvr_last_error()
