@@ -9,6 +9,8 @@ element with the bars in tests/_parity.py.  Cases:
   * one attention layer at the production shape (12 heads, D 128, W 5788,
     N 757): all writes, 4 passes on sampled queries of every head, default and
     single split, determinism, the naive path, the rebase;
+  * the key tiles dealt to the splits: a W = 1000 window (2 heads, D 64, 37
+    queries) at 11 lengths around tile boundaries, with 1 to 16 splits;
   * the 60-layer batched write of a full step (sampled layers), and the full-
     step configuration the benchmark times: 42 steps of 60-layer writes, all
     4 passes of layers 0 and 59 at steps 1 and 42, then the 60-layer rebase;
@@ -437,6 +439,31 @@ def test_edge_cases_small():
     out0 = K.attn_fp8_window(run.cache, 0, 0, 16, torch.zeros_like(qd), 0, run.rope.base)
     torch.cuda.synchronize()
     assert_attention(_f32(out0), oracle.attention(run.orc, 0, 16, np.zeros_like(q), 0), "q=0")
+
+
+def test_key_tiles_dealt_to_splits():
+    """The 64-key tiles are dealt to the splits in turn (split s of S takes
+    tiles s, s + S, ...): windows ending just before, on and just after tile
+    boundaries, against split counts that do and do not divide the tile count
+    (and more splits than tiles, which the library reduces), every output row
+    against the oracle."""
+    shp = inputs.Shape("test", 1, 2, 64, 1000, 125)
+    run = SmallRun(shp, table=(-256, 2048))
+    for step in range(8):
+        run.step(*inputs.np_chunk(shp, step))
+    assert run.ref_n_valid() == 1000
+    q = inputs.np_queries(shp, 8, 0, n_q=37)
+    qd = torch.from_numpy(q).cuda()
+    q_pos = run.ref_pos_next() - 37
+    for n_valid in (1, 63, 64, 65, 127, 128, 129, 448, 449, 640, 1000):
+        # the newest n_valid keys of the window
+        start_ref = oracle.slot_of_token(run.total - n_valid, shp.window)
+        ref = oracle.attention(run.orc, start_ref, n_valid, q, q_pos)
+        for splits in (1, 2, 3, 4, 5, 6, 7, 9, 13, 16):
+            _say(f"tiles dealt to splits: n_valid {n_valid}, splits {splits}")
+            out = K.attn_fp8_window(run.cache, 0, start_ref, n_valid, qd, q_pos, run.rope.base, n_splits=splits)
+            torch.cuda.synchronize()
+            assert_attention(_f32(out), ref, f"n_valid {n_valid}, splits {splits}")
 
 
 def test_lazy_rescale_when_scores_grow():
