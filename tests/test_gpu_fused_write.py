@@ -10,6 +10,9 @@ row (window, slots and positions from the oracle's own token count).  Cases:
     two steps, the first chunk wrapping past the end of the ring;
   * small shapes: W 96 and W 100 (chunks wrap mid-chunk), fp32 and bf16, head_dim 64 and 128, two query blocks, a ring
     filling up over the steps, the workspace reused by every step;
+  * a sweep of windows (130, 300, 640), chunks (33, 64, 65, 129 tokens) and
+    split counts, stepped until the ring wraps: the first new key falls in
+    every local tile of every split;
   * a fixed prefix beside the ring;
   * one split, a chunk most of the window (every tile of some splits holds new
     keys: those wait before their first tile), and a launch with more
@@ -178,6 +181,22 @@ def test_fused_write_small(H, D, W, N, dtype, splits, steps, prefill):
     for s in range(prefill, prefill + steps):
         _say(f"fused H={H} D={D} W={W} N={N} {dtype} splits={splits} step {s} (n_valid {t.ring.n_valid})")
         t.fused_step(s, splits)
+
+
+@pytest.mark.parametrize("W", [130, 300, 640])
+def test_fused_write_sweep(W):
+    """Chunks of 33, 64, 65 and 129 tokens with the default and 2, 3 and 5
+    splits, stepped until the ring has filled and wrapped (at most 12 steps):
+    where the new keys start moves through every local tile of every split,
+    and each step must equal the write + plain call bit for bit and leave the
+    control block at zero."""
+    for N in (33, 64, 65, 129):
+        steps = min(-(-W // N) + 2, 12)
+        for splits in (0, 2, 3, 5):
+            t = Twin(3, 64, W, N, torch.bfloat16, steps=steps)
+            for s in range(steps):
+                _say(f"fused sweep W={W} N={N} splits={splits} step {s} (n_valid {t.ring.n_valid})")
+                t.fused_step(s, splits, oracle_check=False)
 
 
 @pytest.mark.parametrize("D,dtype,splits", [(128, torch.bfloat16, 0), (64, torch.float32, 3)])
