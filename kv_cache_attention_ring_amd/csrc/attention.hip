@@ -59,8 +59,9 @@
 // are the last n_new in logical order, so with the tiles dealt in turn they
 // sit at the end of every split.  Every workgroup writes its share of the
 // chunk's rows after issuing its first tiles (the upkeep kernels' row
-// arithmetic, rowquant.h, with stores that write through to memory), waits
-// for its stores to complete and counts itself done; before it streams its
+// arithmetic, rowquant.h, with stores that write through to memory), prepares
+// its queries while they complete, then waits for them and counts itself
+// done; before it streams its
 // first tile holding new keys it waits (bounded) for the count to reach the
 // grid, and it streams those tiles with device-scope loads, which miss any
 // stale copy.  At the production shape that tile comes ~11 tiles into a
@@ -534,11 +535,14 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     if constexpr (FUSE) {
         // the chunk's rows went to memory through the caches: once every
         // lane's stores are acknowledged, the workgroup counts itself done
-        // (no write-back of this XCD's L2 is needed for them)
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (tid == 0) __hip_atomic_fetch_add(a.sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // (no write-back of this XCD's L2 is needed for them).  A workgroup
+        // that waits in this prologue counts itself first; the others count
+        // after preparing their queries (below), behind which the stores'
+        // latency is hidden -- every workgroup counts itself before it waits
         if (u_new < P) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (tid == 0) __hip_atomic_fetch_add(a.sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             // a tile holding new keys is among the first P: wait for every
             // share of the chunk, then stream those tiles past stale copies
             poll_writers(a, flag);
@@ -887,6 +891,13 @@ __global__ void __launch_bounds__(kThreads, 2) attn_kernel(AttnArgs a) {
     auto land = [&](int u, int m) {                    // local tile m
         if (m < n) wait_tiles<D>(max(P - 1, min(u + P - 1, n - 1)) - m);
     };
+    if constexpr (FUSE) {
+        if (u_new >= P) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (tid == 0) __hip_atomic_fetch_add(a.sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
     land(-1, 0);
     land(-1, 1);
     lds_barrier();
